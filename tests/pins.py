@@ -1,0 +1,386 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each ``check_*`` takes the oracle module (or a patched copy of it) and raises
+AssertionError on a mismatch.  ``test_oracle_pins.py`` runs them against the real
+oracle; ``test_oracle_mutations.py`` runs them against oracles with a planted
+mistake and requires that some check fails.
+
+What pins what:
+  * hand-worked examples in tests/golden (Deja Vu page, section 2.3, Eq. (1)
+    and Eq. (2); predictor and look-ahead readings);
+  * library routines for the dense special cases: torch.nn Linear-ReLU-Linear
+    (the survey-notes page's FFN listing, bias zero) for S = all neurons, and
+    torch scaled_dot_product_attention with concatenation and one output
+    projection (the survey-notes page's projection listing) for S = all heads;
+  * invariants: empty set gives 0, additivity over disjoint sets, the ReLU
+    support reproduces the dense MLP, closed forms of softmax attention
+    (n = 1, equal keys, one dominant logit);
+  * the mean-shift restatement of a head on the Deja Vu page, section 3.2:
+    H_i(y) = m_i(y) W_i^V with m_i a similarity-weighted mean of the x_j;
+  * brute force: all k-subsets for top-k on tiny N, scalar loops for the
+    products, np.lexsort for the ordering rule.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import torch
+
+from conftest import load_golden
+
+RNG_SEED = 12345
+
+
+def _rng(seed=RNG_SEED):
+    return np.random.default_rng(seed)
+
+
+def assert_close(a, b, tol, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol * scale, f"{what}: max err {err:g} > {tol:g} * {scale:g}"
+
+
+# --------------------------------------------------------------------------- #
+# golden, worked by hand                                                      #
+# --------------------------------------------------------------------------- #
+
+def check_golden_mlp(O):
+    g = load_golden("mlp_tiny.json")
+    for c in g["cases"]:
+        out = O.sparse_mlp(np.array(g["y"]), np.array(g["W1t"]), np.array(g["W2t"]), c["S"])
+        assert_close(out, c["out"], 1e-15, f"mlp S={c['S']}")
+
+
+def check_golden_mha(O):
+    g = load_golden("mha_tiny.json")
+    for c in g["cases"]:
+        out = O.sparse_mha(np.array(g["y"]), np.array(g["Wq"]), np.array(g["Wo"]),
+                           np.array(g["K"]), np.array(g["V"]), c["S"], c["scale"])
+        assert_close(out, c["out"], g["tol"], f"mha S={c['S']} scale={c['scale']}")
+
+
+def check_golden_predictor(O):
+    g = load_golden("predictor_tiny.json")
+    s = O.predict_scores(np.array(g["y"]), np.array(g["A"]), np.array(g["Bm"]))
+    assert_close(s, g["scores"], 1e-15, "scores")
+    for c in g["topk"]:
+        got = O.topk_row(np.array(g["scores"][0]), c["k"])
+        assert list(got) == c["set"], f"topk k={c['k']}: {list(got)} != {c['set']}"
+    for c in g["tie_cases"]:
+        got = O.topk_row(np.array(c["scores"]), c["k"])
+        assert list(got) == c["set"], f"ties {c['scores']} k={c['k']}: {list(got)}"
+    for c in g["union_cases"]:
+        got = O.select_sets(np.array(c["scores"]), c["k"], True)
+        assert list(got) == c["set"], f"union {c}: {list(got)}"
+
+
+def check_golden_layer(O):
+    gm, ga, gp, gl = (load_golden(n) for n in
+                      ("mlp_tiny.json", "mha_tiny.json", "predictor_tiny.json", "layer_tiny.json"))
+    layer = dict(W1t=np.array(gm["W1t"]), W2t=np.array(gm["W2t"]), Wq=np.array(ga["Wq"]),
+                 Wo=np.array(ga["Wo"]), K=np.array(ga["K"]), V=np.array(ga["V"]))
+    nxt = dict(A_M=np.array(gp["A"]), B_M=np.array(gp["Bm"]), A_A=np.array(gl["next_A_A"]),
+               B_A=np.array(gl["next_B_A"]), k_m=gl["next_k_m"], k_a=gl["next_k_a"], union=True)
+    y = np.array(gm["y"])
+    y_next, (sm, sa) = O.decode_layer(y, layer, gl["S_M"], gl["S_A"], nxt)
+    assert_close(y_next, gl["y_next"], 1e-12, "layer y_next")
+    assert list(sm) == gl["next_S_M"], f"next S_M {list(sm)}"
+    assert list(sa) == gl["next_S_A"], f"next S_A {list(sa)}"
+
+
+# --------------------------------------------------------------------------- #
+# A1 predictor                                                                #
+# --------------------------------------------------------------------------- #
+
+def check_scores_associative(O):
+    r = _rng(1)
+    for (B, d, rk, N) in [(1, 8, 3, 11), (3, 16, 5, 7), (2, 33, 1, 40)]:
+        y, A, Bm = r.standard_normal((B, d)), r.standard_normal((rk, d)), r.standard_normal((rk, N))
+        s = O.predict_scores(y, A, Bm)
+        # y (A B): the product of the two factors first, a different association.
+        s_ref = y @ (A.T @ Bm)
+        assert_close(s, s_ref, 1e-12, "scores y(AB)")
+
+
+def check_scores_identity_factor(O):
+    r = _rng(2)
+    d, N = 6, 9
+    y, Bm = r.standard_normal((2, d)), r.standard_normal((d, N))
+    s = O.predict_scores(y, np.eye(d), Bm)      # A = I: s = y Bm
+    ref = np.array([[sum(y[b, t] * Bm[t, j] for t in range(d)) for j in range(N)] for b in range(2)])
+    assert_close(s, ref, 1e-13, "scores A=I")
+
+
+def check_scores_bf16_widening(O):
+    # bf16 bit patterns 0x3F80 = 1.0, 0xC000 = -2.0, 0x3E80 = 0.25, 0x0000 = 0.
+    A = np.array([[0x3F80, 0xC000]], dtype=np.uint16)   # [r=1][d=2] = [1, -2]
+    Bm = np.array([[0x3E80, 0x0000, 0xC000]], dtype=np.uint16)  # [1][3] = [0.25, 0, -2]
+    s = O.predict_scores(np.array([[3.0, 1.0]]), A, Bm)  # z = 3 - 2 = 1
+    assert_close(s, [[0.25, 0.0, -2.0]], 0.0, "bf16 widening")
+
+
+# --------------------------------------------------------------------------- #
+# A2 top-k and union                                                          #
+# --------------------------------------------------------------------------- #
+
+def _brute_topk(s, k):
+    """The unique k-subset S with: i in S, j not in S => s_i > s_j or (s_i == s_j and i < j)."""
+    N = len(s)
+    k = max(0, min(k, N))
+    found = []
+    for S in itertools.combinations(range(N), k):
+        Ss = set(S)
+        ok = all((s[i] > s[j]) or (s[i] == s[j] and i < j)
+                 for i in Ss for j in range(N) if j not in Ss)
+        if ok:
+            found.append(list(S))
+    assert len(found) == 1, f"brute force found {len(found)} valid subsets"
+    return found[0]
+
+
+def check_topk_bruteforce(O):
+    r = _rng(3)
+    for trial in range(60):
+        N = int(r.integers(1, 10))
+        # few distinct values so that ties are common; include +-0
+        vals = np.array([-1.0, -0.0, 0.0, 0.5, 2.0, 2.0, 3.0])
+        s = r.choice(vals, size=N) if trial % 2 else r.standard_normal(N)
+        for k in range(0, N + 2):
+            got = list(O.topk_row(s, k))
+            assert got == _brute_topk(list(s), k), f"trial {trial} s={s} k={k}: {got}"
+
+
+def check_topk_lexsort(O):
+    r = _rng(4)
+    for N, k in [(1000, 100), (4096, 409), (257, 0), (300, 300), (50, 1)]:
+        s = np.round(r.standard_normal(N) * 8) / 8       # 3 bits of fraction: many ties
+        got = O.topk_row(s, k)
+        ref = np.sort(np.lexsort((np.arange(N), -s))[:k])
+        assert np.array_equal(got, ref), f"lexsort N={N} k={k}"
+
+
+def check_topk_special(O):
+    N = 37
+    assert list(O.topk_row(np.full(N, 1.5), 5)) == list(range(5)), "constant scores"
+    assert list(O.topk_row(np.arange(N, dtype=float), N)) == list(range(N)), "k = N"
+    assert list(O.topk_row(np.arange(N, dtype=float), 0)) == [], "k = 0"
+    s = np.arange(N, dtype=float)
+    assert list(O.topk_row(s, 3)) == [N - 3, N - 2, N - 1], "increasing scores"
+    r = _rng(5)
+    s2 = r.standard_normal((1, 64))
+    assert list(O.select_sets(s2, 7, True)) == list(O.topk_row(s2[0], 7)), "B=1 union"
+    dup = np.repeat(s2, 3, axis=0)
+    assert list(O.select_sets(dup, 7, True)) == list(O.topk_row(s2[0], 7)), "duplicated tokens"
+    s3 = r.standard_normal((4, 64))
+    per = O.select_sets(s3, 9, False)
+    ref = np.unique(np.concatenate(per))
+    assert list(O.select_sets(s3, 9, True)) == list(ref), "union = set union"
+    for p in per:
+        assert list(p) == sorted(p), "ascending"
+
+
+# --------------------------------------------------------------------------- #
+# A3 sparse MLP                                                               #
+# --------------------------------------------------------------------------- #
+
+def _mlp_data(seed, B=2, d=24, F=40):
+    r = _rng(seed)
+    return (r.standard_normal((B, d)), r.standard_normal((F, d)) * 0.3,
+            r.standard_normal((F, d)) * 0.3)
+
+
+def check_mlp_dense_library(O):
+    y, W1t, W2t = _mlp_data(6)
+    F, d = W1t.shape
+    ffn = torch.nn.Sequential(torch.nn.Linear(d, F), torch.nn.ReLU(), torch.nn.Linear(F, d)).double()
+    with torch.no_grad():
+        ffn[0].weight.copy_(torch.from_numpy(W1t))     # nn.Linear weight is [out][in]
+        ffn[0].bias.zero_()
+        ffn[2].weight.copy_(torch.from_numpy(W2t.T.copy()))
+        ffn[2].bias.zero_()
+        ref = ffn(torch.from_numpy(y)).numpy()
+    out = O.sparse_mlp(y, W1t, W2t, np.arange(F))
+    assert_close(out, ref, 1e-12, "mlp S=all vs nn FFN")
+
+
+def check_mlp_empty_and_additive(O):
+    y, W1t, W2t = _mlp_data(7)
+    F = W1t.shape[0]
+    z = O.sparse_mlp(y, W1t, W2t, [])
+    assert np.array_equal(z, np.zeros_like(y)), "empty set must give exact zero"
+    r = _rng(8)
+    perm = r.permutation(F)
+    S1, S2 = perm[:13], perm[13:29]
+    both = O.sparse_mlp(y, W1t, W2t, np.concatenate([S1, S2]))
+    parts = O.sparse_mlp(y, W1t, W2t, S1) + O.sparse_mlp(y, W1t, W2t, S2)
+    assert_close(both, parts, 1e-12, "mlp additivity")
+
+
+def check_mlp_relu_support(O):
+    y, W1t, W2t = _mlp_data(9, B=1)
+    F = W1t.shape[0]
+    a = y[0] @ W1t.T
+    S_star = np.nonzero(a > 0)[0]
+    assert 0 < len(S_star) < F
+    assert_close(O.sparse_mlp(y, W1t, W2t, S_star), O.sparse_mlp(y, W1t, W2t, np.arange(F)),
+                 1e-12, "ReLU support reproduces dense")
+    S_neg = np.nonzero(a <= 0)[0]
+    assert np.array_equal(O.sparse_mlp(y, W1t, W2t, S_neg), np.zeros_like(y)), "inactive set gives 0"
+
+
+def check_mlp_loops(O):
+    y, W1t, W2t = _mlp_data(10, B=2, d=5, F=7)
+    S = [0, 2, 3, 6]
+    ref = np.zeros_like(y)
+    for b in range(2):
+        for i in S:
+            a = sum(y[b, j] * W1t[i, j] for j in range(5))
+            h = a if a > 0 else 0.0
+            for j in range(5):
+                ref[b, j] += h * W2t[i, j]
+    assert_close(O.sparse_mlp(y, W1t, W2t, S), ref, 1e-13, "mlp loops")
+
+
+def check_mlp_set_order_irrelevant(O):
+    y, W1t, W2t = _mlp_data(11)
+    S = [5, 1, 30, 7]
+    assert_close(O.sparse_mlp(y, W1t, W2t, S), O.sparse_mlp(y, W1t, W2t, sorted(S)), 1e-13,
+                 "set order")
+
+
+# --------------------------------------------------------------------------- #
+# A4 sparse MHA                                                               #
+# --------------------------------------------------------------------------- #
+
+def _mha_data(seed, B=2, d=16, h=3, dh=4, n=7):
+    r = _rng(seed)
+    return (r.standard_normal((B, d)), r.standard_normal((h, dh, d)) * 0.3,
+            r.standard_normal((h, dh, d)) * 0.3, r.standard_normal((B, h, n, dh)),
+            r.standard_normal((B, h, n, dh)))
+
+
+def check_mha_dense_library(O):
+    for scale in (1.0, 0.5):
+        y, Wq, Wo, K, V = _mha_data(12)
+        B, d = y.shape
+        h, dh, _ = Wq.shape
+        yt = torch.from_numpy(y)
+        q = torch.einsum("bd,icd->bic", yt, torch.from_numpy(Wq))      # [B][h][dh]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q.unsqueeze(2), torch.from_numpy(K), torch.from_numpy(V), scale=scale)  # [B][h][1][dh]
+        Z = o.squeeze(2).reshape(B, h * dh)          # concatenate heads in order
+        ref = (Z @ torch.from_numpy(Wo).reshape(h * dh, d)).numpy()
+        out = O.sparse_mha(y, Wq, Wo, K, V, np.arange(h), scale)
+        assert_close(out, ref, 1e-12, f"mha S=all vs sdpa scale={scale}")
+
+
+def check_mha_empty_and_additive(O):
+    y, Wq, Wo, K, V = _mha_data(13, h=5)
+    assert np.array_equal(O.sparse_mha(y, Wq, Wo, K, V, []), np.zeros_like(y)), "empty heads"
+    both = O.sparse_mha(y, Wq, Wo, K, V, [0, 2, 4])
+    parts = O.sparse_mha(y, Wq, Wo, K, V, [0, 4]) + O.sparse_mha(y, Wq, Wo, K, V, [2])
+    assert_close(both, parts, 1e-12, "mha additivity")
+
+
+def check_head_closed_forms(O):
+    r = _rng(14)
+    d, dh = 8, 4
+    y, WQ = r.standard_normal(d), r.standard_normal((d, dh))
+    V1 = r.standard_normal((1, dh))
+    assert_close(O.head_output(y, WQ, r.standard_normal((1, dh)), V1), V1[0], 1e-15, "n=1")
+    Vn = r.standard_normal((6, dh))
+    Keq = np.tile(r.standard_normal((1, dh)), (6, 1))
+    assert_close(O.head_output(y, WQ, Keq, Vn), Vn.mean(axis=0), 1e-13, "equal keys -> mean")
+    q = y @ WQ
+    Kdom = r.standard_normal((6, dh)) * 0.01
+    Kdom[3] = 1e3 * q / np.linalg.norm(q)          # logit of key 3 far above the rest
+    assert_close(O.head_output(y, WQ, Kdom, Vn), Vn[3], 1e-12, "dominant key")
+    # scale: logits scale linearly
+    K = r.standard_normal((5, dh))
+    assert_close(O.head_output(y, WQ, K, Vn[:5], 2.0), O.head_output(y, 2.0 * WQ, K, Vn[:5], 1.0),
+                 1e-12, "scale folds into W^Q")
+
+
+def check_head_mean_shift(O):
+    """Deja Vu page, section 3.2: K_i(x_j, y) = exp(y W^Q (W^K)^T x_j),
+    m_i(y) = sum_j K_i(x_j, y) x_j / sum_j K_i(x_j, y) and H_i(y) = m_i(y) W^V."""
+    r = _rng(15)
+    n, d, dh = 6, 10, 3
+    X = r.standard_normal((n, d)) * 0.5
+    WQ, WK, WV = (r.standard_normal((d, dh)) * 0.5 for _ in range(3))
+    y = r.standard_normal(d)
+    sim = [np.exp(sum(sum(y[a] * WQ[a, c] for a in range(d)) * sum(WK[e, c] * X[j, e] for e in range(d))
+                      for c in range(dh))) for j in range(n)]
+    m = sum(sim[j] * X[j] for j in range(n)) / sum(sim)
+    ref = m @ WV
+    got = O.head_output(y, WQ, X @ WK, X @ WV)
+    assert_close(got, ref, 1e-12, "mean-shift form")
+
+
+# --------------------------------------------------------------------------- #
+# A5 layer                                                                    #
+# --------------------------------------------------------------------------- #
+
+def check_layer_composition(O):
+    y, Wq, Wo, K, V = _mha_data(16, B=2, d=12, h=4, dh=3, n=5)
+    r = _rng(17)
+    F = 20
+    W1t, W2t = r.standard_normal((F, 12)), r.standard_normal((F, 12))
+    layer = dict(W1t=W1t, W2t=W2t, Wq=Wq, Wo=Wo, K=K, V=V)
+    nxt = dict(A_M=r.standard_normal((3, 12)), B_M=r.standard_normal((3, F)),
+               A_A=r.standard_normal((3, 12)), B_A=r.standard_normal((3, 4)),
+               k_m=6, k_a=2, union=True)
+    S_M, S_A = [1, 4, 9, 15], [0, 3]
+    y_next, (sm, sa) = O.decode_layer(y, layer, S_M, S_A, nxt)
+    ref = y + O.sparse_mlp(y, W1t, W2t, S_M) + O.sparse_mha(y, Wq, Wo, K, V, S_A)
+    assert_close(y_next, ref, 1e-13, "layer = y + mlp + mha")
+    sm_ref = O.select_sets(O.predict_scores(y, nxt["A_M"], nxt["B_M"]), 6, True)
+    assert list(sm) == list(sm_ref), "next sets from the layer input"
+    _, none = O.decode_layer(y, layer, S_M, S_A, None)
+    assert none is None
+
+
+def check_stack_lookahead(O):
+    r = _rng(18)
+    d, F, h, dh, n, B = 6, 10, 3, 2, 4, 2
+    def mk():
+        return dict(W1t=r.standard_normal((F, d)), W2t=r.standard_normal((F, d)),
+                    Wq=r.standard_normal((h, dh, d)), Wo=r.standard_normal((h, dh, d)),
+                    K=r.standard_normal((B, h, n, dh)), V=r.standard_normal((B, h, n, dh)),
+                    A_M=r.standard_normal((2, d)), B_M=r.standard_normal((2, F)),
+                    A_A=r.standard_normal((2, d)), B_A=r.standard_normal((2, h)),
+                    k_m=3, k_a=1, union=True)
+    layers = [mk() for _ in range(3)]
+    y0 = r.standard_normal((B, d))
+    yL, used = O.decode_stack(y0, layers)
+    # unrolled by hand: layer 0 predicts its own sets from y0; layer l+1 from y_l
+    def sets(y, L):
+        return (O.select_sets(O.predict_scores(y, L["A_M"], L["B_M"]).astype(np.float32), 3, True),
+                O.select_sets(O.predict_scores(y, L["A_A"], L["B_A"]).astype(np.float32), 1, True))
+    y, expect = y0, []
+    s = sets(y0, layers[0])
+    for l in range(3):
+        expect.append(s)
+        nxt = sets(y, layers[l + 1]) if l + 1 < 3 else None
+        y = y + O.sparse_mlp(y, layers[l]["W1t"], layers[l]["W2t"], s[0]) + \
+            O.sparse_mha(y, layers[l]["Wq"], layers[l]["Wo"], layers[l]["K"], layers[l]["V"], s[1])
+        s = nxt
+    assert_close(yL, y, 1e-12, "stack output")
+    for (a0, a1), (b0, b1) in zip(used, expect):
+        assert list(a0) == list(b0) and list(a1) == list(b1), "stack sets"
+
+
+ALL_CHECKS = [
+    check_golden_mlp, check_golden_mha, check_golden_predictor, check_golden_layer,
+    check_scores_associative, check_scores_identity_factor, check_scores_bf16_widening,
+    check_topk_bruteforce, check_topk_lexsort, check_topk_special,
+    check_mlp_dense_library, check_mlp_empty_and_additive, check_mlp_relu_support,
+    check_mlp_loops, check_mlp_set_order_irrelevant,
+    check_mha_dense_library, check_mha_empty_and_additive, check_head_closed_forms,
+    check_head_mean_shift, check_layer_composition, check_stack_lookahead,
+]
