@@ -1,0 +1,715 @@
+// dv_api.hip - the C ABI of include/dv.h: argument checks, workspace layout,
+// grid planning and launches.  Every check runs on the host before anything is
+// enqueued, so all error codes can be produced without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/dv.h"
+#include "dv_internal.h"
+
+using namespace dv;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+size_t esize(dv_dtype t) { return t == DV_BF16 ? 2 : 4; }
+bool valid_dtype(int t) { return t == DV_F32 || t == DV_BF16; }
+
+#define CHECK_PTR(p) \
+  do { if (!(p)) return fail(DV_EINVAL, "%s: %s is NULL", fn, #p); } while (0)
+#define CHECK_ALIGN(p) \
+  do { if (!aligned16(p)) return fail(DV_EALIGN, "%s: %s is not 16-byte aligned", fn, #p); } while (0)
+
+// ------------------------------------------------------------------------- //
+// device properties                                                         //
+// ------------------------------------------------------------------------- //
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// ------------------------------------------------------------------------- //
+// phase timing                                                              //
+// ------------------------------------------------------------------------- //
+
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;     // 2 events per record
+  size_t used = 0;                  // events handed out
+  struct Rec { int slot; hipEvent_t a, b; };
+  std::vector<Rec> recs;
+};
+TimingState& timing() { static TimingState t; return t; }
+constexpr size_t kTimingPairs = 8192;
+
+// Per-call launch counter (the k-th launch of the current entry point).
+thread_local int t_slot = 0;
+
+int launch(int flags, int bt, const PhaseArgs& a, int grid, int lds, void* stream, const char* fn) {
+  if (grid <= 0) return DV_OK;
+  TimingState& T = timing();
+  hipEvent_t ea = nullptr, eb = nullptr;
+  const int slot = t_slot++;
+  if (T.on) {
+    std::lock_guard<std::mutex> g(T.mu);
+    if (T.used + 2 <= T.pool.size()) {
+      ea = T.pool[T.used++];
+      eb = T.pool[T.used++];
+      T.recs.push_back({slot, ea, eb});
+    }
+  }
+  if (ea) (void)hipEventRecord(ea, static_cast<hipStream_t>(stream));
+  const int err = launch_phase(flags, bt, a, grid, lds, stream);
+  if (eb) (void)hipEventRecord(eb, static_cast<hipStream_t>(stream));
+  if (err != 0)
+    return fail(DV_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString((hipError_t)err));
+  return DV_OK;
+}
+
+// ------------------------------------------------------------------------- //
+// workspace layout                                                          //
+// ------------------------------------------------------------------------- //
+
+struct Ws {
+  size_t off = 0;
+  size_t take(size_t bytes) { size_t o = off; off = align256(off + bytes); return o; }
+};
+
+int pick_bt(int batch) { return batch <= 1 ? 1 : (batch == 2 ? 2 : 4); }
+
+// Axpy segment geometry that does not depend on the device.
+struct AxGeo { int vec, nslices, nbt, chunks_max; };
+AxGeo ax_geo(int batch, int ncols, long long row_stride, dv_dtype wdt, int cap_rows) {
+  AxGeo g;
+  const int full = (wdt == DV_BF16) ? 8 : 4;
+  g.vec = (ncols % full == 0 && row_stride % full == 0) ? full : 1;
+  g.nslices = cdiv(ncols, kThreads * g.vec);
+  const int bt = pick_bt(batch);
+  g.nbt = cdiv(batch, bt);
+  g.chunks_max = std::max(1, std::min(kMaxChunks, cap_rows));
+  return g;
+}
+size_t ax_partial_floats(int batch, int ncols, const AxGeo& g) {
+  return (size_t)g.nbt * g.chunks_max * pick_bt(batch) * ncols;
+}
+size_t ax_tickets(const AxGeo& g) { return (size_t)g.nbt * g.nslices; }
+
+int attn_nsplit_max(int n_ctx) {
+  return std::min(kMaxSplit, std::max(cdiv(n_ctx, kAttnMaxKeys), 64));
+}
+
+struct PredictWs { size_t z, tickets, partial, total; int nt; };
+PredictWs plan_predict(int batch, int d, int r, int N, dv_dtype wdt) {
+  (void)d;
+  PredictWs p; Ws w;
+  const AxGeo g = ax_geo(batch, N, N, wdt, r);
+  p.nt = (int)ax_tickets(g);
+  p.z = w.take((size_t)batch * r * 4);
+  p.tickets = w.take((size_t)p.nt * 4);
+  p.partial = w.take(ax_partial_floats(batch, N, g) * 4);
+  p.total = w.off;
+  return p;
+}
+
+struct SelectWs { size_t bits, total; int nwords; };
+SelectWs plan_select(int batch, int N) {
+  SelectWs p; Ws w;
+  p.nwords = cdiv(N, 32);
+  p.bits = w.take((size_t)batch * p.nwords * 4);
+  p.total = w.off;
+  return p;
+}
+
+struct MlpWs { size_t a, tickets, partial, total; int nt; };
+MlpWs plan_mlp(int batch, int d, int cap, dv_dtype wdt) {
+  MlpWs p; Ws w;
+  const AxGeo g = ax_geo(batch, d, d, wdt, std::max(cap, 1));
+  p.nt = (int)ax_tickets(g);
+  p.a = w.take((size_t)batch * std::max(cap, 1) * 4);
+  p.tickets = w.take((size_t)p.nt * 4);
+  p.partial = w.take(ax_partial_floats(batch, d, g) * 4);
+  p.total = w.off;
+  return p;
+}
+
+struct MhaWs { size_t q, o, part, tickets, partial, total; int nt_attn, nt_ax; };
+MhaWs plan_mha(int batch, int d, int dh, int n_ctx, int cap, dv_dtype wdt) {
+  MhaWs p; Ws w;
+  cap = std::max(cap, 1);
+  const AxGeo g = ax_geo(batch, d, d, wdt, cap * dh);
+  p.nt_attn = batch * cap;
+  p.nt_ax = (int)ax_tickets(g);
+  p.q = w.take((size_t)batch * cap * dh * 4);
+  p.o = w.take((size_t)batch * cap * dh * 4);
+  p.part = w.take((size_t)batch * cap * attn_nsplit_max(n_ctx) * (dh + 2) * 4);
+  p.tickets = w.take((size_t)(p.nt_attn + p.nt_ax) * 4);
+  p.partial = w.take(ax_partial_floats(batch, d, g) * 4);
+  p.total = w.off;
+  return p;
+}
+
+struct LayerWs {
+  size_t a, q, o, part, zm, za, mlp_out, sm, sa, bits_m, bits_a;
+  size_t tickets, p_mlp, p_bm, p_ba, p_wo, total;
+  int t_attn, t_mlp, t_bm, t_ba, t_wo, t_total;
+  int nw_m, nw_a;
+};
+LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int cap_m, int cap_a,
+                   dv_dtype wdt) {
+  LayerWs p; Ws w;
+  cap_m = std::max(cap_m, 1);
+  cap_a = std::max(cap_a, 1);
+  const AxGeo g_mlp = ax_geo(batch, d, d, wdt, cap_m);
+  const AxGeo g_bm = ax_geo(batch, F, F, wdt, r);
+  const AxGeo g_ba = ax_geo(batch, h, h, wdt, r);
+  const AxGeo g_wo = ax_geo(batch, d, d, wdt, cap_a * dh);
+  p.t_attn = batch * cap_a;
+  p.t_mlp = (int)ax_tickets(g_mlp);
+  p.t_bm = (int)ax_tickets(g_bm);
+  p.t_ba = (int)ax_tickets(g_ba);
+  p.t_wo = (int)ax_tickets(g_wo);
+  p.t_total = p.t_attn + p.t_mlp + p.t_bm + p.t_ba + p.t_wo;
+  p.nw_m = cdiv(F, 32);
+  p.nw_a = cdiv(h, 32);
+  p.a = w.take((size_t)batch * cap_m * 4);
+  p.q = w.take((size_t)batch * cap_a * dh * 4);
+  p.o = w.take((size_t)batch * cap_a * dh * 4);
+  p.part = w.take((size_t)batch * cap_a * attn_nsplit_max(n_ctx) * (dh + 2) * 4);
+  p.zm = w.take((size_t)batch * r * 4);
+  p.za = w.take((size_t)batch * r * 4);
+  p.mlp_out = w.take((size_t)batch * d * 4);
+  p.sm = w.take((size_t)batch * F * 4);
+  p.sa = w.take((size_t)batch * h * 4);
+  p.bits_m = w.take((size_t)batch * p.nw_m * 4);
+  p.bits_a = w.take((size_t)batch * p.nw_a * 4);
+  p.tickets = w.take((size_t)p.t_total * 4);
+  p.p_mlp = w.take(ax_partial_floats(batch, d, g_mlp) * 4);
+  p.p_bm = w.take(ax_partial_floats(batch, F, g_bm) * 4);
+  p.p_ba = w.take(ax_partial_floats(batch, h, g_ba) * 4);
+  p.p_wo = w.take(ax_partial_floats(batch, d, g_wo) * 4);
+  p.total = w.off;
+  return p;
+}
+
+// ------------------------------------------------------------------------- //
+// task builders                                                             //
+// ------------------------------------------------------------------------- //
+
+RowList make_list(const int32_t* idx, const int32_t* count, int host_count, int expand, int items) {
+  RowList L;
+  L.idx = idx; L.count = count; L.host_count = host_count; L.expand = expand; L.items = items;
+  return L;
+}
+
+void add_rowdot(RowdotTask& T, const void* W, long long stride, dv_dtype wdt, RowList L, float* out,
+                int out_ld) {
+  RowdotSeg& S = T.seg[T.nseg++];
+  S.W = W; S.row_stride = stride; S.wdt = (wdt == DV_BF16) ? W_BF16 : W_F32;
+  S.rows = L; S.out = out; S.out_ld = out_ld; S.cap = L.host_count * L.expand;
+}
+
+// Rowdot blocks: enough waves for every row, at most a few resident blocks per CU.
+void finish_rowdot(RowdotTask& T, const float* y, int batch, int d, uint32_t* zero, int nzero) {
+  T.y = y; T.batch = batch; T.d = d;
+  T.bt_lds = std::max(1, std::min(pick_bt(batch), kLdsBudget / (d * 4)));
+  int cap = 0;
+  for (int s = 0; s < T.nseg; ++s) cap += T.seg[s].cap;
+  const int want = std::max(1, cdiv(cap, kWaves));
+  T.blocks = std::min(want, device_cus() * 4);
+  T.zero_ptr = zero; T.zero_words = nzero;
+}
+int rowdot_lds(const RowdotTask& T) { return T.bt_lds * T.d * 4; }
+
+// Axpy segment; `chunk_bytes` steers how many row chunks (blocks) it gets.
+void add_axpy(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype wdt, RowList L,
+              const float* coef, int coef_ld, int relu, int ncols, float* partial, uint32_t* tickets,
+              float* out, int out_ld, const float* add0, const float* add1, int add_ld,
+              int accumulate) {
+  AxpySeg& S = T.seg[T.nseg];
+  const int cap_rows = std::max(1, L.host_count * L.expand);
+  const AxGeo g = ax_geo(batch, ncols, stride, wdt, cap_rows);
+  S.W = W; S.row_stride = stride; S.wdt = (wdt == DV_BF16) ? W_BF16 : W_F32;
+  S.rows = L; S.coef = coef; S.coef_ld = coef_ld; S.relu = relu; S.ncols = ncols;
+  S.vec = g.vec; S.nslices = g.nslices; S.nbt = g.nbt;
+  // Aim for about 256 KiB of weights per block at full capacity, spread over 2 blocks/CU.
+  const double bytes = (double)cap_rows * ncols * esize(wdt);
+  int chunks = (int)std::ceil(bytes / (256.0 * 1024.0) / (double)(g.nslices * g.nbt));
+  const int min_chunks = cdiv(device_cus() * 2, g.nslices * g.nbt);
+  chunks = std::max(chunks, std::min(min_chunks, cap_rows));
+  S.nchunks = std::max(1, std::min(chunks, g.chunks_max));
+  S.block0 = T.blocks;
+  S.partial = partial; S.tickets = tickets;
+  S.out = out; S.out_ld = out_ld; S.add0 = add0; S.add1 = add1; S.add_ld = add_ld;
+  S.accumulate = accumulate;
+  T.blocks += S.nbt * S.nslices * S.nchunks;
+  T.nseg++;
+}
+int axpy_lds(int bt) { return (256 + bt * 256) * 4; }
+
+void setup_attn(AttnTask& A, const float* q, int q_ld, const void* K, const void* V, dv_dtype kvdt,
+                int batch, int h, int n, int dh, RowList heads, float scale, float* part,
+                uint32_t* tickets, float* o, int o_ld, int extra_blocks_hint) {
+  A.q = q; A.q_ld = q_ld; A.K = K; A.V = V; A.kvdt = (kvdt == DV_BF16) ? W_BF16 : W_F32;
+  A.batch = batch; A.h = h; A.n = n; A.dh = dh; A.heads = heads; A.scale = scale;
+  const int cap = heads.host_count;
+  // Enough (token, head, split) blocks to spread the cache over the chip, splits of
+  // at least 64 keys and at most kAttnMaxKeys keys.
+  const int base = std::max(1, batch * cap);
+  int ns = cdiv(device_cus() * 2 - std::min(extra_blocks_hint, device_cus()), base);
+  ns = std::max(ns, cdiv(n, kAttnMaxKeys));
+  ns = std::min(ns, std::max(1, cdiv(n, 64)));
+  ns = std::max(1, std::min(ns, attn_nsplit_max(n)));
+  A.nsplit = ns;
+  A.per = cdiv(n, ns);
+  A.part = part; A.tickets = tickets; A.o = o; A.o_ld = o_ld;
+  A.blocks = batch * cap * ns;
+}
+int attn_lds() { return (kAttnMaxKeys + kWaves * 256 + 16) * 4; }
+
+int select_lds() { return (256 + 16) * 4; }
+int union_lds() { return 16 * 4; }
+
+PhaseArgs zero_args() {
+  PhaseArgs a;
+  memset(&a, 0, sizeof a);
+  return a;
+}
+
+// ------------------------------------------------------------------------- //
+// shared validation                                                         //
+// ------------------------------------------------------------------------- //
+
+int check_ws(const char* fn, void* ws, size_t ws_bytes, size_t need) {
+  if (need > 0 && !ws) return fail(DV_EWORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (ws_bytes < need)
+    return fail(DV_EWORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
+  if (ws && !aligned16(ws)) return fail(DV_EALIGN, "%s: ws is not 16-byte aligned", fn);
+  return DV_OK;
+}
+
+int check_d(const char* fn, int d) {
+  if (d <= 0) return fail(DV_EINVAL, "%s: d = %d must be positive", fn, d);
+  if (d % 8 != 0) return fail(DV_EALIGN, "%s: d = %d must be a multiple of 8", fn, d);
+  if (d * 4 > kLdsBudget) return fail(DV_EUNSUPPORTED, "%s: d = %d exceeds %d", fn, d, kLdsBudget / 4);
+  return DV_OK;
+}
+
+int check_nctx(const char* fn, int n) {
+  if (n <= 0) return fail(DV_EINVAL, "%s: n_ctx = %d must be >= 1", fn, n);
+  if (n > kMaxSplit * kAttnMaxKeys)
+    return fail(DV_EUNSUPPORTED, "%s: n_ctx = %d exceeds %d", fn, n, kMaxSplit * kAttnMaxKeys);
+  return DV_OK;
+}
+
+int check_dh(const char* fn, int dh) {
+  if (dh != 32 && dh != 64 && dh != 128 && dh != 256)
+    return fail(DV_EUNSUPPORTED, "%s: dh = %d not in {32, 64, 128, 256}", fn, dh);
+  return DV_OK;
+}
+
+}  // namespace
+
+// =========================================================================== //
+// C ABI                                                                       //
+// =========================================================================== //
+
+extern "C" {
+
+const char* dv_last_error(void) { return g_err.c_str(); }
+
+int dv_version(void) { return 100; }
+
+static size_t ws_bytes_for(int op, const dv_shape* s, dv_dtype wdt) {
+  const int B = s->batch;
+  switch (op) {
+    case DV_OP_PREDICT: return plan_predict(B, s->d, s->r, s->N, wdt).total;
+    case DV_OP_SELECT_TOPK: return plan_select(B, s->N).total;
+    case DV_OP_SPARSE_MLP: return plan_mlp(B, s->d, s->max_count_m, wdt).total;
+    case DV_OP_SPARSE_MHA: return plan_mha(B, s->d, s->dh, s->n_ctx, s->max_count_a, wdt).total;
+    default:
+      return plan_layer(B, s->d, s->F, s->h, s->dh, s->n_ctx, s->r, s->max_count_m, s->max_count_a,
+                        wdt).total;
+  }
+}
+
+size_t dv_workspace_bytes(int op, const dv_shape* s) {
+  const char* fn = "dv_workspace_bytes";
+  if (!s) { fail(DV_EINVAL, "%s: shape is NULL", fn); return 0; }
+  const int B = s->batch;
+  if (B <= 0) { fail(DV_EINVAL, "%s: batch = %d", fn, B); return 0; }
+  switch (op) {
+    case DV_OP_PREDICT:
+      if (s->r <= 0 || s->N <= 0 || s->d <= 0) { fail(DV_EINVAL, "%s: bad predict shape", fn); return 0; }
+      break;
+    case DV_OP_SELECT_TOPK:
+      if (s->N <= 0) { fail(DV_EINVAL, "%s: N = %d", fn, s->N); return 0; }
+      break;
+    case DV_OP_SPARSE_MLP:
+      if (s->d <= 0 || s->max_count_m < 0) { fail(DV_EINVAL, "%s: bad mlp shape", fn); return 0; }
+      break;
+    case DV_OP_SPARSE_MHA:
+      if (s->d <= 0 || s->dh <= 0 || s->n_ctx <= 0 || s->max_count_a < 0) {
+        fail(DV_EINVAL, "%s: bad mha shape", fn); return 0;
+      }
+      break;
+    case DV_OP_DECODE_LAYER:
+      if (s->d <= 0 || s->F <= 0 || s->h <= 0 || s->dh <= 0 || s->n_ctx <= 0 || s->r <= 0 ||
+          s->max_count_m < 0 || s->max_count_a < 0) {
+        fail(DV_EINVAL, "%s: bad layer shape", fn); return 0;
+      }
+      break;
+    default:
+      fail(DV_EINVAL, "%s: unknown op %d", fn, op);
+      return 0;
+  }
+  // The layout depends on the weight dtype only through the column split of the
+  // axpy tiles; report the larger of the two so one size serves both.
+  return std::max(ws_bytes_for(op, s, DV_BF16), ws_bytes_for(op, s, DV_F32));
+}
+
+int dv_predict(const float* y, int batch, int d, const void* A, const void* Bm, int r, int N,
+               dv_dtype wdt, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dv_predict";
+  t_slot = 0;
+  CHECK_PTR(y); CHECK_PTR(A); CHECK_PTR(Bm); CHECK_PTR(scores);
+  if (batch <= 0) return fail(DV_EINVAL, "%s: batch = %d", fn, batch);
+  if (r <= 0 || N <= 0) return fail(DV_EINVAL, "%s: r = %d, N = %d", fn, r, N);
+  if (!valid_dtype(wdt)) return fail(DV_EINVAL, "%s: bad dtype %d", fn, (int)wdt);
+  if (int e = check_d(fn, d)) return e;
+  CHECK_ALIGN(y); CHECK_ALIGN(A); CHECK_ALIGN(Bm); CHECK_ALIGN(scores);
+  const PredictWs P = plan_predict(batch, d, r, N, wdt);
+  if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
+  char* w = static_cast<char*>(ws);
+  float* z = reinterpret_cast<float*>(w + P.z);
+  uint32_t* tickets = reinterpret_cast<uint32_t*>(w + P.tickets);
+  const int bt = pick_bt(batch);
+
+  PhaseArgs a1 = zero_args();
+  add_rowdot(a1.rowdot, A, d, wdt, make_list(nullptr, nullptr, r, 1, r), z, r);
+  finish_rowdot(a1.rowdot, y, batch, d, tickets, P.nt);
+  if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
+
+  PhaseArgs a2 = zero_args();
+  add_axpy(a2.axpy, batch, Bm, N, wdt, make_list(nullptr, nullptr, r, 1, r), z, r, 0, N,
+           reinterpret_cast<float*>(w + P.partial), tickets, scores, N, nullptr, nullptr, 0, 0);
+  a2.axpy.batch = batch;
+  return launch(T_AXPY, bt, a2, a2.axpy.blocks, axpy_lds(bt), stream, fn);
+}
+
+int dv_select_topk(const float* scores, int batch, int N, int k, int union_rows, int32_t* idx,
+                   int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dv_select_topk";
+  t_slot = 0;
+  CHECK_PTR(scores); CHECK_PTR(idx); CHECK_PTR(count);
+  if (batch <= 0) return fail(DV_EINVAL, "%s: batch = %d", fn, batch);
+  if (N <= 0) return fail(DV_EINVAL, "%s: N = %d", fn, N);
+  if (k < 0 || k > N) return fail(DV_EINVAL, "%s: k = %d not in [0, N = %d]", fn, k, N);
+  CHECK_ALIGN(scores); CHECK_ALIGN(idx); CHECK_ALIGN(count);
+  const bool use_bits = union_rows && batch > 1;
+  const SelectWs P = plan_select(batch, N);
+  if (use_bits) {
+    if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
+  }
+  PhaseArgs a = zero_args();
+  SelectProblem& sp = a.select.p[0];
+  sp.scores = scores; sp.ld = N; sp.N = N; sp.k = k;
+  sp.mode = use_bits ? 1 : 0;
+  sp.idx = idx; sp.count = count;
+  sp.bits = use_bits ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + P.bits) : nullptr;
+  sp.nwords = P.nwords;
+  a.select.np = 1; a.select.batch = batch; a.select.blocks = batch;
+  if (int e = launch(T_SELECT, 1, a, a.select.blocks, select_lds(), stream, fn)) return e;
+  if (!use_bits) return DV_OK;
+  PhaseArgs u = zero_args();
+  UnionProblem& up = u.uni.p[0];
+  up.bits = sp.bits; up.nwords = P.nwords; up.N = N; up.batch = batch; up.idx = idx; up.count = count;
+  u.uni.np = 1; u.uni.blocks = 1;
+  return launch(T_UNION, 1, u, 1, union_lds(), stream, fn);
+}
+
+int dv_sparse_mlp(const float* y, int batch, int d, const void* W1t, const void* W2t, int F,
+                  dv_dtype wdt, const int32_t* idx, const int32_t* count, int max_count, float* out,
+                  int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dv_sparse_mlp";
+  t_slot = 0;
+  CHECK_PTR(y); CHECK_PTR(W1t); CHECK_PTR(W2t); CHECK_PTR(idx); CHECK_PTR(count); CHECK_PTR(out);
+  if (batch <= 0) return fail(DV_EINVAL, "%s: batch = %d", fn, batch);
+  if (F <= 0) return fail(DV_EINVAL, "%s: F = %d", fn, F);
+  if (max_count < 0 || max_count > F) return fail(DV_EINVAL, "%s: max_count = %d not in [0, F]", fn, max_count);
+  if (!valid_dtype(wdt)) return fail(DV_EINVAL, "%s: bad dtype %d", fn, (int)wdt);
+  if (int e = check_d(fn, d)) return e;
+  CHECK_ALIGN(y); CHECK_ALIGN(W1t); CHECK_ALIGN(W2t); CHECK_ALIGN(idx); CHECK_ALIGN(count);
+  CHECK_ALIGN(out);
+  if (out == y) return fail(DV_EINVAL, "%s: out must not alias y", fn);
+  const MlpWs P = plan_mlp(batch, d, max_count, wdt);
+  if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
+  char* w = static_cast<char*>(ws);
+  const int cap = std::max(max_count, 1);
+  float* act = reinterpret_cast<float*>(w + P.a);
+  uint32_t* tickets = reinterpret_cast<uint32_t*>(w + P.tickets);
+  const int bt = pick_bt(batch);
+  const RowList L = make_list(idx, count, max_count, 1, F);
+
+  PhaseArgs a1 = zero_args();
+  add_rowdot(a1.rowdot, W1t, d, wdt, L, act, cap);
+  finish_rowdot(a1.rowdot, y, batch, d, tickets, P.nt);
+  if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
+
+  PhaseArgs a2 = zero_args();
+  add_axpy(a2.axpy, batch, W2t, d, wdt, L, act, cap, 1, d, reinterpret_cast<float*>(w + P.partial),
+           tickets, out, d, nullptr, nullptr, 0, accumulate);
+  a2.axpy.batch = batch;
+  return launch(T_AXPY, bt, a2, a2.axpy.blocks, axpy_lds(bt), stream, fn);
+}
+
+int dv_sparse_mha(const float* y, int batch, int d, int h, int dh, const void* Wq, const void* Wo,
+                  dv_dtype wdt, const void* K, const void* V, int n_ctx, dv_dtype kvdt,
+                  const int32_t* heads, const int32_t* count, int max_count, float scale, float* out,
+                  int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dv_sparse_mha";
+  t_slot = 0;
+  CHECK_PTR(y); CHECK_PTR(Wq); CHECK_PTR(Wo); CHECK_PTR(K); CHECK_PTR(V); CHECK_PTR(heads);
+  CHECK_PTR(count); CHECK_PTR(out);
+  if (batch <= 0) return fail(DV_EINVAL, "%s: batch = %d", fn, batch);
+  if (h <= 0) return fail(DV_EINVAL, "%s: h = %d", fn, h);
+  if (int e = check_nctx(fn, n_ctx)) return e;
+  if (max_count < 0 || max_count > h) return fail(DV_EINVAL, "%s: max_count = %d not in [0, h]", fn, max_count);
+  if (!valid_dtype(wdt) || !valid_dtype(kvdt)) return fail(DV_EINVAL, "%s: bad dtype", fn);
+  if (!(scale == scale)) return fail(DV_EINVAL, "%s: scale is NaN", fn);
+  if (int e = check_d(fn, d)) return e;
+  if (int e = check_dh(fn, dh)) return e;
+  CHECK_ALIGN(y); CHECK_ALIGN(Wq); CHECK_ALIGN(Wo); CHECK_ALIGN(K); CHECK_ALIGN(V);
+  CHECK_ALIGN(heads); CHECK_ALIGN(count); CHECK_ALIGN(out);
+  if (out == y) return fail(DV_EINVAL, "%s: out must not alias y", fn);
+  const MhaWs P = plan_mha(batch, d, dh, n_ctx, max_count, wdt);
+  if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
+  char* w = static_cast<char*>(ws);
+  const int cap = std::max(max_count, 1);
+  float* q = reinterpret_cast<float*>(w + P.q);
+  float* o = reinterpret_cast<float*>(w + P.o);
+  uint32_t* t_attn = reinterpret_cast<uint32_t*>(w + P.tickets);
+  uint32_t* t_ax = t_attn + P.nt_attn;
+  const int bt = pick_bt(batch);
+  const RowList L = make_list(heads, count, max_count, dh, h);
+
+  PhaseArgs a1 = zero_args();
+  add_rowdot(a1.rowdot, Wq, d, wdt, L, q, cap * dh);
+  finish_rowdot(a1.rowdot, y, batch, d, t_attn, P.nt_attn + P.nt_ax);
+  if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
+
+  PhaseArgs a2 = zero_args();
+  setup_attn(a2.attn, q, cap * dh, K, V, kvdt, batch, h, n_ctx, dh,
+             make_list(heads, count, max_count, 1, h), scale, reinterpret_cast<float*>(w + P.part),
+             t_attn, o, cap * dh, 0);
+  if (max_count > 0) {
+    if (int e = launch(T_ATTN, 1, a2, a2.attn.blocks, attn_lds(), stream, fn)) return e;
+  }
+
+  PhaseArgs a3 = zero_args();
+  add_axpy(a3.axpy, batch, Wo, d, wdt, L, o, cap * dh, 0, d, reinterpret_cast<float*>(w + P.partial),
+           t_ax, out, d, nullptr, nullptr, 0, accumulate);
+  a3.axpy.batch = batch;
+  return launch(T_AXPY, bt, a3, a3.axpy.blocks, axpy_lds(bt), stream, fn);
+}
+
+int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const float* y_in, float* y_out,
+                    const int32_t* idx_m, const int32_t* count_m, int max_count_m,
+                    const int32_t* idx_a, const int32_t* count_a, int max_count_a,
+                    int32_t* next_idx_m, int32_t* next_count_m, int32_t* next_idx_a,
+                    int32_t* next_count_a, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dv_decode_layer";
+  t_slot = 0;
+  CHECK_PTR(L); CHECK_PTR(y_in); CHECK_PTR(y_out);
+  CHECK_PTR(idx_m); CHECK_PTR(count_m); CHECK_PTR(idx_a); CHECK_PTR(count_a);
+  if (batch <= 0) return fail(DV_EINVAL, "%s: batch = %d", fn, batch);
+  const int d = L->d, F = L->F, h = L->h, dh = L->dh, n = L->n_ctx;
+  if (F <= 0 || h <= 0) return fail(DV_EINVAL, "%s: F = %d, h = %d", fn, F, h);
+  if (int e = check_nctx(fn, n)) return e;
+  if (!valid_dtype(L->wdt) || !valid_dtype(L->kvdt)) return fail(DV_EINVAL, "%s: bad dtype", fn);
+  if (!(L->scale == L->scale)) return fail(DV_EINVAL, "%s: scale is NaN", fn);
+  if (int e = check_d(fn, d)) return e;
+  if (int e = check_dh(fn, dh)) return e;
+  if (max_count_m < 0 || max_count_m > F) return fail(DV_EINVAL, "%s: max_count_m = %d", fn, max_count_m);
+  if (max_count_a < 0 || max_count_a > h) return fail(DV_EINVAL, "%s: max_count_a = %d", fn, max_count_a);
+  CHECK_PTR(L->W1t); CHECK_PTR(L->W2t); CHECK_PTR(L->Wq); CHECK_PTR(L->Wo); CHECK_PTR(L->K);
+  CHECK_PTR(L->V);
+  CHECK_ALIGN(y_in); CHECK_ALIGN(y_out); CHECK_ALIGN(idx_m); CHECK_ALIGN(count_m);
+  CHECK_ALIGN(idx_a); CHECK_ALIGN(count_a);
+  CHECK_ALIGN(L->W1t); CHECK_ALIGN(L->W2t); CHECK_ALIGN(L->Wq); CHECK_ALIGN(L->Wo);
+  CHECK_ALIGN(L->K); CHECK_ALIGN(L->V);
+  int r = 1, Fn = 1, hn = 1, km = 0, ka = 0;
+  if (nx) {
+    CHECK_PTR(next_idx_m); CHECK_PTR(next_count_m); CHECK_PTR(next_idx_a); CHECK_PTR(next_count_a);
+    CHECK_PTR(nx->A_M); CHECK_PTR(nx->B_M); CHECK_PTR(nx->A_A); CHECK_PTR(nx->B_A);
+    CHECK_ALIGN(next_idx_m); CHECK_ALIGN(next_count_m); CHECK_ALIGN(next_idx_a);
+    CHECK_ALIGN(next_count_a);
+    CHECK_ALIGN(nx->A_M); CHECK_ALIGN(nx->B_M); CHECK_ALIGN(nx->A_A); CHECK_ALIGN(nx->B_A);
+    if (nx->d != d) return fail(DV_EINVAL, "%s: next->d = %d differs from d = %d", fn, nx->d, d);
+    if (nx->wdt != L->wdt) return fail(DV_EUNSUPPORTED, "%s: next layer weight dtype differs", fn);
+    r = nx->r; Fn = nx->F; hn = nx->h; km = nx->k_m; ka = nx->k_a;
+    if (r <= 0 || Fn <= 0 || hn <= 0) return fail(DV_EINVAL, "%s: next r/F/h", fn);
+    if (km < 0 || km > Fn || ka < 0 || ka > hn)
+      return fail(DV_EINVAL, "%s: next k_m = %d / k_a = %d out of range", fn, km, ka);
+  }
+  const dv_dtype wdt = L->wdt;
+  const LayerWs P = plan_layer(batch, d, std::max(F, Fn), std::max(h, hn), dh, n, r, max_count_m,
+                               max_count_a, wdt);
+  if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
+
+  char* w = static_cast<char*>(ws);
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  const int cap_m = std::max(max_count_m, 1), cap_a = std::max(max_count_a, 1);
+  uint32_t* tk = reinterpret_cast<uint32_t*>(w + P.tickets);
+  uint32_t* t_attn = tk;
+  uint32_t* t_mlp = t_attn + P.t_attn;
+  uint32_t* t_bm = t_mlp + P.t_mlp;
+  uint32_t* t_ba = t_bm + P.t_bm;
+  uint32_t* t_wo = t_ba + P.t_ba;
+  const int bt = pick_bt(batch);
+  const RowList LM = make_list(idx_m, count_m, max_count_m, 1, F);
+  const RowList LQ = make_list(idx_a, count_a, max_count_a, dh, h);
+  const RowList LH = make_list(idx_a, count_a, max_count_a, 1, h);
+
+  // Phase 1: every gathered row dotted with y_in (W1 rows of S_M, W^Q columns of
+  // S_A, and the next layer's predictor factors A_M, A_A).
+  PhaseArgs a1 = zero_args();
+  add_rowdot(a1.rowdot, L->W1t, d, wdt, LM, fp(P.a), cap_m);
+  add_rowdot(a1.rowdot, L->Wq, d, wdt, LQ, fp(P.q), cap_a * dh);
+  if (nx) {
+    add_rowdot(a1.rowdot, nx->A_M, d, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r);
+    add_rowdot(a1.rowdot, nx->A_A, d, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r);
+  }
+  finish_rowdot(a1.rowdot, y_in, batch, d, tk, P.t_total);
+  if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
+
+  // Phase 2: attention over the cache for S_A; ReLU(a) W2 rows; predictor scores.
+  PhaseArgs a2 = zero_args();
+  add_axpy(a2.axpy, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, 1, d, fp(P.p_mlp), t_mlp,
+           fp(P.mlp_out), d, nullptr, nullptr, 0, 0);
+  if (nx) {
+    add_axpy(a2.axpy, batch, nx->B_M, Fn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r, 0,
+             Fn, fp(P.p_bm), t_bm, fp(P.sm), Fn, nullptr, nullptr, 0, 0);
+    add_axpy(a2.axpy, batch, nx->B_A, hn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r, 0,
+             hn, fp(P.p_ba), t_ba, fp(P.sa), hn, nullptr, nullptr, 0, 0);
+  }
+  a2.axpy.batch = batch;
+  int flags2 = T_AXPY;
+  if (max_count_a > 0) {
+    setup_attn(a2.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n, dh, LH, L->scale,
+               fp(P.part), t_attn, fp(P.o), cap_a * dh, a2.axpy.blocks);
+    flags2 |= T_ATTN;
+    a2.b_attn = 0;
+    a2.b_axpy = a2.attn.blocks;
+  }
+  const int lds2 = std::max(axpy_lds(bt), (flags2 & T_ATTN) ? attn_lds() : 0);
+  if (int e = launch(flags2, bt, a2, a2.attn.blocks + a2.axpy.blocks, lds2, stream, fn)) return e;
+
+  // Phase 3: W^O rows scaled by the head outputs, added to y_in + MLP; the next
+  // layer's top-k runs beside it.
+  PhaseArgs a3 = zero_args();
+  add_axpy(a3.axpy, batch, L->Wo, d, wdt, LQ, fp(P.o), cap_a * dh, 0, d, fp(P.p_wo), t_wo, y_out, d,
+           y_in, fp(P.mlp_out), d, 0);
+  a3.axpy.batch = batch;
+  int flags3 = T_AXPY;
+  const bool use_bits = batch > 1;
+  if (nx) {
+    SelectTask& S = a3.select;
+    S.p[0].scores = fp(P.sm); S.p[0].ld = Fn; S.p[0].N = Fn; S.p[0].k = km;
+    S.p[0].mode = use_bits ? 1 : 0; S.p[0].idx = next_idx_m; S.p[0].count = next_count_m;
+    S.p[0].bits = reinterpret_cast<uint32_t*>(w + P.bits_m); S.p[0].nwords = cdiv(Fn, 32);
+    S.p[1].scores = fp(P.sa); S.p[1].ld = hn; S.p[1].N = hn; S.p[1].k = ka;
+    S.p[1].mode = use_bits ? 1 : 0; S.p[1].idx = next_idx_a; S.p[1].count = next_count_a;
+    S.p[1].bits = reinterpret_cast<uint32_t*>(w + P.bits_a); S.p[1].nwords = cdiv(hn, 32);
+    S.np = 2; S.batch = batch; S.blocks = 2 * batch;
+    flags3 |= T_SELECT;
+    a3.b_select = 0;
+    a3.b_axpy = S.blocks;
+  }
+  const int lds3 = std::max(axpy_lds(bt), (flags3 & T_SELECT) ? select_lds() : 0);
+  if (int e = launch(flags3, bt, a3, a3.select.blocks + a3.axpy.blocks, lds3, stream, fn)) return e;
+
+  if (nx && use_bits) {
+    PhaseArgs a4 = zero_args();
+    UnionTask& U = a4.uni;
+    U.p[0].bits = a3.select.p[0].bits; U.p[0].nwords = a3.select.p[0].nwords; U.p[0].N = Fn;
+    U.p[0].batch = batch; U.p[0].idx = next_idx_m; U.p[0].count = next_count_m;
+    U.p[1].bits = a3.select.p[1].bits; U.p[1].nwords = a3.select.p[1].nwords; U.p[1].N = hn;
+    U.p[1].batch = batch; U.p[1].idx = next_idx_a; U.p[1].count = next_count_a;
+    U.np = 2; U.blocks = 2;
+    if (int e = launch(T_UNION, 1, a4, 2, union_lds(), stream, fn)) return e;
+  }
+  return DV_OK;
+}
+
+int dv_timing_enable(int on) {
+  TimingState& T = timing();
+  std::lock_guard<std::mutex> g(T.mu);
+  if (on && T.pool.empty()) {
+    T.pool.resize(2 * kTimingPairs);
+    for (auto& e : T.pool) {
+      if (hipEventCreate(&e) != hipSuccess) {
+        T.pool.clear();
+        return fail(DV_EHIP, "dv_timing_enable: hipEventCreate failed");
+      }
+    }
+  }
+  T.on = on != 0;
+  return DV_OK;
+}
+
+int dv_timing_read(float* ms_sum, int* launches, int max_slots, int* n_slots) {
+  const char* fn = "dv_timing_read";
+  CHECK_PTR(ms_sum); CHECK_PTR(launches); CHECK_PTR(n_slots);
+  TimingState& T = timing();
+  std::lock_guard<std::mutex> g(T.mu);
+  for (int i = 0; i < max_slots; ++i) { ms_sum[i] = 0.f; launches[i] = 0; }
+  int filled = 0;
+  for (const auto& r : T.recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(DV_EHIP, "%s: event sync failed", fn);
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(DV_EHIP, "%s: elapsed failed", fn);
+    if (r.slot < max_slots) {
+      ms_sum[r.slot] += ms;
+      launches[r.slot] += 1;
+      filled = std::max(filled, r.slot + 1);
+    }
+  }
+  T.recs.clear();
+  T.used = 0;
+  *n_slots = filled;
+  return DV_OK;
+}
+
+}  // extern "C"

@@ -169,6 +169,16 @@ def make_layer(cfg: LayerConfig, device="cpu", layer: int = 0, batch: int | None
     return LayerTensors(cfg, W1t, W2t, Wq, Wo, K, V, A_M, B_M, A_A, B_A)
 
 
+def make_predictor(cfg: LayerConfig, device="cpu", layer: int = 0):
+    """Only the predictor factors (A_M, B_M, A_A, B_A) of a layer, same seeds as make_layer."""
+    wdt = cfg.torch_wdtype
+    s = lambda name: seed_of(cfg.cfg_id, layer, name)  # noqa: E731
+    return dict(A_M=_normal((cfg.r, cfg.d), cfg.pred_std, s("A_M"), device, wdt),
+                B_M=_normal((cfg.r, cfg.F), cfg.pred_std, s("B_M"), device, wdt),
+                A_A=_normal((cfg.r, cfg.d), cfg.pred_std, s("A_A"), device, wdt),
+                B_A=_normal((cfg.r, cfg.h), cfg.pred_std, s("B_A"), device, wdt))
+
+
 def random_index_set(N: int, count: int, seed: int) -> torch.Tensor:
     """A seeded ascending subset of [0, N) of the given size (int32), for tests that
     feed the sparse blocks a set directly rather than through the predictor."""
