@@ -1,0 +1,77 @@
+"""Algorithmic bytes and flops of the decode step (host arithmetic for reporting).
+
+"Algorithmic" means what the method must move, not what a kernel happens to
+fetch: each selected row, head weight and cached key/value is counted once, in
+its stored width.  Counted per decode layer, with the actual (union) set sizes.
+
+Sources for what is read: Deja Vu page, section 2.3, Eq. (1) reads W1_i and W2_i
+for i in S_M; Eq. (2) reads W_i^Q, W_i^O for i in S_A and the cached X W_i^K,
+X W_i^V of every token; the predictor reads both low-rank factors in full.
+KV size per token follows the survey-notes page (KV cache sizing): 2 tensors x
+hidden width x layers x bytes per element.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+
+def kv_bytes_per_token(hidden: int, layers: int, bytes_per_elem: int = 2) -> int:
+    """K and V of one token across layers: 2 * hidden * layers * bytes."""
+    return 2 * hidden * layers * bytes_per_elem
+
+
+@dataclass
+class StepBytes:
+    mlp: int            # W1 and W2 rows of S_M
+    attn_weights: int   # W^Q and W^O rows of S_A
+    kv: int             # K and V rows of S_A for every token
+    io: int             # y in, y out (and the MLP partial the combine reads)
+    predictor: int      # A_M, B_M, A_A, B_A in full
+
+    @property
+    def selected(self) -> int:
+        return self.mlp + self.attn_weights + self.kv + self.io
+
+    @property
+    def total(self) -> int:
+        return self.selected + self.predictor
+
+
+def step_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
+               u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True) -> StepBytes:
+    mlp = u_m * 2 * d * w_bytes
+    attn_w = u_a * 2 * dh * d * w_bytes
+    kv = batch * u_a * 2 * n_ctx * dh * kv_bytes
+    io = 2 * batch * d * 4
+    pred = (2 * d * r + r * F + r * h) * w_bytes if with_predictor else 0
+    return StepBytes(mlp, attn_w, kv, io, pred)
+
+
+def step_flops(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
+               u_a: int, with_predictor: bool = True) -> int:
+    f = batch * (4 * d * u_m + u_a * (4 * d * dh + 4 * n_ctx * dh))
+    if with_predictor:
+        f += batch * 2 * (2 * d * r + r * F + r * h)
+    return f
+
+
+def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
+                u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True):
+    """Bytes each launch of the look-ahead decode layer must move.
+
+    phase 1 (gathered row dots): W1 rows, W^Q rows, predictor A factors, y.
+    phase 2 (attention + scaled row sums): W2 rows, K/V of the selected heads,
+             predictor B factors, the MLP result written.
+    phase 3 (output projection + combine, next layer's top-k): W^O rows,
+             y_in and the MLP result read, y_out written, scores read by the top-k.
+    Small intermediates handed between launches (row dots, q, head outputs,
+    scores written: under 1 MB at batch 1) are not counted.
+    """
+    p1 = u_m * d * w_bytes + u_a * dh * d * w_bytes + batch * d * 4
+    p2 = u_m * d * w_bytes + batch * u_a * 2 * n_ctx * dh * kv_bytes + batch * d * 4
+    p3 = u_a * dh * d * w_bytes + 3 * batch * d * 4
+    if with_predictor:
+        p1 += 2 * r * d * w_bytes
+        p2 += (r * F + r * h) * w_bytes
+        p3 += batch * (F + h) * 4
+    return [p1, p2, p3]

@@ -115,7 +115,7 @@ AxGeo ax_geo(int batch, int ncols, long long row_stride, dv_dtype wdt, int cap_r
   AxGeo g;
   const int full = (wdt == DV_BF16) ? 8 : 4;
   g.vec = (ncols % full == 0 && row_stride % full == 0) ? full : 1;
-  g.nslices = cdiv(ncols, kThreads * g.vec);
+  g.nslices = cdiv(ncols, kAxSliceLanes * g.vec);
   const int bt = pick_bt(batch);
   g.nbt = cdiv(batch, bt);
   g.chunks_max = std::max(1, std::min(kMaxChunks, cap_rows));
@@ -126,8 +126,19 @@ size_t ax_partial_floats(int batch, int ncols, const AxGeo& g) {
 }
 size_t ax_tickets(const AxGeo& g) { return (size_t)g.nbt * g.nslices; }
 
-int attn_nsplit_max(int n_ctx) {
-  return std::min(kMaxSplit, std::max(cdiv(n_ctx, kAttnMaxKeys), 64));
+int attn_nsplit_max(int n_ctx) { return std::max(1, std::min(kMaxSplit, cdiv(n_ctx, 64))); }
+
+// Top-k scratch for one problem (N scores per row, `batch` rows).
+struct TopkWs { size_t bits, cand, ccount, need; int nseg, nwords; };
+TopkWs plan_topk_parts(Ws& w, int batch, int N) {
+  TopkWs t;
+  t.nseg = cdiv(N, kSegElems);
+  t.nwords = cdiv(N, 32);
+  t.bits = w.take((size_t)batch * t.nwords * 4);
+  t.cand = w.take(((size_t)batch * t.nseg * kSegElems + (size_t)batch * N) * 8);
+  t.ccount = w.take((size_t)batch * t.nseg * 4);
+  t.need = w.take((size_t)batch * 4);
+  return t;
 }
 
 struct PredictWs { size_t z, tickets, partial, total; int nt; };
@@ -143,11 +154,16 @@ PredictWs plan_predict(int batch, int d, int r, int N, dv_dtype wdt) {
   return p;
 }
 
-struct SelectWs { size_t bits, total; int nwords; };
+// Zero region first: histogram [batch][kHistBins] and the union ticket.
+struct SelectWs { size_t zero, hist, ticket, total; int zero_words; TopkWs t; };
 SelectWs plan_select(int batch, int N) {
   SelectWs p; Ws w;
-  p.nwords = cdiv(N, 32);
-  p.bits = w.take((size_t)batch * p.nwords * 4);
+  p.zero = w.off;
+  p.hist = w.take((size_t)batch * kHistBins * 4);
+  p.ticket = p.hist + (size_t)batch * kHistBins * 4;
+  w.off = align256(p.ticket + 4);
+  p.zero_words = (int)((p.ticket + 4 - p.zero) / 4);
+  p.t = plan_topk_parts(w, batch, N);
   p.total = w.off;
   return p;
 }
@@ -180,11 +196,13 @@ MhaWs plan_mha(int batch, int d, int dh, int n_ctx, int cap, dv_dtype wdt) {
   return p;
 }
 
+// Zero region first: all tickets, both score histograms and both union tickets.
 struct LayerWs {
-  size_t a, q, o, part, zm, za, mlp_out, sm, sa, bits_m, bits_a;
-  size_t tickets, p_mlp, p_bm, p_ba, p_wo, total;
-  int t_attn, t_mlp, t_bm, t_ba, t_wo, t_total;
-  int nw_m, nw_a;
+  size_t zero, tickets, hist_m, hist_a, uticket;
+  size_t a, q, o, part, zm, za, mlp_out, sm, sa;
+  size_t p_mlp, p_bm, p_ba, p_wo, total;
+  int t_attn, t_mlp, t_bm, t_ba, t_wo, t_total, zero_words;
+  TopkWs tm, ta;
 };
 LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int cap_m, int cap_a,
                    dv_dtype wdt) {
@@ -201,8 +219,14 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   p.t_ba = (int)ax_tickets(g_ba);
   p.t_wo = (int)ax_tickets(g_wo);
   p.t_total = p.t_attn + p.t_mlp + p.t_bm + p.t_ba + p.t_wo;
-  p.nw_m = cdiv(F, 32);
-  p.nw_a = cdiv(h, 32);
+  // zero region: tickets | hist_m | hist_a | union tickets (2)
+  p.zero = w.off;
+  p.tickets = p.zero;
+  p.hist_m = p.tickets + (size_t)p.t_total * 4;
+  p.hist_a = p.hist_m + (size_t)batch * kHistBins * 4;
+  p.uticket = p.hist_a + (size_t)batch * kHistBins * 4;
+  w.off = align256(p.uticket + 8);
+  p.zero_words = (int)((p.uticket + 8 - p.zero) / 4);
   p.a = w.take((size_t)batch * cap_m * 4);
   p.q = w.take((size_t)batch * cap_a * dh * 4);
   p.o = w.take((size_t)batch * cap_a * dh * 4);
@@ -212,13 +236,12 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   p.mlp_out = w.take((size_t)batch * d * 4);
   p.sm = w.take((size_t)batch * F * 4);
   p.sa = w.take((size_t)batch * h * 4);
-  p.bits_m = w.take((size_t)batch * p.nw_m * 4);
-  p.bits_a = w.take((size_t)batch * p.nw_a * 4);
-  p.tickets = w.take((size_t)p.t_total * 4);
   p.p_mlp = w.take(ax_partial_floats(batch, d, g_mlp) * 4);
   p.p_bm = w.take(ax_partial_floats(batch, F, g_bm) * 4);
   p.p_ba = w.take(ax_partial_floats(batch, h, g_ba) * 4);
   p.p_wo = w.take(ax_partial_floats(batch, d, g_wo) * 4);
+  p.tm = plan_topk_parts(w, batch, F);
+  p.ta = plan_topk_parts(w, batch, h);
   p.total = w.off;
   return p;
 }
@@ -263,43 +286,73 @@ void add_axpy(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype 
   S.W = W; S.row_stride = stride; S.wdt = (wdt == DV_BF16) ? W_BF16 : W_F32;
   S.rows = L; S.coef = coef; S.coef_ld = coef_ld; S.relu = relu; S.ncols = ncols;
   S.vec = g.vec; S.nslices = g.nslices; S.nbt = g.nbt;
-  // Aim for about 256 KiB of weights per block at full capacity, spread over 2 blocks/CU.
-  const double bytes = (double)cap_rows * ncols * esize(wdt);
-  int chunks = (int)std::ceil(bytes / (256.0 * 1024.0) / (double)(g.nslices * g.nbt));
-  const int min_chunks = cdiv(device_cus() * 2, g.nslices * g.nbt);
-  chunks = std::max(chunks, std::min(min_chunks, cap_rows));
+  // About three blocks per CU for the segment; at most kMaxChunks chunk partials per
+  // slice (a short, fixed-order final sum) and at least one row per row group.
+  const int per_chunk = g.nslices * g.nbt;
+  int chunks = cdiv(device_cus() * 3, per_chunk);
+  chunks = std::min(chunks, std::max(1, cap_rows / kAxGroups));
   S.nchunks = std::max(1, std::min(chunks, g.chunks_max));
   S.block0 = T.blocks;
-  S.partial = partial; S.tickets = tickets;
+  S.partial = partial; S.tickets = tickets; S.hist = nullptr;
   S.out = out; S.out_ld = out_ld; S.add0 = add0; S.add1 = add1; S.add_ld = add_ld;
   S.accumulate = accumulate;
   T.blocks += S.nbt * S.nslices * S.nchunks;
   T.nseg++;
 }
-int axpy_lds(int bt) { return (256 + bt * 256) * 4; }
+int axpy_lds(int bt) {
+  return std::max((kAxpyTileRows * (1 + bt) + kAxGroups * bt * kAxSliceLanes * 8) * 4,
+                  (16 + kHistBins) * 4);
+}
 
 void setup_attn(AttnTask& A, const float* q, int q_ld, const void* K, const void* V, dv_dtype kvdt,
                 int batch, int h, int n, int dh, RowList heads, float scale, float* part,
-                uint32_t* tickets, float* o, int o_ld, int extra_blocks_hint) {
+                uint32_t* tickets, float* o, int o_ld, int other_blocks) {
   A.q = q; A.q_ld = q_ld; A.K = K; A.V = V; A.kvdt = (kvdt == DV_BF16) ? W_BF16 : W_F32;
   A.batch = batch; A.h = h; A.n = n; A.dh = dh; A.heads = heads; A.scale = scale;
   const int cap = heads.host_count;
-  // Enough (token, head, split) blocks to spread the cache over the chip, splits of
-  // at least 64 keys and at most kAttnMaxKeys keys.
+  // Enough (token, head, split) blocks to spread the cache over the chip when the
+  // launch has little else to run, splits of at least 64 keys.
   const int base = std::max(1, batch * cap);
-  int ns = cdiv(device_cus() * 2 - std::min(extra_blocks_hint, device_cus()), base);
-  ns = std::max(ns, cdiv(n, kAttnMaxKeys));
-  ns = std::min(ns, std::max(1, cdiv(n, 64)));
+  const int want = std::max(device_cus() * 2 - other_blocks / 2, device_cus() / 2);
+  int ns = cdiv(want, base);
   ns = std::max(1, std::min(ns, attn_nsplit_max(n)));
   A.nsplit = ns;
   A.per = cdiv(n, ns);
   A.part = part; A.tickets = tickets; A.o = o; A.o_ld = o_ld;
   A.blocks = batch * cap * ns;
 }
-int attn_lds() { return (kAttnMaxKeys + kWaves * 256 + 16) * 4; }
+int attn_lds() { return (128 + 2048 + 16) * 4; }
 
-int select_lds() { return (256 + 16) * 4; }
-int union_lds() { return 16 * 4; }
+int hist_lds() { return kHistBins * 4; }
+int classify_lds() { return (kHistBins + 16) * 4; }
+int resolve_lds() { return (kHistBins + 16) * 4 + kCandCap * 8; }
+
+// One top-k problem over `batch` score rows of N (row stride ld).
+TopkProblem make_topk(const float* scores, int ld, int N, int k, int batch, int unite,
+                      int32_t* idx, int32_t* count, uint32_t* hist, uint32_t* ticket, char* ws,
+                      const TopkWs& t) {
+  TopkProblem P;
+  P.scores = scores; P.ld = ld; P.N = N; P.k = k; P.batch = batch;
+  P.unite = (unite && batch > 1) ? 1 : 0;
+  P.idx = idx; P.count = count; P.hist = hist; P.ticket = ticket;
+  P.bits = reinterpret_cast<uint32_t*>(ws + t.bits);
+  P.nwords = cdiv(N, 32);
+  P.cand = reinterpret_cast<uint2*>(ws + t.cand);
+  P.ccount = reinterpret_cast<int32_t*>(ws + t.ccount);
+  P.need = reinterpret_cast<int32_t*>(ws + t.need);
+  P.nseg = cdiv(N, kSegElems);
+  return P;
+}
+int topk_seg_blocks(const TopkTask& T) {
+  int n = 0;
+  for (int i = 0; i < T.np; ++i) n += T.p[i].batch * T.p[i].nseg;
+  return n;
+}
+int topk_row_blocks(const TopkTask& T) {
+  int n = 0;
+  for (int i = 0; i < T.np; ++i) n += T.p[i].batch;
+  return n;
+}
 
 PhaseArgs zero_args() {
   PhaseArgs a;
@@ -326,10 +379,11 @@ int check_d(const char* fn, int d) {
   return DV_OK;
 }
 
+constexpr int kMaxCtx = 1 << 20;
+
 int check_nctx(const char* fn, int n) {
   if (n <= 0) return fail(DV_EINVAL, "%s: n_ctx = %d must be >= 1", fn, n);
-  if (n > kMaxSplit * kAttnMaxKeys)
-    return fail(DV_EUNSUPPORTED, "%s: n_ctx = %d exceeds %d", fn, n, kMaxSplit * kAttnMaxKeys);
+  if (n > kMaxCtx) return fail(DV_EUNSUPPORTED, "%s: n_ctx = %d exceeds %d", fn, n, kMaxCtx);
   return DV_OK;
 }
 
@@ -437,26 +491,26 @@ int dv_select_topk(const float* scores, int batch, int N, int k, int union_rows,
   if (N <= 0) return fail(DV_EINVAL, "%s: N = %d", fn, N);
   if (k < 0 || k > N) return fail(DV_EINVAL, "%s: k = %d not in [0, N = %d]", fn, k, N);
   CHECK_ALIGN(scores); CHECK_ALIGN(idx); CHECK_ALIGN(count);
-  const bool use_bits = union_rows && batch > 1;
   const SelectWs P = plan_select(batch, N);
-  if (use_bits) {
-    if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
-  }
+  if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
+  char* w = static_cast<char*>(ws);
+
+  PhaseArgs z = zero_args();
+  z.zero.ptr = reinterpret_cast<uint32_t*>(w + P.zero);
+  z.zero.words = P.zero_words;
+  z.zero.blocks = std::max(1, std::min(cdiv(P.zero_words, kThreads * 4), 64));
+  if (int e = launch(T_ZERO, 1, z, z.zero.blocks, 0, stream, fn)) return e;
+
   PhaseArgs a = zero_args();
-  SelectProblem& sp = a.select.p[0];
-  sp.scores = scores; sp.ld = N; sp.N = N; sp.k = k;
-  sp.mode = use_bits ? 1 : 0;
-  sp.idx = idx; sp.count = count;
-  sp.bits = use_bits ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + P.bits) : nullptr;
-  sp.nwords = P.nwords;
-  a.select.np = 1; a.select.batch = batch; a.select.blocks = batch;
-  if (int e = launch(T_SELECT, 1, a, a.select.blocks, select_lds(), stream, fn)) return e;
-  if (!use_bits) return DV_OK;
-  PhaseArgs u = zero_args();
-  UnionProblem& up = u.uni.p[0];
-  up.bits = sp.bits; up.nwords = P.nwords; up.N = N; up.batch = batch; up.idx = idx; up.count = count;
-  u.uni.np = 1; u.uni.blocks = 1;
-  return launch(T_UNION, 1, u, 1, union_lds(), stream, fn);
+  a.topk.np = 1;
+  a.topk.p[0] = make_topk(scores, N, N, k, batch, union_rows,
+                          idx, count, reinterpret_cast<uint32_t*>(w + P.hist),
+                          reinterpret_cast<uint32_t*>(w + P.ticket), w, P.t);
+  a.topk.blocks = topk_seg_blocks(a.topk);
+  if (int e = launch(T_HIST, 1, a, a.topk.blocks, hist_lds(), stream, fn)) return e;
+  if (int e = launch(T_CLASSIFY, 1, a, a.topk.blocks, classify_lds(), stream, fn)) return e;
+  a.topk.blocks = topk_row_blocks(a.topk);
+  return launch(T_RESOLVE, 1, a, a.topk.blocks, resolve_lds(), stream, fn);
 }
 
 int dv_sparse_mlp(const float* y, int batch, int d, const void* W1t, const void* W2t, int F,
@@ -590,8 +644,9 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
 
   char* w = static_cast<char*>(ws);
   auto fp = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  auto up = [&](size_t off) { return reinterpret_cast<uint32_t*>(w + off); };
   const int cap_m = std::max(max_count_m, 1), cap_a = std::max(max_count_a, 1);
-  uint32_t* tk = reinterpret_cast<uint32_t*>(w + P.tickets);
+  uint32_t* tk = up(P.tickets);
   uint32_t* t_attn = tk;
   uint32_t* t_mlp = t_attn + P.t_attn;
   uint32_t* t_bm = t_mlp + P.t_mlp;
@@ -603,7 +658,8 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   const RowList LH = make_list(idx_a, count_a, max_count_a, 1, h);
 
   // Phase 1: every gathered row dotted with y_in (W1 rows of S_M, W^Q columns of
-  // S_A, and the next layer's predictor factors A_M, A_A).
+  // S_A, and the next layer's predictor factors A_M, A_A); clears the counters and
+  // histograms the later phases use.
   PhaseArgs a1 = zero_args();
   add_rowdot(a1.rowdot, L->W1t, d, wdt, LM, fp(P.a), cap_m);
   add_rowdot(a1.rowdot, L->Wq, d, wdt, LQ, fp(P.q), cap_a * dh);
@@ -611,18 +667,21 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     add_rowdot(a1.rowdot, nx->A_M, d, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r);
     add_rowdot(a1.rowdot, nx->A_A, d, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r);
   }
-  finish_rowdot(a1.rowdot, y_in, batch, d, tk, P.t_total);
+  finish_rowdot(a1.rowdot, y_in, batch, d, up(P.zero), P.zero_words);
   if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
 
-  // Phase 2: attention over the cache for S_A; ReLU(a) W2 rows; predictor scores.
+  // Phase 2: attention over the cache for S_A; ReLU(a) W2 rows; predictor scores
+  // (with their top-digit histograms).
   PhaseArgs a2 = zero_args();
   add_axpy(a2.axpy, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, 1, d, fp(P.p_mlp), t_mlp,
            fp(P.mlp_out), d, nullptr, nullptr, 0, 0);
   if (nx) {
     add_axpy(a2.axpy, batch, nx->B_M, Fn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r, 0,
              Fn, fp(P.p_bm), t_bm, fp(P.sm), Fn, nullptr, nullptr, 0, 0);
+    a2.axpy.seg[a2.axpy.nseg - 1].hist = up(P.hist_m);
     add_axpy(a2.axpy, batch, nx->B_A, hn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r, 0,
              hn, fp(P.p_ba), t_ba, fp(P.sa), hn, nullptr, nullptr, 0, 0);
+    a2.axpy.seg[a2.axpy.nseg - 1].hist = up(P.hist_a);
   }
   a2.axpy.batch = batch;
   int flags2 = T_AXPY;
@@ -637,38 +696,35 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   if (int e = launch(flags2, bt, a2, a2.attn.blocks + a2.axpy.blocks, lds2, stream, fn)) return e;
 
   // Phase 3: W^O rows scaled by the head outputs, added to y_in + MLP; the next
-  // layer's top-k runs beside it.
+  // layer's top-k classifies its scores beside it.
   PhaseArgs a3 = zero_args();
   add_axpy(a3.axpy, batch, L->Wo, d, wdt, LQ, fp(P.o), cap_a * dh, 0, d, fp(P.p_wo), t_wo, y_out, d,
            y_in, fp(P.mlp_out), d, 0);
   a3.axpy.batch = batch;
   int flags3 = T_AXPY;
-  const bool use_bits = batch > 1;
+  TopkTask tk3;
+  memset(&tk3, 0, sizeof tk3);
   if (nx) {
-    SelectTask& S = a3.select;
-    S.p[0].scores = fp(P.sm); S.p[0].ld = Fn; S.p[0].N = Fn; S.p[0].k = km;
-    S.p[0].mode = use_bits ? 1 : 0; S.p[0].idx = next_idx_m; S.p[0].count = next_count_m;
-    S.p[0].bits = reinterpret_cast<uint32_t*>(w + P.bits_m); S.p[0].nwords = cdiv(Fn, 32);
-    S.p[1].scores = fp(P.sa); S.p[1].ld = hn; S.p[1].N = hn; S.p[1].k = ka;
-    S.p[1].mode = use_bits ? 1 : 0; S.p[1].idx = next_idx_a; S.p[1].count = next_count_a;
-    S.p[1].bits = reinterpret_cast<uint32_t*>(w + P.bits_a); S.p[1].nwords = cdiv(hn, 32);
-    S.np = 2; S.batch = batch; S.blocks = 2 * batch;
-    flags3 |= T_SELECT;
-    a3.b_select = 0;
-    a3.b_axpy = S.blocks;
+    tk3.np = 2;
+    tk3.p[0] = make_topk(fp(P.sm), Fn, Fn, km, batch, 1, next_idx_m, next_count_m, up(P.hist_m),
+                         up(P.uticket), w, P.tm);
+    tk3.p[1] = make_topk(fp(P.sa), hn, hn, ka, batch, 1, next_idx_a, next_count_a, up(P.hist_a),
+                         up(P.uticket) + 1, w, P.ta);
+    tk3.blocks = topk_seg_blocks(tk3);
+    a3.topk = tk3;
+    flags3 |= T_CLASSIFY;
+    a3.b_topk = 0;
+    a3.b_axpy = tk3.blocks;
   }
-  const int lds3 = std::max(axpy_lds(bt), (flags3 & T_SELECT) ? select_lds() : 0);
-  if (int e = launch(flags3, bt, a3, a3.select.blocks + a3.axpy.blocks, lds3, stream, fn)) return e;
+  const int lds3 = std::max(axpy_lds(bt), (flags3 & T_CLASSIFY) ? classify_lds() : 0);
+  if (int e = launch(flags3, bt, a3, a3.topk.blocks + a3.axpy.blocks, lds3, stream, fn)) return e;
 
-  if (nx && use_bits) {
+  // Phase 4: the next layer's sets (and, for a batch, their union).
+  if (nx) {
     PhaseArgs a4 = zero_args();
-    UnionTask& U = a4.uni;
-    U.p[0].bits = a3.select.p[0].bits; U.p[0].nwords = a3.select.p[0].nwords; U.p[0].N = Fn;
-    U.p[0].batch = batch; U.p[0].idx = next_idx_m; U.p[0].count = next_count_m;
-    U.p[1].bits = a3.select.p[1].bits; U.p[1].nwords = a3.select.p[1].nwords; U.p[1].N = hn;
-    U.p[1].batch = batch; U.p[1].idx = next_idx_a; U.p[1].count = next_count_a;
-    U.np = 2; U.blocks = 2;
-    if (int e = launch(T_UNION, 1, a4, 2, union_lds(), stream, fn)) return e;
+    a4.topk = tk3;
+    a4.topk.blocks = topk_row_blocks(tk3);
+    if (int e = launch(T_RESOLVE, 1, a4, a4.topk.blocks, resolve_lds(), stream, fn)) return e;
   }
   return DV_OK;
 }

@@ -9,7 +9,7 @@
 //   axpy   : out[b]   = sum_s c[b][s] * R[row(s)] gathered rows scaled and summed
 //            (W2_i of Eq. 1 with c = ReLU(a), rows of W_i^O of Eq. 2, factor Bm)
 //   attn   : softmax(scale q K^T) V per selected head, the n-loop of Eq. (2)
-//   select : per-row top-k by radix select, and the union of rows
+//   top-k  : per-row exact top-k (histogram, classify, resolve) and the batch union
 // A launch ("phase") runs any mix of them; each block picks its routine from its
 // index, so independent work shares one grid and one launch.
 #pragma once
@@ -21,12 +21,16 @@ namespace dv {
 constexpr int kThreads = 256;            // threads per block, every kernel
 constexpr int kWaves = kThreads / 64;    // wave64
 constexpr int kMaxSeg = 4;               // segments per rowdot / axpy task
-constexpr int kMaxChunks = 64;           // row chunks per axpy segment (partials bound)
+constexpr int kMaxChunks = 16;           // row chunks per axpy segment (partials bound)
+constexpr int kAxSliceLanes = 32;        // lanes across the columns of one axpy slice
+constexpr int kAxGroups = 8;             // row groups (half-waves) per axpy block
+constexpr int kAxpyTileRows = 512;       // axpy rows whose ids / coefficients sit in LDS
 constexpr int kMaxSplit = 64;            // key splits per (token, head)
-constexpr int kAttnMaxKeys = 2048;       // keys per attention block (logits in LDS)
 constexpr int kLdsBudget = 64 * 1024;    // dynamic LDS per block
-constexpr int kSelectTile = kThreads * 16;   // elements per selection tile
-constexpr int kUnionWordsPerThread = 4;
+constexpr int kHistBins = 2048;          // top 11 bits of a score key
+constexpr int kSegElems = kThreads * 8;  // scores per top-k classify block
+constexpr int kCandCap = 4096;           // candidates a resolve block keeps in LDS
+constexpr int kWordsPerThread = 4;       // bitmask words per thread when compacting
 
 enum : int { W_F32 = 0, W_BF16 = 1 };
 
@@ -74,6 +78,7 @@ struct AxpySeg {
   int block0;              // first block of this segment inside the task
   float* partial;          // [nbt][nchunks][BT][ncols]
   uint32_t* tickets;       // [nbt][nslices], zero on entry
+  uint32_t* hist;          // optional [batch][kHistBins]: top-digit histogram of the output
   float* out;              // out[b * out_ld + col]
   int out_ld;
   const float* add0;       // optional addends [b * add_ld + col]
@@ -106,42 +111,53 @@ struct AttnTask {
   int blocks;              // batch * cap * nsplit
 };
 
-struct SelectProblem {
+// Exact top-k of score rows, in three steps that each spread over many blocks:
+//   hist     11-bit top-digit histogram of every row (built by the blocks that
+//            produce the scores, or by a launch of its own)
+//   classify one block per (row, segment of kSegElems scores): finds the digit of
+//            the k-th key from the histogram, marks keys above it in the row's
+//            bitmask and lists the keys of that digit (index order) as candidates
+//   resolve  one block per row: picks the needed candidates (lower index first on
+//            equal keys), ORs them into the bitmask and compacts the ascending
+//            index list; with a batch union the last row to finish ORs all rows.
+struct TopkProblem {
   const float* scores;     // row b at scores + b * ld
-  int ld, N, k;
-  int mode;                // 0: ascending indices at idx + b*k, count[b]; 1: bitmask rows
+  int ld, N, k, batch;
+  int unite;               // 1: union of rows -> idx, count[0]; 0: row b -> idx + b*k, count[b]
   int32_t* idx;
   int32_t* count;
+  uint32_t* hist;          // [batch][kHistBins], zero before it is built
   uint32_t* bits;          // [batch][nwords]
   int nwords;
+  uint2* cand;             // [batch][nseg * kSegElems] (key, index); [batch][N] scratch follows
+  int32_t* ccount;         // [batch][nseg] candidates per segment
+  int32_t* need;           // [batch] candidates to keep
+  uint32_t* ticket;        // rows resolved (union), zero before the resolve launch
+  int nseg;                // segments per row = ceil(N / kSegElems)
 };
 
-struct SelectTask {
-  SelectProblem p[2];
-  int np, batch, blocks;   // blocks = np * batch
+struct TopkTask {
+  TopkProblem p[2];
+  int np;
+  int blocks;
 };
 
-struct UnionProblem {
-  const uint32_t* bits;    // [batch][nwords]
-  int nwords, N, batch;
-  int32_t* idx;
-  int32_t* count;
+struct ZeroTask {
+  uint32_t* ptr;
+  int words;
+  int blocks;
 };
 
-struct UnionTask {
-  UnionProblem p[2];
-  int np, blocks;
-};
-
-enum : int { T_ROWDOT = 1, T_ATTN = 2, T_AXPY = 4, T_SELECT = 8, T_UNION = 16 };
+enum : int { T_ROWDOT = 1, T_ATTN = 2, T_AXPY = 4, T_HIST = 8, T_CLASSIFY = 16, T_RESOLVE = 32,
+             T_ZERO = 64 };
 
 struct PhaseArgs {
   RowdotTask rowdot;
   AttnTask attn;
   AxpyTask axpy;
-  SelectTask select;
-  UnionTask uni;
-  int b_rowdot, b_attn, b_axpy, b_select, b_union;   // first block of each task
+  TopkTask topk;
+  ZeroTask zero;
+  int b_rowdot, b_attn, b_axpy, b_topk, b_zero;   // first block of each task
 };
 
 // Host-side launcher implemented in dv_kernels.hip.  Returns a hipError_t as int.

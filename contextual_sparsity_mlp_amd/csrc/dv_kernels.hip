@@ -1,30 +1,33 @@
 // dv_kernels.hip - device code of the Deja Vu sparse decode step for gfx950.
 //
-// Four routines, each written for CDNA's 64-wide waves and 256-thread blocks:
+// The routines are written for CDNA's 64-wide waves and 256-thread blocks:
 //
-//  rowdot  One wave owns one gathered row of d elements at a time and streams it
-//          in 1 KiB wave-loads (16 B per lane), dotting it with the token inputs
-//          staged once per block in LDS; the 64 lane partials are combined with
-//          cross-lane shuffles.  Covers W1_i of Eq. (1), the d_h columns of a
-//          selected W_i^Q of Eq. (2) and the predictor's first factor.
-//  axpy    A block owns a (column slice x row chunk) tile.  Each thread keeps the
-//          running sum of 8 (bf16) or 4 (fp32) output columns in registers across
-//          the chunk's rows, reading 16 B per row; the chunk's row indices and
-//          coefficients are staged in LDS and broadcast.  Partial sums go to the
-//          workspace and the last block to finish a column slice (device-scope
-//          ticket) adds the chunks in fixed order, so results are deterministic.
-//          Covers W2_i scaled by ReLU(a_i) in Eq. (1), W_i^O scaled by H_i(y) in
-//          Eq. (2) and the predictor's second factor.
-//  attn    Decode attention over the cache for one (token, selected head, key
-//          split): logits in LDS, max-subtracted exp, p.V, then the last split to
-//          finish rescales and merges the splits (splitting the key axis follows
-//          the Flash-Decoding idea named on the survey-notes page).
-//  select  Exact top-k of one score row by a 4-pass 8-bit radix select on
-//          order-preserving keys, then an index-ordered block scan that keeps the
-//          lowest indices among keys equal to the threshold.  `union` ORs per-row
-//          bitmasks and compacts them to an ascending list.
+//  rowdot   One wave owns one gathered row of d elements at a time and streams it
+//           in 1 KiB wave-loads (16 B per lane), dotting it with the token inputs
+//           staged once per block in LDS; lane partials are combined with
+//           cross-lane shuffles.  Covers W1_i of Eq. (1), the d_h columns of a
+//           selected W_i^Q of Eq. (2) and the predictor's first factor.
+//  axpy     A block owns a (column slice x row chunk) tile: 256 bf16 columns (512 B
+//           of each row) and a chunk of the gathered rows.  Each half-wave is a
+//           row group that keeps 8 columns per lane in registers across every 8th
+//           row; the chunk's row indices and coefficients are staged in LDS and
+//           broadcast.  Row groups are summed in LDS, chunk partials are handed to
+//           the last block of the slice, which adds the at most 16 chunks in a
+//           fixed order: results are deterministic.  Covers W2_i scaled by ReLU(a_i)
+//           in Eq. (1), W_i^O scaled by H_i(y) in Eq. (2) and the predictor's
+//           second factor.
+//  attn     Decode attention over the cache for one (token, selected head, key
+//           split): K and V rows are loaded together and folded with a running
+//           (max, sum, p.V), then the last split to finish merges the splits
+//           (splitting the key axis follows the Flash-Decoding idea named on the
+//           survey-notes page).
+//  top-k    hist / classify / resolve, see dv_internal.h.
 //
-// No floating-point atomics anywhere; only integer tickets and LDS histograms.
+// Blocks of one launch hand values to each other only through device-coherent
+// (agent-scope) atomic stores and loads plus a wait for store completion before
+// the ticket: no cache writeback or invalidate is needed for that.  Values that
+// a later launch reads use plain stores (a launch boundary orders them).  There are
+// no floating-point atomics; only integer tickets and histograms.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -47,41 +50,21 @@ __device__ __forceinline__ void unpack8(const uint4& x, float (&f)[8]) {
   f[6] = bf16_lo(x.w); f[7] = bf16_hi(x.w);
 }
 
+// Device-coherent accesses for values handed between blocks of one launch.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-
-// Block-wide reductions over 256 threads; `scratch` holds kWaves floats.
-__device__ __forceinline__ float block_sum(float v, float* scratch) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) scratch[wave] = v;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += scratch[w];
-  return t;
-}
-
-__device__ __forceinline__ float block_max(float v, float* scratch) {
-  v = wave_max(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) scratch[wave] = v;
-  __syncthreads();
-  float t = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) t = fmaxf(t, scratch[w]);
-  return t;
 }
 
 // Inclusive prefix sum over the 256 threads of a block, in thread order.
@@ -114,19 +97,57 @@ __device__ __forceinline__ int list_slots(const RowList& L) {
   return max(n, 0);
 }
 
-// Device-scope "last block to arrive" test: every thread calls it after writing
-// its partial results; returns true in all threads of the last arriving block.
+// "Last block to arrive": every thread calls it after storing (st_dev) what the
+// last block will read; returns true in all threads of the last arriving block.
 __device__ __forceinline__ bool arrive_last(uint32_t* ticket, uint32_t expected, int* flag) {
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's device-coherent stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t t = atomicAdd(ticket, 1u);
+    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = (t == expected - 1u) ? 1 : 0;
   }
   __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
+  return *flag != 0;
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// -0.0 is mapped like +0.0.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Given a histogram `h` of nbins digits (bin = digit), in LDS, and `remaining` >= 1
+// keys still to pick from the top, find the digit D holding the remaining-th key
+// from the top and the number of keys in bins above D.  All threads call; the
+// result is returned to every thread.
+__device__ __forceinline__ void find_digit(const uint32_t* h, int nbins, uint32_t remaining,
+                                           uint32_t* scratch, uint32_t* bcast, uint32_t* D,
+                                           uint32_t* above) {
+  const int tid = threadIdx.x;
+  const int per_t = nbins / kThreads;
+  const int top = nbins - 1 - tid * per_t;
+  uint32_t v = 0u;
+  for (int j = 0; j < per_t; ++j) v += h[top - j];
+  uint32_t tot;
+  const uint32_t inc = block_incl_scan(v, scratch, &tot);
+  if (v > 0u && inc >= remaining && inc - v < remaining) {
+    uint32_t cum = inc - v;
+    for (int j = 0; j < per_t; ++j) {
+      const uint32_t c = h[top - j];
+      if (cum + c >= remaining) {
+        bcast[0] = (uint32_t)(top - j);
+        bcast[1] = cum;
+        break;
+      }
+      cum += c;
+    }
+  }
+  __syncthreads();
+  *D = bcast[0];
+  *above = bcast[1];
+  __syncthreads();
 }
 
 // --------------------------------------------------------------------------- //
@@ -211,7 +232,7 @@ __device__ __forceinline__ void rowdot_f32(const float4* __restrict__ rp, const 
 template <int BT>
 __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Counters used by later launches of the same call start at zero.
+  // Counters and histograms used by later launches of the same call start at zero.
   for (int i = blk * kThreads + tid; i < T.zero_words; i += T.blocks * kThreads) T.zero_ptr[i] = 0u;
 
   int total_cap = 0;
@@ -274,7 +295,7 @@ __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float*
 // axpy                                                                         //
 // --------------------------------------------------------------------------- //
 
-constexpr int kAxpyTile = 256;   // rows whose indices / coefficients are staged at once
+constexpr int kAxpyTile = kAxpyTileRows;
 
 __device__ __forceinline__ AxpySeg ax_seg(const AxpyTask& T, int s) {
   switch (s) {
@@ -302,15 +323,53 @@ __device__ __forceinline__ void load_cols(const void* W, long long off, float (&
   }
 }
 
-// Accumulate rows [r0, r1) of the segment's list into acc (this thread's VEC columns).
-template <int BT, int VEC, int WT>
-__device__ __forceinline__ void axpy_rows(const AxpySeg& S, int r0, int r1, int b0, int nb,
-                                          int col0, bool active, float* lds,
-                                          float (&acc)[BT][VEC]) {
-  constexpr int U = 8;
-  int* lrow = reinterpret_cast<int*>(lds);                 // [kAxpyTile] row or -1
-  float* lcoef = lds + kAxpyTile;                          // [BT][kAxpyTile]
+// Adds the top-digit of each active thread's score to an LDS histogram, then the
+// non-zero bins to the device histogram `gh`.  All threads of the block call.
+__device__ __forceinline__ void hist_flush_one(float score, bool active, uint32_t* lh, uint32_t* gh) {
   const int tid = threadIdx.x;
+  __syncthreads();
+  for (int i = tid; i < kHistBins; i += kThreads) lh[i] = 0u;
+  __syncthreads();
+  if (active) atomicAdd(&lh[score_key(score) >> 21], 1u);
+  __syncthreads();
+  for (int i = tid; i < kHistBins; i += kThreads) {
+    const uint32_t c = lh[i];
+    if (c) __hip_atomic_fetch_add(&gh[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// One block: a slice of kAxSliceLanes*VEC output columns and a chunk of the row list.
+template <int BT, int VEC, int WT>
+__device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, float* lds) {
+  constexpr int U = 8;
+  constexpr int SW = kAxSliceLanes * VEC;    // columns per slice
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave * 2 + (lane >> 5);
+  const int hl = lane & 31;
+  const int slice = lb % S.nslices;
+  const int rest = lb / S.nslices;
+  const int chunk = rest % S.nchunks;
+  const int bti = rest / S.nchunks;
+  const int b0 = bti * BT;
+  const int nb = min(BT, batch - b0);
+  const int col0 = slice * SW + hl * VEC;
+  const bool active = col0 < S.ncols;
+
+  const int nrows = list_slots(S.rows) * S.rows.expand;
+  const int per = (nrows + S.nchunks - 1) / S.nchunks;
+  const int r0 = min(chunk * per, nrows);
+  const int r1 = min(r0 + per, nrows);
+
+  int* lrow = reinterpret_cast<int*>(lds);               // [kAxpyTile] row or -1
+  float* lcoef = lds + kAxpyTile;                        // [BT][kAxpyTile]
+  float* red = lds + kAxpyTile * (1 + BT);               // [kAxGroups][BT][SW]
+
+  float acc[BT][VEC];
+#pragma unroll
+  for (int b = 0; b < BT; ++b)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[b][v] = 0.f;
+
   const int ex = S.rows.expand;
   for (int t0 = r0; t0 < r1; t0 += kAxpyTile) {
     const int tn = min(kAxpyTile, r1 - t0);
@@ -334,12 +393,12 @@ __device__ __forceinline__ void axpy_rows(const AxpySeg& S, int r0, int r1, int 
     }
     __syncthreads();
     if (active) {
-      for (int i0 = 0; i0 < tn; i0 += U) {
+      for (int i0 = grp; i0 < tn; i0 += kAxGroups * U) {
         float w[U][VEC];
         float c[U][BT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int i = i0 + u;
+          const int i = i0 + u * kAxGroups;
           const int row = (i < tn) ? lrow[i] : -1;
           if (row >= 0) {
             load_cols<VEC, WT>(S.W, (long long)row * S.row_stride + col0, w[u]);
@@ -359,63 +418,70 @@ __device__ __forceinline__ void axpy_rows(const AxpySeg& S, int r0, int r1, int 
       }
     }
   }
-}
 
-template <int BT, int VEC, int WT>
-__device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, float* lds) {
-  const int tid = threadIdx.x;
-  const int chunk = lb % S.nchunks;
-  const int rest = lb / S.nchunks;
-  const int slice = rest % S.nslices;
-  const int bti = rest / S.nslices;
-  const int b0 = bti * BT;
-  const int nb = min(BT, batch - b0);
-  const int col0 = slice * (kThreads * VEC) + tid * VEC;
-  const bool active = col0 < S.ncols;
-
-  const int nrows = list_slots(S.rows) * S.rows.expand;
-  const int per = (nrows + S.nchunks - 1) / S.nchunks;
-  const int r0 = min(chunk * per, nrows);
-  const int r1 = min(r0 + per, nrows);
-
-  float acc[BT][VEC];
+  // sum the row groups in order 0..7
+  __syncthreads();
 #pragma unroll
   for (int b = 0; b < BT; ++b)
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[b][v] = 0.f;
-  axpy_rows<BT, VEC, WT>(S, r0, r1, b0, nb, col0, active, lds, acc);
-
+    for (int v = 0; v < VEC; ++v) red[(grp * BT + b) * SW + hl * VEC + v] = acc[b][v];
+  __syncthreads();
   const size_t ncols = (size_t)S.ncols;
-  float* P = S.partial + (size_t)(bti * S.nchunks + chunk) * BT * ncols;
-  if (active) {
+  const int col = slice * SW + tid;
+  const bool cact = tid < SW && col < S.ncols;
+  float part[BT];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    float t = 0.f;
+    if (cact) {
+#pragma unroll
+      for (int g = 0; g < kAxGroups; ++g) t += red[(g * BT + b) * SW + tid];
+    }
+    part[b] = t;
+  }
+
+  if (S.nchunks > 1) {
+    float* P = S.partial + ((size_t)(bti * S.nchunks + chunk) * BT) * ncols;
+    if (cact) {
+#pragma unroll
+      for (int b = 0; b < BT; ++b)
+        if (b < nb) st_dev(&P[b * ncols + col], part[b]);
+    }
+    int* flag = reinterpret_cast<int*>(lds);
+    if (!arrive_last(&S.tickets[bti * S.nslices + slice], (uint32_t)S.nchunks, flag)) return;
+    const float* P0 = S.partial + (size_t)bti * S.nchunks * BT * ncols;
 #pragma unroll
     for (int b = 0; b < BT; ++b) {
-      if (b < nb) {
+      if (b < nb && cact) {
+        float v[kMaxChunks];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) P[b * ncols + col0 + v] = acc[b][v];
+        for (int c = 0; c < kMaxChunks; ++c)
+          v[c] = (c < S.nchunks) ? ld_dev(&P0[((size_t)c * BT + b) * ncols + col]) : 0.f;
+        float t = 0.f;
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) t += v[c];
+        part[b] = t;
       }
     }
   }
-  int* flag = reinterpret_cast<int*>(lds);
-  if (!arrive_last(&S.tickets[bti * S.nslices + slice], (uint32_t)S.nchunks, flag)) return;
-  if (!active) return;
-  const float* P0 = S.partial + (size_t)bti * S.nchunks * BT * ncols;
 #pragma unroll
   for (int b = 0; b < BT; ++b) {
-    if (b < nb) {
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const size_t col = (size_t)col0 + v;
-        float sum = 0.f;
-        for (int c = 0; c < S.nchunks; ++c) sum += P0[((size_t)c * BT + b) * ncols + col];
-        const size_t bo = (size_t)(b0 + b);
-        if (S.add1) sum = S.add1[bo * S.add_ld + col] + sum;
-        if (S.add0) sum = S.add0[bo * S.add_ld + col] + sum;
-        float* o = S.out + bo * S.out_ld + col;
-        if (S.accumulate) sum = *o + sum;
-        *o = sum;
-      }
+    if (b < nb && cact) {
+      const size_t bo = (size_t)(b0 + b);
+      float sum = part[b];
+      if (S.add1) sum = S.add1[bo * S.add_ld + col] + sum;
+      if (S.add0) sum = S.add0[bo * S.add_ld + col] + sum;
+      float* o = S.out + bo * S.out_ld + col;
+      if (S.accumulate) sum = *o + sum;
+      *o = sum;
+      part[b] = sum;
     }
+  }
+  if (S.hist) {
+    uint32_t* lh = reinterpret_cast<uint32_t*>(lds) + 16;
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+      if (b < nb) hist_flush_one(part[b], cact, lh, S.hist + (size_t)(b0 + b) * kHistBins);
   }
 }
 
@@ -440,6 +506,9 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
 // attention                                                                    //
 // --------------------------------------------------------------------------- //
 
+// Each key group (LPK lanes sharing a key row) keeps a running max m, sum l and
+// p.V for its keys; groups merge in LDS (weight exp(m_g - M), 0 for a group that
+// saw no key) and the splits of a (token, head) merge the same way.
 template <int WT>
 __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds) {
   constexpr int VEC = (WT == W_BF16) ? 8 : 4;
@@ -457,15 +526,17 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
   const int dh = T.dh;
   const int LPK = dh / VEC;          // lanes per key row
   const int KPW = 64 / LPK;          // keys per wave-load
-  const int stride = kWaves * KPW;   // keys per block-load
+  const int NG = kWaves * KPW;       // key groups in the block
   const int dg = lane % LPK, ks = lane / LPK;
+  const int grp = wave * KPW + ks;
   const int k0 = split * T.per;
   const int k1 = min(k0 + T.per, T.n);
   const int len = max(k1 - k0, 0);
 
-  float* logit = lds;                          // [kAttnMaxKeys]
-  float* red = lds + kAttnMaxKeys;             // [kWaves][256]
-  float* scratch = red + kWaves * 256;         // [16]
+  float* gm = lds;                   // [NG <= 64] group max
+  float* gl = lds + 64;              // [NG] group sum
+  float* go = lds + 128;             // [NG][dh] group p.V; NG * dh = 256 * VEC <= 2048
+  int* flag = reinterpret_cast<int*>(lds + 128 + 2048);
 
   const size_t row0 = ((size_t)b * T.h + head) * (size_t)T.n + k0;   // first key row
   float qv[VEC];
@@ -473,219 +544,204 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
   for (int v = 0; v < VEC; ++v)
     qv[v] = T.scale * T.q[(size_t)b * T.q_ld + (size_t)slot * dh + dg * VEC + v];
 
-  // logits
-  for (int base = 0; base < len; base += stride * U) {
-    float part[U];
+  float m = -INFINITY, l = 0.f;
+  float o[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) o[v] = 0.f;
+  for (int base = 0; base < len; base += NG * U) {
+    float kv[U][VEC], vv[U][VEC];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = base + u * stride + wave * KPW + ks;
-      float p = 0.f;
+      const int j = base + u * NG + grp;
       if (j < len) {
-        float kv[VEC];
-        load_cols<VEC, WT>(T.K, (long long)(row0 + j) * dh + dg * VEC, kv);
+        load_cols<VEC, WT>(T.K, (long long)(row0 + j) * dh + dg * VEC, kv[u]);
+        load_cols<VEC, WT>(T.V, (long long)(row0 + j) * dh + dg * VEC, vv[u]);
+      } else {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) p = fmaf(qv[v], kv[v], p);
+        for (int v = 0; v < VEC; ++v) { kv[u][v] = 0.f; vv[u][v] = 0.f; }
       }
-      part[u] = p;
+    }
+    float t[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float p = 0.f;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) p = fmaf(qv[v], kv[u][v], p);
+      t[u] = p;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      for (int off = LPK >> 1; off >= 1; off >>= 1) part[u] += __shfl_xor(part[u], off);
+      for (int off = LPK >> 1; off >= 1; off >>= 1) t[u] += __shfl_xor(t[u], off);
+    float mc = m;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = base + u * stride + wave * KPW + ks;
-      if (j < len && dg == 0) logit[j] = part[u];
-    }
-  }
-  __syncthreads();
-  float m = -INFINITY;
-  for (int j = tid; j < len; j += kThreads) m = fmaxf(m, logit[j]);
-  m = block_max(m, scratch);
-  float l = 0.f;
-  for (int j = tid; j < len; j += kThreads) {
-    const float p = expf(logit[j] - m);
-    logit[j] = p;
-    l += p;
-  }
-  l = block_sum(l, scratch + 8);   // also orders the p writes before the reads below
-
-  float acc[VEC];
+    for (int u = 0; u < U; ++u)
+      if (base + u * NG + grp < len) mc = fmaxf(mc, t[u]);
+    if (mc != -INFINITY) {
+      const float alpha = (m == -INFINITY) ? 0.f : expf(m - mc);
+      l *= alpha;
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-  for (int base = 0; base < len; base += stride * U) {
+      for (int v = 0; v < VEC; ++v) o[v] *= alpha;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = base + u * stride + wave * KPW + ks;
-      if (j < len) {
-        const float p = logit[j];
-        float vv[VEC];
-        load_cols<VEC, WT>(T.V, (long long)(row0 + j) * dh + dg * VEC, vv);
+      for (int u = 0; u < U; ++u) {
+        if (base + u * NG + grp < len) {
+          const float p = expf(t[u] - mc);
+          l += p;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = fmaf(p, vv[v], acc[v]);
+          for (int v = 0; v < VEC; ++v) o[v] = fmaf(p, vv[u][v], o[v]);
+        }
       }
+      m = mc;
     }
   }
-  for (int off = LPK; off < 64; off <<= 1)
+  // per-group state to LDS, then merge the groups in order
+  if (dg == 0) { gm[grp] = m; gl[grp] = l; }
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], off);
-  if (ks == 0) {
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) red[wave * 256 + dg * VEC + v] = acc[v];
-  }
+  for (int v = 0; v < VEC; ++v) go[grp * dh + dg * VEC + v] = o[v];
   __syncthreads();
+  float M = -INFINITY;
+  for (int g = 0; g < NG; ++g) M = fmaxf(M, gm[g]);
+  float L = 0.f, O = 0.f;
+  if (tid < dh) {
+    for (int g = 0; g < NG; ++g) {
+      const float w = (gm[g] == -INFINITY) ? 0.f : expf(gm[g] - M);
+      L = fmaf(w, gl[g], L);
+      O = fmaf(w, go[g * dh + tid], O);
+    }
+  }
+  float* outp = T.o + (size_t)b * T.o_ld + (size_t)slot * dh;
+  if (T.nsplit == 1) {
+    if (tid < dh) outp[tid] = O / L;
+    return;
+  }
   const int w2 = dh + 2;
   float* P = T.part + (((size_t)b * cap + slot) * T.nsplit + split) * w2;
-  if (tid < dh) {
-    float o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) o += red[w * 256 + tid];
-    P[2 + tid] = o;
-  }
-  if (tid == 0) { P[0] = m; P[1] = l; }
-  int* flag = reinterpret_cast<int*>(scratch + 15);
+  if (tid < dh) st_dev(&P[2 + tid], O);
+  if (tid == 0) { st_dev(&P[0], M); st_dev(&P[1], L); }
   if (!arrive_last(&T.tickets[(size_t)b * cap + slot], (uint32_t)T.nsplit, flag)) return;
   if (tid < dh) {
     const float* P0 = T.part + ((size_t)b * cap + slot) * T.nsplit * w2;
-    float M = -INFINITY;
-    for (int s = 0; s < T.nsplit; ++s) M = fmaxf(M, P0[(size_t)s * w2]);
-    float L = 0.f, O = 0.f;
+    float MM = -INFINITY;
+    for (int s = 0; s < T.nsplit; ++s) MM = fmaxf(MM, ld_dev(&P0[(size_t)s * w2]));
+    float LL = 0.f, OO = 0.f;
     for (int s = 0; s < T.nsplit; ++s) {
-      const float ms = P0[(size_t)s * w2];
-      const float wgt = (ms == -INFINITY) ? 0.f : expf(ms - M);
-      L = fmaf(wgt, P0[(size_t)s * w2 + 1], L);
-      O = fmaf(wgt, P0[(size_t)s * w2 + 2 + tid], O);
+      const float ms = ld_dev(&P0[(size_t)s * w2]);
+      const float wgt = (ms == -INFINITY) ? 0.f : expf(ms - MM);
+      LL = fmaf(wgt, ld_dev(&P0[(size_t)s * w2 + 1]), LL);
+      OO = fmaf(wgt, ld_dev(&P0[(size_t)s * w2 + 2 + tid]), OO);
     }
-    T.o[(size_t)b * T.o_ld + (size_t)slot * dh + tid] = O / L;
+    outp[tid] = OO / LL;
   }
 }
 
 // --------------------------------------------------------------------------- //
-// top-k select and union                                                       //
+// top-k: histogram, classify, resolve                                          //
 // --------------------------------------------------------------------------- //
 
-// Order-preserving map of a float to uint32 (larger float -> larger key);
-// -0.0 is mapped like +0.0.
-__device__ __forceinline__ uint32_t score_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+__device__ __forceinline__ int topk_problem(const TopkTask& T, int blk, int per0, int* local) {
+  if (T.np > 1 && blk >= per0) { *local = blk - per0; return 1; }
+  *local = blk;
+  return 0;
 }
 
-__device__ __forceinline__ void select_row(const SelectProblem& P, int b, float* lds) {
+// hist: one block per (row, segment) adds the segment's top-digit histogram.
+__device__ __forceinline__ void hist_block(const TopkProblem& P, int lb, float* lds) {
   const int tid = threadIdx.x;
-  uint32_t* hist = reinterpret_cast<uint32_t*>(lds);      // [256]
-  uint32_t* scan = hist + 256;                            // [kWaves]
-  uint32_t* bcast = scan + 8;                             // [2]
+  const int g = lb % P.nseg, b = lb / P.nseg;
+  uint32_t* lh = reinterpret_cast<uint32_t*>(lds);
   const float* s = P.scores + (size_t)b * P.ld;
+  for (int i = tid; i < kHistBins; i += kThreads) lh[i] = 0u;
+  __syncthreads();
+  const int j0 = g * kSegElems;
+  const int j1 = min(j0 + kSegElems, P.N);
+  for (int j = j0 + tid; j < j1; j += kThreads) atomicAdd(&lh[score_key(s[j]) >> 21], 1u);
+  __syncthreads();
+  uint32_t* gh = P.hist + (size_t)b * kHistBins;
+  for (int i = tid; i < kHistBins; i += kThreads) {
+    const uint32_t c = lh[i];
+    if (c) __hip_atomic_fetch_add(&gh[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// classify: one block per (row, segment of kSegElems scores, 8 per thread).
+__device__ __forceinline__ void classify_block(const TopkProblem& P, int lb, float* lds) {
+  const int tid = threadIdx.x;
+  const int g = lb % P.nseg, b = lb / P.nseg;
+  uint32_t* lh = reinterpret_cast<uint32_t*>(lds);        // [kHistBins]
+  uint32_t* scratch = lh + kHistBins;                     // [8]
+  uint32_t* bcast = scratch + 8;                          // [2]
   const int N = P.N;
   const int k = min(max(P.k, 0), N);
 
-  // threshold key T and how many keys equal to T to keep (lowest indices first)
-  uint32_t T, take;
+  // digit D1 of the k-th key from the top, and how many keys of that digit are needed
+  int D1;
+  uint32_t need = 0u;
   if (k == 0) {
-    T = 0xffffffffu; take = 0u;
+    D1 = kHistBins;          // nothing above, nothing equal
   } else if (k == N) {
-    T = 0u; take = (uint32_t)N;
+    D1 = -1;                 // everything above
   } else {
-    uint32_t prefix = 0u, remaining = (uint32_t)k;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      __syncthreads();
-      hist[tid] = 0u;
-      __syncthreads();
-      for (int j = tid; j < N; j += kThreads) {
-        const uint32_t key = score_key(s[j]);
-        const bool match = (pass == 0) || ((key >> (shift + 8)) == (prefix >> (shift + 8)));
-        if (match) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      // thread t holds bin 255-t, so the inclusive scan is the count at or above that bin
-      const uint32_t v = hist[255 - tid];
-      uint32_t tot;
-      const uint32_t inc = block_incl_scan(v, scan, &tot);
-      if (v > 0u && inc >= remaining && inc - v < remaining) {
-        bcast[0] = 255u - (uint32_t)tid;
-        bcast[1] = inc - v;
-      }
-      __syncthreads();
-      prefix |= bcast[0] << shift;
-      remaining -= bcast[1];
-    }
-    T = prefix; take = remaining;
+    const uint32_t* gh = P.hist + (size_t)b * kHistBins;
+    for (int i = tid; i < kHistBins; i += kThreads) lh[i] = gh[i];
+    __syncthreads();
+    uint32_t D, above;
+    find_digit(lh, kHistBins, (uint32_t)k, scratch, bcast, &D, &above);
+    D1 = (int)D;
+    need = (uint32_t)k - above;
   }
 
-  // index-ordered pass: keep key > T, and the first `take` keys == T
-  uint32_t carry_eq = 0u, carry_sel = 0u;
-  constexpr int E = kSelectTile / kThreads;   // 16 contiguous elements per thread
-  for (int base = 0; base < N; base += kSelectTile) {
-    const int j0 = base + tid * E;
-    uint32_t keys[E];
-    uint32_t n_eq = 0u;
+  const float* s = P.scores + (size_t)b * P.ld;
+  const int j0 = g * kSegElems + tid * 8;
+  uint32_t keys[8];
+  uint32_t m8 = 0u, n_cand = 0u;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = j0 + e;
-      keys[e] = (j < N) ? score_key(s[j]) : 0u;
-      n_eq += (j < N && keys[e] == T) ? 1u : 0u;
-    }
-    uint32_t tot_eq;
-    uint32_t eq_before = block_incl_scan(n_eq, scan, &tot_eq) - n_eq + carry_eq;
-    uint32_t selmask = 0u, n_sel = 0u;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = j0 + e;
-      bool sel = false;
-      if (j < N) {
-        if (keys[e] > T) sel = true;
-        else if (keys[e] == T) { sel = eq_before < take; ++eq_before; }
-      }
-      if (sel) { selmask |= 1u << e; ++n_sel; }
-    }
-    if (P.mode == 0) {
-      uint32_t tot_sel;
-      uint32_t pos = block_incl_scan(n_sel, scan, &tot_sel) - n_sel + carry_sel;
-      int32_t* out = P.idx + (size_t)b * P.k;
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (selmask & (1u << e)) out[pos++] = j0 + e;
-      carry_sel += tot_sel;
-    } else {
-      // two threads fill one 32-bit word (16 elements each)
-      const uint32_t other = __shfl_xor(selmask, 1);
-      if ((tid & 1) == 0) {
-        const int word = j0 >> 5;
-        if (word < P.nwords) P.bits[(size_t)b * P.nwords + word] = selmask | (other << 16);
-      }
-    }
-    carry_eq += tot_eq;
+  for (int e = 0; e < 8; ++e) {
+    const int j = j0 + e;
+    keys[e] = (j < N) ? score_key(s[j]) : 0u;
+    const int dig = (int)(keys[e] >> 21);
+    if (j < N && dig > D1) m8 |= 1u << e;
+    if (j < N && dig == D1) ++n_cand;
   }
-  if (P.mode == 0 && tid == 0) P.count[b] = k;
+  uint32_t tot;
+  uint32_t pos = block_incl_scan(n_cand, scratch, &tot) - n_cand;
+  uint2* cand = P.cand + ((size_t)b * P.nseg + g) * kSegElems;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = j0 + e;
+    if (j < N && (int)(keys[e] >> 21) == D1) cand[pos++] = make_uint2(keys[e], (uint32_t)j);
+  }
+  // four threads fill one 32-bit word (8 elements each)
+  uint32_t w = m8 << ((tid & 3) * 8);
+  w |= __shfl_xor(w, 1);
+  w |= __shfl_xor(w, 2);
+  const int word = j0 >> 5;
+  if ((tid & 3) == 0 && word < P.nwords) P.bits[(size_t)b * P.nwords + word] = w;
+  if (tid == 0) {
+    P.ccount[(size_t)b * P.nseg + g] = (int32_t)tot;
+    if (g == 0) P.need[b] = (int32_t)need;
+  }
 }
 
-__device__ __forceinline__ void select_task(const SelectTask& T, int blk, float* lds) {
-  const int pi = blk / T.batch, b = blk % T.batch;
-  if (pi == 0) select_row(T.p[0], b, lds);
-  else select_row(T.p[1], b, lds);
-}
-
-__device__ __forceinline__ void union_problem(const UnionProblem& P, float* lds) {
+// Ascending indices of the set bits of `nwords` words (read with ld_dev) into idx;
+// returns the count.  `rows` words arrays at stride `nwords` are ORed first.
+__device__ __forceinline__ uint32_t compact_bits(const uint32_t* bits, int rows, int nwords,
+                                                 int32_t* idx, uint32_t* scratch) {
   const int tid = threadIdx.x;
-  uint32_t* scan = reinterpret_cast<uint32_t*>(lds);
-  constexpr int E = kUnionWordsPerThread;
+  constexpr int E = kWordsPerThread;
   uint32_t carry = 0u;
-  for (int base = 0; base < P.nwords; base += kThreads * E) {
+  for (int base = 0; base < nwords; base += kThreads * E) {
     uint32_t w[E];
     uint32_t n = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int word = base + tid * E + e;
       uint32_t x = 0u;
-      if (word < P.nwords)
-        for (int b = 0; b < P.batch; ++b) x |= P.bits[(size_t)b * P.nwords + word];
+      if (word < nwords)
+        for (int r = 0; r < rows; ++r) x |= ld_dev(&bits[(size_t)r * nwords + word]);
       w[e] = x;
       n += (uint32_t)__popc(x);
     }
     uint32_t tot;
-    uint32_t pos = block_incl_scan(n, scan, &tot) - n + carry;
+    uint32_t pos = block_incl_scan(n, scratch, &tot) - n + carry;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       uint32_t x = w[e];
@@ -693,17 +749,120 @@ __device__ __forceinline__ void union_problem(const UnionProblem& P, float* lds)
       while (x) {
         const int bit = __ffs(x) - 1;
         x &= x - 1u;
-        P.idx[pos++] = word * 32 + bit;
+        idx[pos++] = word * 32 + bit;
       }
     }
     carry += tot;
   }
-  if (tid == 0) P.count[0] = (int32_t)carry;
+  return carry;
 }
 
-__device__ __forceinline__ void union_task(const UnionTask& T, int blk, float* lds) {
-  if (blk == 0) union_problem(T.p[0], lds);
-  else union_problem(T.p[1], lds);
+// resolve: one block per row.  Candidates (all of digit D1, index order) are
+// copied to one contiguous list (LDS when few), the `need` largest are picked
+// (equal keys: lower index first), their bits set, and the row (or, for a batch
+// union, all rows once the last one is done) compacted to ascending indices.
+__device__ __forceinline__ void resolve_block(const TopkProblem& P, int b, float* lds) {
+  const int tid = threadIdx.x;
+  uint32_t* lh = reinterpret_cast<uint32_t*>(lds);          // [kHistBins]
+  uint32_t* scratch = lh + kHistBins;                       // [8]
+  uint32_t* bcast = scratch + 8;                            // [4]
+  int* flag = reinterpret_cast<int*>(bcast + 4);            // [4]
+  uint2* lc = reinterpret_cast<uint2*>(lh + kHistBins + 16);   // [kCandCap]
+
+  const uint32_t need = (uint32_t)P.need[b];
+  const int32_t* cc = P.ccount + (size_t)b * P.nseg;
+  uint32_t C = 0u;
+  for (int g = 0; g < P.nseg; ++g) C += (uint32_t)cc[g];
+  uint32_t* bits = P.bits + (size_t)b * P.nwords;
+
+  if (need > 0u && C > 0u) {
+    // contiguous candidate list, index order
+    uint2* cs = (C <= (uint32_t)kCandCap)
+                    ? lc
+                    : P.cand + (size_t)P.batch * P.nseg * kSegElems + (size_t)b * P.N;
+    uint32_t off = 0u;
+    for (int g = 0; g < P.nseg; ++g) {
+      const uint32_t n = (uint32_t)cc[g];
+      const uint2* src = P.cand + ((size_t)b * P.nseg + g) * kSegElems;
+      for (uint32_t i = tid; i < n; i += kThreads) cs[off + i] = src[i];
+      off += n;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // radix over the low 21 bits: [20:10] then [9:0]
+    uint32_t T = cs[0].x & 0xffe00000u;    // all candidates share the top 11 bits
+    uint32_t remaining = need;
+    int hi = 21;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int width = (pass == 0) ? 11 : 10;
+      const int shift = hi - width;
+      const int nbins = 1 << width;
+      __syncthreads();
+      for (int i = tid; i < nbins; i += kThreads) lh[i] = 0u;
+      __syncthreads();
+      for (uint32_t c = tid; c < C; c += kThreads) {
+        const uint32_t key = cs[c].x;
+        if ((key >> hi) == (T >> hi)) atomicAdd(&lh[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+      }
+      __syncthreads();
+      uint32_t D, above;
+      find_digit(lh, nbins, remaining, scratch, bcast, &D, &above);
+      T |= D << shift;
+      remaining -= above;
+      hi = shift;
+    }
+    const uint32_t take = remaining;
+    // index-ordered pass: keep key > T and the first `take` keys equal to T
+    constexpr int E = 16;
+    uint32_t carry_eq = 0u;
+    for (uint32_t base = 0; base < C; base += kThreads * E) {
+      const uint32_t c0 = base + tid * E;
+      uint32_t n_eq = 0u;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (c0 + e < C && cs[c0 + e].x == T) ++n_eq;
+      uint32_t tot;
+      uint32_t eq_before = block_incl_scan(n_eq, scratch, &tot) - n_eq + carry_eq;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (c0 + e < C) {
+          const uint2 kv = cs[c0 + e];
+          bool sel = kv.x > T;
+          if (kv.x == T) { sel = eq_before < take; ++eq_before; }
+          if (sel)
+            __hip_atomic_fetch_or(&bits[kv.y >> 5], 1u << (kv.y & 31u), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      carry_eq += tot;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (!P.unite) {
+    const uint32_t n = compact_bits(bits, 1, P.nwords, P.idx + (size_t)b * P.k, scratch);
+    if (tid == 0) P.count[b] = (int32_t)n;
+    return;
+  }
+  if (!arrive_last(P.ticket, (uint32_t)P.batch, flag)) return;
+  const uint32_t n = compact_bits(P.bits, P.batch, P.nwords, P.idx, scratch);
+  if (tid == 0) P.count[0] = (int32_t)n;
+}
+
+__device__ __forceinline__ void topk_task(int stage, const TopkTask& T, int blk, float* lds) {
+  if (stage == T_RESOLVE) {
+    const int per0 = T.p[0].batch;
+    int lb;
+    if (topk_problem(T, blk, per0, &lb) == 0) resolve_block(T.p[0], lb, lds);
+    else resolve_block(T.p[1], lb, lds);
+    return;
+  }
+  const int per0 = T.p[0].batch * T.p[0].nseg;
+  int lb;
+  const int pi = topk_problem(T, blk, per0, &lb);
+  const TopkProblem& P = pi == 0 ? T.p[0] : T.p[1];
+  if (stage == T_HIST) hist_block(P, lb, lds);
+  else classify_block(P, lb, lds);
 }
 
 // --------------------------------------------------------------------------- //
@@ -714,9 +873,23 @@ template <int FLAGS, int BT>
 __global__ __launch_bounds__(kThreads) void phase_kernel(PhaseArgs a) {
   extern __shared__ float lds[];
   const int blk = blockIdx.x;
+  if constexpr ((FLAGS & T_ZERO) != 0) {
+    if (blk >= a.b_zero && blk < a.b_zero + a.zero.blocks) {
+      for (int i = (blk - a.b_zero) * kThreads + threadIdx.x; i < a.zero.words;
+           i += a.zero.blocks * kThreads)
+        a.zero.ptr[i] = 0u;
+      return;
+    }
+  }
   if constexpr ((FLAGS & T_ROWDOT) != 0) {
     if (blk >= a.b_rowdot && blk < a.b_rowdot + a.rowdot.blocks) {
       rowdot_task<BT>(a.rowdot, blk - a.b_rowdot, lds);
+      return;
+    }
+  }
+  if constexpr ((FLAGS & (T_HIST | T_CLASSIFY | T_RESOLVE)) != 0) {
+    if (blk >= a.b_topk && blk < a.b_topk + a.topk.blocks) {
+      topk_task(FLAGS & (T_HIST | T_CLASSIFY | T_RESOLVE), a.topk, blk - a.b_topk, lds);
       return;
     }
   }
@@ -730,18 +903,6 @@ __global__ __launch_bounds__(kThreads) void phase_kernel(PhaseArgs a) {
   if constexpr ((FLAGS & T_AXPY) != 0) {
     if (blk >= a.b_axpy && blk < a.b_axpy + a.axpy.blocks) {
       axpy_task<BT>(a.axpy, blk - a.b_axpy, lds);
-      return;
-    }
-  }
-  if constexpr ((FLAGS & T_SELECT) != 0) {
-    if (blk >= a.b_select && blk < a.b_select + a.select.blocks) {
-      select_task(a.select, blk - a.b_select, lds);
-      return;
-    }
-  }
-  if constexpr ((FLAGS & T_UNION) != 0) {
-    if (blk >= a.b_union && blk < a.b_union + a.uni.blocks) {
-      union_task(a.uni, blk - a.b_union, lds);
       return;
     }
   }
@@ -768,10 +929,12 @@ int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes,
     case T_ROWDOT: return launch_bt<T_ROWDOT>(bt, a, grid, lds_bytes, stream);
     case T_AXPY: return launch_bt<T_AXPY>(bt, a, grid, lds_bytes, stream);
     case T_ATTN | T_AXPY: return launch_bt<T_ATTN | T_AXPY>(bt, a, grid, lds_bytes, stream);
-    case T_AXPY | T_SELECT: return launch_bt<T_AXPY | T_SELECT>(bt, a, grid, lds_bytes, stream);
+    case T_AXPY | T_CLASSIFY: return launch_bt<T_AXPY | T_CLASSIFY>(bt, a, grid, lds_bytes, stream);
     case T_ATTN: return launch_t<T_ATTN, 1>(a, grid, lds_bytes, stream);
-    case T_SELECT: return launch_t<T_SELECT, 1>(a, grid, lds_bytes, stream);
-    case T_UNION: return launch_t<T_UNION, 1>(a, grid, lds_bytes, stream);
+    case T_ZERO: return launch_t<T_ZERO, 1>(a, grid, lds_bytes, stream);
+    case T_HIST: return launch_t<T_HIST, 1>(a, grid, lds_bytes, stream);
+    case T_CLASSIFY: return launch_t<T_CLASSIFY, 1>(a, grid, lds_bytes, stream);
+    case T_RESOLVE: return launch_t<T_RESOLVE, 1>(a, grid, lds_bytes, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }

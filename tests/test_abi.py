@@ -98,7 +98,7 @@ def call_mha(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(K=None), dv.DV_EINVAL), (dict(n_ctx=0), dv.DV_EINVAL), (dict(h=0), dv.DV_EINVAL),
     (dict(max_count=5), dv.DV_EINVAL), (dict(dh=48), dv.DV_EUNSUPPORTED),
-    (dict(dh=512), dv.DV_EUNSUPPORTED), (dict(n_ctx=64 * 2048 + 1), dv.DV_EUNSUPPORTED),
+    (dict(dh=512), dv.DV_EUNSUPPORTED), (dict(n_ctx=(1 << 20) + 1), dv.DV_EUNSUPPORTED),
     (dict(V=BAD), dv.DV_EALIGN), (dict(kvdt=3), dv.DV_EINVAL), (dict(scale=float("nan")), dv.DV_EINVAL),
     (dict(ws_bytes=16), dv.DV_EWORKSPACE), (dict(d=12), dv.DV_EALIGN),
 ])

@@ -1,0 +1,40 @@
+"""Byte accounting used by the benchmark, pinned to the survey-notes page's KV-cache
+sizing example and to the sizes the configs imply."""
+from conftest import load_golden
+
+from contextual_sparsity_mlp_amd import accounting as A
+from contextual_sparsity_mlp_amd.synth import CONFIGS
+
+
+def test_kv_bytes_example():
+    g = load_golden("kv_bytes.json")
+    per = A.kv_bytes_per_token(g["hidden"], g["layers"], g["bytes_per_elem"])
+    assert per == g["per_token_bytes"]
+    assert per * g["tokens"] == g["total_bytes"]
+
+
+def test_c4_batch1_bytes():
+    c = CONFIGS["c4"]
+    b = A.step_bytes(batch=1, d=c.d, F=c.F, h=c.h, dh=c.dh, n_ctx=c.n_ctx, r=c.r, u_m=c.k_m,
+                     u_a=c.k_a)
+    # 4915 neurons x 2 rows x 12288 x 2 B; 19 heads x 2 x 128 rows x 12288 x 2 B;
+    # 19 heads x 2 x 2048 tokens x 128 x 2 B
+    assert b.mlp == 4915 * 2 * 12288 * 2 == 241_582_080
+    assert b.attn_weights == 19 * 2 * 128 * 12288 * 2
+    assert b.kv == 19 * 2 * 2048 * 128 * 2
+    assert b.predictor == (2 * 12288 * 1000 + 1000 * 49152 + 1000 * 96) * 2
+    # the KV of one selected head and token matches the per-token formula for one layer
+    assert b.kv == A.kv_bytes_per_token(c.dh, 1) * c.n_ctx * c.k_a
+    ph = A.phase_bytes(batch=1, d=c.d, F=c.F, h=c.h, dh=c.dh, n_ctx=c.n_ctx, r=c.r, u_m=c.k_m,
+                       u_a=c.k_a)
+    # the three launches together move every algorithmic byte of the step once,
+    # plus y read a second time, the MLP result written and read, and the scores
+    assert sum(ph) == b.total + 3 * c.d * 4 + (c.F + c.h) * 4
+
+
+def test_flops_intensity_batch1():
+    c = CONFIGS["c4"]
+    kw = dict(d=c.d, F=c.F, h=c.h, dh=c.dh, n_ctx=c.n_ctx, r=c.r, u_m=c.k_m, u_a=c.k_a)
+    f = A.step_flops(batch=1, **kw)
+    b = A.step_bytes(batch=1, **kw).total
+    assert 0.9 < f / b < 1.1      # about one flop per byte at batch 1: bound by HBM
