@@ -270,7 +270,9 @@ void finish_rowdot(RowdotTask& T, const float* y, int batch, int d, uint32_t* ze
   int cap = 0;
   for (int s = 0; s < T.nseg; ++s) cap += T.seg[s].cap;
   const int want = std::max(1, cdiv(cap, kWaves));
-  T.blocks = std::min(want, device_cus() * 4);
+  // one resident round: LDS holds bt_lds * d floats per block
+  const int per_cu = std::max(1, std::min(4, (160 * 1024) / std::max(1, T.bt_lds * d * 4)));
+  T.blocks = std::min(want, device_cus() * per_cu);
   T.zero_ptr = zero; T.zero_words = nzero;
 }
 int rowdot_lds(const RowdotTask& T) { return T.bt_lds * T.d * 4; }
@@ -286,10 +288,11 @@ void add_axpy(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype 
   S.W = W; S.row_stride = stride; S.wdt = (wdt == DV_BF16) ? W_BF16 : W_F32;
   S.rows = L; S.coef = coef; S.coef_ld = coef_ld; S.relu = relu; S.ncols = ncols;
   S.vec = g.vec; S.nslices = g.nslices; S.nbt = g.nbt;
-  // About three blocks per CU for the segment; at most kMaxChunks chunk partials per
-  // slice (a short, fixed-order final sum) and at least one row per row group.
+  // About six blocks per CU for the segment (512-byte row slices need that many
+  // loads in flight to stream well); at most kMaxChunks chunk partials per slice
+  // (a short, fixed-order final sum) and at least one row per row group.
   const int per_chunk = g.nslices * g.nbt;
-  int chunks = cdiv(device_cus() * 3, per_chunk);
+  int chunks = cdiv(device_cus() * 6, per_chunk);
   chunks = std::min(chunks, std::max(1, cap_rows / kAxGroups));
   S.nchunks = std::max(1, std::min(chunks, g.chunks_max));
   S.block0 = T.blocks;
@@ -325,7 +328,7 @@ int attn_lds() { return (128 + 2048 + 16) * 4; }
 
 int hist_lds() { return kHistBins * 4; }
 int classify_lds() { return (kHistBins + 16) * 4; }
-int resolve_lds() { return (kHistBins + 16) * 4 + kCandCap * 8; }
+int resolve_lds(int max_nseg) { return (kHistBins + 16) * 4 + kCandCap * 8 + (max_nseg + 1) * 4; }
 
 // One top-k problem over `batch` score rows of N (row stride ld).
 TopkProblem make_topk(const float* scores, int ld, int N, int k, int batch, int unite,
@@ -510,7 +513,7 @@ int dv_select_topk(const float* scores, int batch, int N, int k, int union_rows,
   if (int e = launch(T_HIST, 1, a, a.topk.blocks, hist_lds(), stream, fn)) return e;
   if (int e = launch(T_CLASSIFY, 1, a, a.topk.blocks, classify_lds(), stream, fn)) return e;
   a.topk.blocks = topk_row_blocks(a.topk);
-  return launch(T_RESOLVE, 1, a, a.topk.blocks, resolve_lds(), stream, fn);
+  return launch(T_RESOLVE, 1, a, a.topk.blocks, resolve_lds(a.topk.p[0].nseg), stream, fn);
 }
 
 int dv_sparse_mlp(const float* y, int batch, int d, const void* W1t, const void* W2t, int F,
@@ -724,7 +727,8 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     PhaseArgs a4 = zero_args();
     a4.topk = tk3;
     a4.topk.blocks = topk_row_blocks(tk3);
-    if (int e = launch(T_RESOLVE, 1, a4, a4.topk.blocks, resolve_lds(), stream, fn)) return e;
+    const int ms = std::max(tk3.p[0].nseg, tk3.p[1].nseg);
+    if (int e = launch(T_RESOLVE, 1, a4, a4.topk.blocks, resolve_lds(ms), stream, fn)) return e;
   }
   return DV_OK;
 }

@@ -21,7 +21,7 @@ namespace dv {
 constexpr int kThreads = 256;            // threads per block, every kernel
 constexpr int kWaves = kThreads / 64;    // wave64
 constexpr int kMaxSeg = 4;               // segments per rowdot / axpy task
-constexpr int kMaxChunks = 16;           // row chunks per axpy segment (partials bound)
+constexpr int kMaxChunks = 32;           // row chunks per axpy segment (partials bound)
 constexpr int kAxSliceLanes = 32;        // lanes across the columns of one axpy slice
 constexpr int kAxGroups = 8;             // row groups (half-waves) per axpy block
 constexpr int kAxpyTileRows = 512;       // axpy rows whose ids / coefficients sit in LDS

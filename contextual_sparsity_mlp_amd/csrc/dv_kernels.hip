@@ -50,6 +50,19 @@ __device__ __forceinline__ void unpack8(const uint4& x, float (&f)[8]) {
   f[6] = bf16_lo(x.w); f[7] = bf16_hi(x.w);
 }
 
+// Streaming loads of weights and cache rows: each byte is read once per call, so
+// the loads are marked non-temporal (they bypass reuse in the caches).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // Device-coherent accesses for values handed between blocks of one launch.
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -173,7 +186,7 @@ __device__ __forceinline__ void rowdot_bf16(const uint4* __restrict__ rp, const 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int v = v0 + u * 64 + lane;
-      w[u] = (v < nv) ? rp[v] : make_uint4(0u, 0u, 0u, 0u);
+      w[u] = (v < nv) ? ld_stream(rp + v) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -208,7 +221,7 @@ __device__ __forceinline__ void rowdot_f32(const float4* __restrict__ rp, const 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int v = v0 + u * 64 + lane;
-      w[u] = (v < nv) ? rp[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+      w[u] = (v < nv) ? ld_stream(rp + v) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -273,7 +286,7 @@ __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float*
         if (S.wdt == W_BF16) {
           const uint4* rp = reinterpret_cast<const uint4*>(
               static_cast<const uint16_t*>(S.W) + row * S.row_stride);
-          rowdot_bf16<BT, 8>(rp, lds, d, nb, lane, acc);
+          rowdot_bf16<BT, 24>(rp, lds, d, nb, lane, acc);
         } else {
           const float4* rp = reinterpret_cast<const float4*>(
               static_cast<const float*>(S.W) + row * S.row_stride);
@@ -310,11 +323,11 @@ template <int VEC, int WT>
 __device__ __forceinline__ void load_cols(const void* W, long long off, float (&w)[VEC]) {
   if constexpr (WT == W_BF16 && VEC == 8) {
     float f[8];
-    unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + off), f);
+    unpack8(ld_stream(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + off)), f);
 #pragma unroll
     for (int v = 0; v < 8; ++v) w[v] = f[v];
   } else if constexpr (WT == W_F32 && VEC == 4) {
-    const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + off);
+    const float4 x = ld_stream(reinterpret_cast<const float4*>(static_cast<const float*>(W) + off));
     w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
   } else if constexpr (WT == W_BF16) {
     w[0] = __uint_as_float((uint32_t)(static_cast<const uint16_t*>(W)[off]) << 16);
@@ -341,7 +354,7 @@ __device__ __forceinline__ void hist_flush_one(float score, bool active, uint32_
 // One block: a slice of kAxSliceLanes*VEC output columns and a chunk of the row list.
 template <int BT, int VEC, int WT>
 __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, float* lds) {
-  constexpr int U = 8;
+  constexpr int U = 4;
   constexpr int SW = kAxSliceLanes * VEC;    // columns per slice
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave * 2 + (lane >> 5);
@@ -769,10 +782,21 @@ __device__ __forceinline__ void resolve_block(const TopkProblem& P, int b, float
   int* flag = reinterpret_cast<int*>(bcast + 4);            // [4]
   uint2* lc = reinterpret_cast<uint2*>(lh + kHistBins + 16);   // [kCandCap]
 
+  uint32_t* segoff = reinterpret_cast<uint32_t*>(lc + kCandCap);   // [nseg + 1]
   const uint32_t need = (uint32_t)P.need[b];
   const int32_t* cc = P.ccount + (size_t)b * P.nseg;
+  // segment offsets of the candidate list (index order), all segments in parallel
   uint32_t C = 0u;
-  for (int g = 0; g < P.nseg; ++g) C += (uint32_t)cc[g];
+  for (int g0 = 0; g0 < P.nseg; g0 += kThreads) {
+    const int g = g0 + tid;
+    const uint32_t n = (g < P.nseg) ? (uint32_t)cc[g] : 0u;
+    uint32_t tot;
+    const uint32_t inc = block_incl_scan(n, scratch, &tot);
+    if (g < P.nseg) segoff[g] = C + inc - n;
+    C += tot;
+  }
+  if (tid == 0) segoff[P.nseg] = C;
+  __syncthreads();
   uint32_t* bits = P.bits + (size_t)b * P.nwords;
 
   if (need > 0u && C > 0u) {
@@ -780,12 +804,28 @@ __device__ __forceinline__ void resolve_block(const TopkProblem& P, int b, float
     uint2* cs = (C <= (uint32_t)kCandCap)
                     ? lc
                     : P.cand + (size_t)P.batch * P.nseg * kSegElems + (size_t)b * P.N;
-    uint32_t off = 0u;
-    for (int g = 0; g < P.nseg; ++g) {
-      const uint32_t n = (uint32_t)cc[g];
-      const uint2* src = P.cand + ((size_t)b * P.nseg + g) * kSegElems;
-      for (uint32_t i = tid; i < n; i += kThreads) cs[off + i] = src[i];
-      off += n;
+    const uint2* src = P.cand + (size_t)b * P.nseg * kSegElems;
+    constexpr int UG = 16;   // candidates in flight per thread
+    for (uint32_t c0 = 0; c0 < C; c0 += kThreads * UG) {
+      uint2 v[UG];
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        const uint32_t c = c0 + u * kThreads + tid;
+        if (c < C) {
+          // segment of candidate c: the last g with segoff[g] <= c
+          int lo = 0, hi = P.nseg - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (segoff[mid] <= c) lo = mid; else hi = mid - 1;
+          }
+          v[u] = src[(size_t)lo * kSegElems + (c - segoff[lo])];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        const uint32_t c = c0 + u * kThreads + tid;
+        if (c < C) cs[c] = v[u];
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
