@@ -129,15 +129,14 @@ size_t ax_tickets(const AxGeo& g) { return (size_t)g.nbt * g.nslices; }
 int attn_nsplit_max(int n_ctx) { return std::max(1, std::min(kMaxSplit, cdiv(n_ctx, 64))); }
 
 // Top-k scratch for one problem (N scores per row, `batch` rows).
-struct TopkWs { size_t bits, cand, ccount, need; int nseg, nwords; };
+struct TopkWs { size_t bits, cand, ccount; int nseg, nwords; };
 TopkWs plan_topk_parts(Ws& w, int batch, int N) {
   TopkWs t;
   t.nseg = cdiv(N, kSegElems);
   t.nwords = cdiv(N, 32);
   t.bits = w.take((size_t)batch * t.nwords * 4);
-  t.cand = w.take(((size_t)batch * t.nseg * kSegElems + (size_t)batch * N) * 8);
+  t.cand = w.take((size_t)batch * t.nseg * kSegElems * 8);
   t.ccount = w.take((size_t)batch * t.nseg * 4);
-  t.need = w.take((size_t)batch * 4);
   return t;
 }
 
@@ -154,13 +153,14 @@ PredictWs plan_predict(int batch, int d, int r, int N, dv_dtype wdt) {
   return p;
 }
 
-// Zero region first: histogram [batch][kHistBins] and the union ticket.
-struct SelectWs { size_t zero, hist, ticket, total; int zero_words; TopkWs t; };
+// Zero region first: histogram [batch][kHistBins], row tickets [batch], union ticket.
+struct SelectWs { size_t zero, hist, rtick, ticket, total; int zero_words; TopkWs t; };
 SelectWs plan_select(int batch, int N) {
   SelectWs p; Ws w;
   p.zero = w.off;
-  p.hist = w.take((size_t)batch * kHistBins * 4);
-  p.ticket = p.hist + (size_t)batch * kHistBins * 4;
+  p.hist = p.zero;
+  p.rtick = p.hist + (size_t)batch * kHistBins * 4;
+  p.ticket = p.rtick + (size_t)batch * 4;
   w.off = align256(p.ticket + 4);
   p.zero_words = (int)((p.ticket + 4 - p.zero) / 4);
   p.t = plan_topk_parts(w, batch, N);
@@ -196,9 +196,9 @@ MhaWs plan_mha(int batch, int d, int dh, int n_ctx, int cap, dv_dtype wdt) {
   return p;
 }
 
-// Zero region first: all tickets, both score histograms and both union tickets.
+// Zero region first: all tickets, both score histograms, row and union tickets.
 struct LayerWs {
-  size_t zero, tickets, hist_m, hist_a, uticket;
+  size_t zero, tickets, hist_m, hist_a, rtick_m, rtick_a, uticket;
   size_t a, q, o, part, zm, za, mlp_out, sm, sa;
   size_t p_mlp, p_bm, p_ba, p_wo, total;
   int t_attn, t_mlp, t_bm, t_ba, t_wo, t_total, zero_words;
@@ -224,7 +224,9 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   p.tickets = p.zero;
   p.hist_m = p.tickets + (size_t)p.t_total * 4;
   p.hist_a = p.hist_m + (size_t)batch * kHistBins * 4;
-  p.uticket = p.hist_a + (size_t)batch * kHistBins * 4;
+  p.rtick_m = p.hist_a + (size_t)batch * kHistBins * 4;
+  p.rtick_a = p.rtick_m + (size_t)batch * 4;
+  p.uticket = p.rtick_a + (size_t)batch * 4;
   w.off = align256(p.uticket + 8);
   p.zero_words = (int)((p.uticket + 8 - p.zero) / 4);
   p.a = w.take((size_t)batch * cap_m * 4);
@@ -327,33 +329,26 @@ void setup_attn(AttnTask& A, const float* q, int q_ld, const void* K, const void
 int attn_lds() { return (128 + 2048 + 16) * 4; }
 
 int hist_lds() { return kHistBins * 4; }
-int classify_lds() { return (kHistBins + 16) * 4; }
-int resolve_lds(int max_nseg) { return (kHistBins + 16) * 4 + kCandCap * 8 + (max_nseg + 1) * 4; }
+int classify_lds() { return (16 + kLowBins + kResolveWords + kMaxSegs + 1) * 4; }
 
 // One top-k problem over `batch` score rows of N (row stride ld).
 TopkProblem make_topk(const float* scores, int ld, int N, int k, int batch, int unite,
-                      int32_t* idx, int32_t* count, uint32_t* hist, uint32_t* ticket, char* ws,
-                      const TopkWs& t) {
+                      int32_t* idx, int32_t* count, uint32_t* hist, uint32_t* row_tickets,
+                      uint32_t* ticket, char* ws, const TopkWs& t) {
   TopkProblem P;
   P.scores = scores; P.ld = ld; P.N = N; P.k = k; P.batch = batch;
   P.unite = (unite && batch > 1) ? 1 : 0;
-  P.idx = idx; P.count = count; P.hist = hist; P.ticket = ticket;
+  P.idx = idx; P.count = count; P.hist = hist; P.row_tickets = row_tickets; P.ticket = ticket;
   P.bits = reinterpret_cast<uint32_t*>(ws + t.bits);
   P.nwords = cdiv(N, 32);
   P.cand = reinterpret_cast<uint2*>(ws + t.cand);
   P.ccount = reinterpret_cast<int32_t*>(ws + t.ccount);
-  P.need = reinterpret_cast<int32_t*>(ws + t.need);
   P.nseg = cdiv(N, kSegElems);
   return P;
 }
 int topk_seg_blocks(const TopkTask& T) {
   int n = 0;
   for (int i = 0; i < T.np; ++i) n += T.p[i].batch * T.p[i].nseg;
-  return n;
-}
-int topk_row_blocks(const TopkTask& T) {
-  int n = 0;
-  for (int i = 0; i < T.np; ++i) n += T.p[i].batch;
   return n;
 }
 
@@ -493,6 +488,8 @@ int dv_select_topk(const float* scores, int batch, int N, int k, int union_rows,
   if (batch <= 0) return fail(DV_EINVAL, "%s: batch = %d", fn, batch);
   if (N <= 0) return fail(DV_EINVAL, "%s: N = %d", fn, N);
   if (k < 0 || k > N) return fail(DV_EINVAL, "%s: k = %d not in [0, N = %d]", fn, k, N);
+  if (N > kMaxSegs * kSegElems)
+    return fail(DV_EUNSUPPORTED, "%s: N = %d exceeds %d", fn, N, kMaxSegs * kSegElems);
   CHECK_ALIGN(scores); CHECK_ALIGN(idx); CHECK_ALIGN(count);
   const SelectWs P = plan_select(batch, N);
   if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
@@ -508,12 +505,11 @@ int dv_select_topk(const float* scores, int batch, int N, int k, int union_rows,
   a.topk.np = 1;
   a.topk.p[0] = make_topk(scores, N, N, k, batch, union_rows,
                           idx, count, reinterpret_cast<uint32_t*>(w + P.hist),
+                          reinterpret_cast<uint32_t*>(w + P.rtick),
                           reinterpret_cast<uint32_t*>(w + P.ticket), w, P.t);
   a.topk.blocks = topk_seg_blocks(a.topk);
   if (int e = launch(T_HIST, 1, a, a.topk.blocks, hist_lds(), stream, fn)) return e;
-  if (int e = launch(T_CLASSIFY, 1, a, a.topk.blocks, classify_lds(), stream, fn)) return e;
-  a.topk.blocks = topk_row_blocks(a.topk);
-  return launch(T_RESOLVE, 1, a, a.topk.blocks, resolve_lds(a.topk.p[0].nseg), stream, fn);
+  return launch(T_CLASSIFY, 1, a, a.topk.blocks, classify_lds(), stream, fn);
 }
 
 int dv_sparse_mlp(const float* y, int batch, int d, const void* W1t, const void* W2t, int F,
@@ -639,6 +635,8 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     if (r <= 0 || Fn <= 0 || hn <= 0) return fail(DV_EINVAL, "%s: next r/F/h", fn);
     if (km < 0 || km > Fn || ka < 0 || ka > hn)
       return fail(DV_EINVAL, "%s: next k_m = %d / k_a = %d out of range", fn, km, ka);
+    if (Fn > kMaxSegs * kSegElems)
+      return fail(DV_EUNSUPPORTED, "%s: next F = %d exceeds %d", fn, Fn, kMaxSegs * kSegElems);
   }
   const dv_dtype wdt = L->wdt;
   const LayerWs P = plan_layer(batch, d, std::max(F, Fn), std::max(h, hn), dh, n, r, max_count_m,
@@ -698,8 +696,9 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   const int lds2 = std::max(axpy_lds(bt), (flags2 & T_ATTN) ? attn_lds() : 0);
   if (int e = launch(flags2, bt, a2, a2.attn.blocks + a2.axpy.blocks, lds2, stream, fn)) return e;
 
-  // Phase 3: W^O rows scaled by the head outputs, added to y_in + MLP; the next
-  // layer's top-k classifies its scores beside it.
+  // Phase 3: W^O rows scaled by the head outputs, added to y_in + MLP; beside it the
+  // next layer's top-k classifies its scores, and the last block of each row
+  // resolves that row (and, for a batch, the union).
   PhaseArgs a3 = zero_args();
   add_axpy(a3.axpy, batch, L->Wo, d, wdt, LQ, fp(P.o), cap_a * dh, 0, d, fp(P.p_wo), t_wo, y_out, d,
            y_in, fp(P.mlp_out), d, 0);
@@ -710,9 +709,9 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   if (nx) {
     tk3.np = 2;
     tk3.p[0] = make_topk(fp(P.sm), Fn, Fn, km, batch, 1, next_idx_m, next_count_m, up(P.hist_m),
-                         up(P.uticket), w, P.tm);
+                         up(P.rtick_m), up(P.uticket), w, P.tm);
     tk3.p[1] = make_topk(fp(P.sa), hn, hn, ka, batch, 1, next_idx_a, next_count_a, up(P.hist_a),
-                         up(P.uticket) + 1, w, P.ta);
+                         up(P.rtick_a), up(P.uticket) + 1, w, P.ta);
     tk3.blocks = topk_seg_blocks(tk3);
     a3.topk = tk3;
     flags3 |= T_CLASSIFY;
@@ -722,14 +721,6 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   const int lds3 = std::max(axpy_lds(bt), (flags3 & T_CLASSIFY) ? classify_lds() : 0);
   if (int e = launch(flags3, bt, a3, a3.topk.blocks + a3.axpy.blocks, lds3, stream, fn)) return e;
 
-  // Phase 4: the next layer's sets (and, for a batch, their union).
-  if (nx) {
-    PhaseArgs a4 = zero_args();
-    a4.topk = tk3;
-    a4.topk.blocks = topk_row_blocks(tk3);
-    const int ms = std::max(tk3.p[0].nseg, tk3.p[1].nseg);
-    if (int e = launch(T_RESOLVE, 1, a4, a4.topk.blocks, resolve_lds(ms), stream, fn)) return e;
-  }
   return DV_OK;
 }
 

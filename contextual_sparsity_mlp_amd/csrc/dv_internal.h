@@ -27,9 +27,14 @@ constexpr int kAxGroups = 8;             // row groups (half-waves) per axpy blo
 constexpr int kAxpyTileRows = 512;       // axpy rows whose ids / coefficients sit in LDS
 constexpr int kMaxSplit = 64;            // key splits per (token, head)
 constexpr int kLdsBudget = 64 * 1024;    // dynamic LDS per block
-constexpr int kHistBins = 2048;          // top 11 bits of a score key
+constexpr int kTopShift = 20;            // first-level digit: the top 12 bits of a score key
+constexpr int kHistBins = 1 << (32 - kTopShift);
+constexpr int kLowBins = 1024;           // the remaining 20 bits: two 10-bit digits
 constexpr int kSegElems = kThreads * 8;  // scores per top-k classify block
-constexpr int kCandCap = 4096;           // candidates a resolve block keeps in LDS
+constexpr int kCandPerThread = 8;        // candidates a resolving thread holds in registers
+constexpr int kCandTile = kThreads * kCandPerThread;
+constexpr int kResolveWords = 1536;      // bitmask words a resolving block keeps in LDS (N <= 49152)
+constexpr int kMaxSegs = 256;            // classify segments per row (N <= 524288)
 constexpr int kWordsPerThread = 4;       // bitmask words per thread when compacting
 
 enum : int { W_F32 = 0, W_BF16 = 1 };
@@ -111,15 +116,16 @@ struct AttnTask {
   int blocks;              // batch * cap * nsplit
 };
 
-// Exact top-k of score rows, in three steps that each spread over many blocks:
-//   hist     11-bit top-digit histogram of every row (built by the blocks that
+// Exact top-k of score rows, in two steps that each spread over many blocks:
+//   hist     12-bit top-digit histogram of every row (built by the blocks that
 //            produce the scores, or by a launch of its own)
 //   classify one block per (row, segment of kSegElems scores): finds the digit of
 //            the k-th key from the histogram, marks keys above it in the row's
-//            bitmask and lists the keys of that digit (index order) as candidates
-//   resolve  one block per row: picks the needed candidates (lower index first on
-//            equal keys), ORs them into the bitmask and compacts the ascending
-//            index list; with a batch union the last row to finish ORs all rows.
+//            bitmask and lists the keys of that digit (index order) as candidates.
+//            The last segment of a row to finish resolves the row: it picks the
+//            needed candidates (lower index first on equal keys), ORs them into the
+//            bitmask and compacts the ascending index list; with a batch union the
+//            last row to be resolved ORs all rows.
 struct TopkProblem {
   const float* scores;     // row b at scores + b * ld
   int ld, N, k, batch;
@@ -129,11 +135,11 @@ struct TopkProblem {
   uint32_t* hist;          // [batch][kHistBins], zero before it is built
   uint32_t* bits;          // [batch][nwords]
   int nwords;
-  uint2* cand;             // [batch][nseg * kSegElems] (key, index); [batch][N] scratch follows
+  uint2* cand;             // [batch][nseg * kSegElems] (key, index) per segment
   int32_t* ccount;         // [batch][nseg] candidates per segment
-  int32_t* need;           // [batch] candidates to keep
-  uint32_t* ticket;        // rows resolved (union), zero before the resolve launch
-  int nseg;                // segments per row = ceil(N / kSegElems)
+  uint32_t* row_tickets;   // [batch] segments classified, zero before classify
+  uint32_t* ticket;        // rows resolved (union), zero before classify
+  int nseg;                // segments per row = ceil(N / kSegElems) <= kMaxSegs
 };
 
 struct TopkTask {
@@ -148,8 +154,7 @@ struct ZeroTask {
   int blocks;
 };
 
-enum : int { T_ROWDOT = 1, T_ATTN = 2, T_AXPY = 4, T_HIST = 8, T_CLASSIFY = 16, T_RESOLVE = 32,
-             T_ZERO = 64 };
+enum : int { T_ROWDOT = 1, T_ATTN = 2, T_AXPY = 4, T_HIST = 8, T_CLASSIFY = 16, T_ZERO = 64 };
 
 struct PhaseArgs {
   RowdotTask rowdot;

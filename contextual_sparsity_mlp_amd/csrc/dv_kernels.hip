@@ -21,7 +21,8 @@
 //           (max, sum, p.V), then the last split to finish merges the splits
 //           (splitting the key axis follows the Flash-Decoding idea named on the
 //           survey-notes page).
-//  top-k    hist / classify / resolve, see dv_internal.h.
+//  top-k    hist / classify (with the row's resolve in its last block), see
+//           dv_internal.h.
 //
 // Blocks of one launch hand values to each other only through device-coherent
 // (agent-scope) atomic stores and loads plus a wait for store completion before
@@ -131,30 +132,30 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Given a histogram `h` of nbins digits (bin = digit), in LDS, and `remaining` >= 1
-// keys still to pick from the top, find the digit D holding the remaining-th key
-// from the top and the number of keys in bins above D.  All threads call; the
-// result is returned to every thread.
-__device__ __forceinline__ void find_digit(const uint32_t* h, int nbins, uint32_t remaining,
+// Threshold digit from a histogram of nbins = kThreads * PT digits: thread t holds
+// the counts of bins top, top-1, ..., top-PT+1 with top = nbins - 1 - t*PT, so a
+// block scan in thread order counts keys from the top.  Finds the digit D holding
+// the remaining-th key from the top (remaining >= 1) and the number of keys in bins
+// above D; every thread receives both.
+template <int PT>
+__device__ __forceinline__ void find_digit(const uint32_t (&hv)[PT], uint32_t remaining,
                                            uint32_t* scratch, uint32_t* bcast, uint32_t* D,
                                            uint32_t* above) {
-  const int tid = threadIdx.x;
-  const int per_t = nbins / kThreads;
-  const int top = nbins - 1 - tid * per_t;
+  const int top = kThreads * PT - 1 - (int)threadIdx.x * PT;
   uint32_t v = 0u;
-  for (int j = 0; j < per_t; ++j) v += h[top - j];
+#pragma unroll
+  for (int j = 0; j < PT; ++j) v += hv[j];
   uint32_t tot;
   const uint32_t inc = block_incl_scan(v, scratch, &tot);
   if (v > 0u && inc >= remaining && inc - v < remaining) {
     uint32_t cum = inc - v;
-    for (int j = 0; j < per_t; ++j) {
-      const uint32_t c = h[top - j];
-      if (cum + c >= remaining) {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      if (cum < remaining && cum + hv[j] >= remaining) {
         bcast[0] = (uint32_t)(top - j);
         bcast[1] = cum;
-        break;
       }
-      cum += c;
+      cum += hv[j];
     }
   }
   __syncthreads();
@@ -343,7 +344,7 @@ __device__ __forceinline__ void hist_flush_one(float score, bool active, uint32_
   __syncthreads();
   for (int i = tid; i < kHistBins; i += kThreads) lh[i] = 0u;
   __syncthreads();
-  if (active) atomicAdd(&lh[score_key(score) >> 21], 1u);
+  if (active) atomicAdd(&lh[score_key(score) >> kTopShift], 1u);
   __syncthreads();
   for (int i = tid; i < kHistBins; i += kThreads) {
     const uint32_t c = lh[i];
@@ -525,7 +526,7 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
 template <int WT>
 __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds) {
   constexpr int VEC = (WT == W_BF16) ? 8 : 4;
-  constexpr int U = 4;
+  constexpr int U = 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = T.heads.host_count;
   const int split = blk % T.nsplit;
@@ -666,7 +667,7 @@ __device__ __forceinline__ void hist_block(const TopkProblem& P, int lb, float* 
   __syncthreads();
   const int j0 = g * kSegElems;
   const int j1 = min(j0 + kSegElems, P.N);
-  for (int j = j0 + tid; j < j1; j += kThreads) atomicAdd(&lh[score_key(s[j]) >> 21], 1u);
+  for (int j = j0 + tid; j < j1; j += kThreads) atomicAdd(&lh[score_key(s[j]) >> kTopShift], 1u);
   __syncthreads();
   uint32_t* gh = P.hist + (size_t)b * kHistBins;
   for (int i = tid; i < kHistBins; i += kThreads) {
@@ -675,67 +676,26 @@ __device__ __forceinline__ void hist_block(const TopkProblem& P, int lb, float* 
   }
 }
 
-// classify: one block per (row, segment of kSegElems scores, 8 per thread).
-__device__ __forceinline__ void classify_block(const TopkProblem& P, int lb, float* lds) {
-  const int tid = threadIdx.x;
-  const int g = lb % P.nseg, b = lb / P.nseg;
-  uint32_t* lh = reinterpret_cast<uint32_t*>(lds);        // [kHistBins]
-  uint32_t* scratch = lh + kHistBins;                     // [8]
-  uint32_t* bcast = scratch + 8;                          // [2]
-  const int N = P.N;
-  const int k = min(max(P.k, 0), N);
-
-  // digit D1 of the k-th key from the top, and how many keys of that digit are needed
-  int D1;
-  uint32_t need = 0u;
-  if (k == 0) {
-    D1 = kHistBins;          // nothing above, nothing equal
-  } else if (k == N) {
-    D1 = -1;                 // everything above
-  } else {
-    const uint32_t* gh = P.hist + (size_t)b * kHistBins;
-    for (int i = tid; i < kHistBins; i += kThreads) lh[i] = gh[i];
-    __syncthreads();
-    uint32_t D, above;
-    find_digit(lh, kHistBins, (uint32_t)k, scratch, bcast, &D, &above);
-    D1 = (int)D;
-    need = (uint32_t)k - above;
-  }
-
-  const float* s = P.scores + (size_t)b * P.ld;
-  const int j0 = g * kSegElems + tid * 8;
-  uint32_t keys[8];
-  uint32_t m8 = 0u, n_cand = 0u;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int j = j0 + e;
-    keys[e] = (j < N) ? score_key(s[j]) : 0u;
-    const int dig = (int)(keys[e] >> 21);
-    if (j < N && dig > D1) m8 |= 1u << e;
-    if (j < N && dig == D1) ++n_cand;
-  }
-  uint32_t tot;
-  uint32_t pos = block_incl_scan(n_cand, scratch, &tot) - n_cand;
-  uint2* cand = P.cand + ((size_t)b * P.nseg + g) * kSegElems;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int j = j0 + e;
-    if (j < N && (int)(keys[e] >> 21) == D1) cand[pos++] = make_uint2(keys[e], (uint32_t)j);
-  }
-  // four threads fill one 32-bit word (8 elements each)
-  uint32_t w = m8 << ((tid & 3) * 8);
-  w |= __shfl_xor(w, 1);
-  w |= __shfl_xor(w, 2);
-  const int word = j0 >> 5;
-  if ((tid & 3) == 0 && word < P.nwords) P.bits[(size_t)b * P.nwords + word] = w;
-  if (tid == 0) {
-    P.ccount[(size_t)b * P.nseg + g] = (int32_t)tot;
-    if (g == 0) P.need[b] = (int32_t)need;
-  }
+__device__ __forceinline__ void st_dev_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u64(uint2* p, uint2 v) {
+  const unsigned long long x = ((unsigned long long)v.y << 32) | v.x;
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), x, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint2 ld_dev_u64(const uint2* p) {
+  const unsigned long long x = __hip_atomic_load(
+      reinterpret_cast<unsigned long long*>(const_cast<uint2*>(p)), __ATOMIC_RELAXED,
+      __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2((uint32_t)x, (uint32_t)(x >> 32));
 }
 
-// Ascending indices of the set bits of `nwords` words (read with ld_dev) into idx;
-// returns the count.  `rows` words arrays at stride `nwords` are ORed first.
+// Ascending indices of the set bits of `nwords` words into idx; returns the count.
+// `rows` words arrays at stride `nwords` are ORed first.  COHERENT: the words were
+// written by other blocks of this launch (read with ld_dev); otherwise they are in
+// LDS or were written by this block.
+template <bool COHERENT>
 __device__ __forceinline__ uint32_t compact_bits(const uint32_t* bits, int rows, int nwords,
                                                  int32_t* idx, uint32_t* scratch) {
   const int tid = threadIdx.x;
@@ -749,7 +709,8 @@ __device__ __forceinline__ uint32_t compact_bits(const uint32_t* bits, int rows,
       const int word = base + tid * E + e;
       uint32_t x = 0u;
       if (word < nwords)
-        for (int r = 0; r < rows; ++r) x |= ld_dev(&bits[(size_t)r * nwords + word]);
+        for (int r = 0; r < rows; ++r)
+          x |= COHERENT ? ld_dev(&bits[(size_t)r * nwords + word]) : bits[(size_t)r * nwords + word];
       w[e] = x;
       n += (uint32_t)__popc(x);
     }
@@ -770,26 +731,60 @@ __device__ __forceinline__ uint32_t compact_bits(const uint32_t* bits, int rows,
   return carry;
 }
 
-// resolve: one block per row.  Candidates (all of digit D1, index order) are
-// copied to one contiguous list (LDS when few), the `need` largest are picked
-// (equal keys: lower index first), their bits set, and the row (or, for a batch
-// union, all rows once the last one is done) compacted to ascending indices.
-__device__ __forceinline__ void resolve_block(const TopkProblem& P, int b, float* lds) {
-  const int tid = threadIdx.x;
-  uint32_t* lh = reinterpret_cast<uint32_t*>(lds);          // [kHistBins]
-  uint32_t* scratch = lh + kHistBins;                       // [8]
-  uint32_t* bcast = scratch + 8;                            // [4]
-  int* flag = reinterpret_cast<int*>(bcast + 4);            // [4]
-  uint2* lc = reinterpret_cast<uint2*>(lh + kHistBins + 16);   // [kCandCap]
+// Candidates [t0 + tid*E, t0 + tid*E + E), E = kCandPerThread, of a row's list, which is stored per
+// segment (segment g holds segoff[g+1] - segoff[g] entries at src + g*kSegElems).
+__device__ __forceinline__ void load_cand_tile(const uint2* src, const uint32_t* segoff, int nseg,
+                                               uint32_t C, uint32_t t0,
+                                               uint32_t (&key)[kCandPerThread],
+                                               uint32_t (&ix)[kCandPerThread]) {
+  const uint32_t c0 = t0 + threadIdx.x * kCandPerThread;
+  int g = 0;
+  if (c0 < C) {
+    int lo = 0, hi = nseg - 1;   // last g with segoff[g] <= c0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (segoff[mid] <= c0) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+  }
+#pragma unroll
+  for (int e = 0; e < kCandPerThread; ++e) {
+    const uint32_t c = c0 + e;
+    key[e] = 0u;
+    ix[e] = 0xffffffffu;
+    if (c < C) {
+      while (g + 1 < nseg && segoff[g + 1] <= c) ++g;
+      const uint2 kv = ld_dev_u64(&src[(size_t)g * kSegElems + (c - segoff[g])]);
+      key[e] = kv.x;
+      ix[e] = kv.y;
+    }
+  }
+}
 
-  uint32_t* segoff = reinterpret_cast<uint32_t*>(lc + kCandCap);   // [nseg + 1]
-  const uint32_t need = (uint32_t)P.need[b];
-  const int32_t* cc = P.ccount + (size_t)b * P.nseg;
-  // segment offsets of the candidate list (index order), all segments in parallel
+// Resolve a classified row (run by the last of its classify blocks): the `need`
+// largest candidates of digit D1 (equal keys: lower index first) join the keys
+// above D1, and the row is compacted (or published for the batch union).
+__device__ __forceinline__ void resolve_row(const TopkProblem& P, int b, uint32_t D1, uint32_t need,
+                                            float* lds) {
+  const int tid = threadIdx.x;
+  uint32_t* scratch = reinterpret_cast<uint32_t*>(lds);   // [8]
+  uint32_t* bcast = scratch + 8;                          // [4]
+  int* flag = reinterpret_cast<int*>(bcast + 4);          // [4]
+  uint32_t* lh = scratch + 16;                            // [kLowBins]
+  uint32_t* lw = lh + kLowBins;                           // [kResolveWords]
+  uint32_t* segoff = lw + kResolveWords;                  // [kMaxSegs + 1]
+
+  const int nwords = P.nwords;
+  uint32_t* gbits = P.bits + (size_t)b * nwords;
+  const bool words_in_lds = nwords <= kResolveWords;
+  uint32_t* words = words_in_lds ? lw : gbits;
+  if (words_in_lds)
+    for (int w = tid; w < nwords; w += kThreads) lw[w] = ld_dev(&gbits[w]);
+  const uint32_t* cc = reinterpret_cast<const uint32_t*>(P.ccount) + (size_t)b * P.nseg;
   uint32_t C = 0u;
   for (int g0 = 0; g0 < P.nseg; g0 += kThreads) {
     const int g = g0 + tid;
-    const uint32_t n = (g < P.nseg) ? (uint32_t)cc[g] : 0u;
+    const uint32_t n = (g < P.nseg) ? ld_dev(&cc[g]) : 0u;
     uint32_t tot;
     const uint32_t inc = block_incl_scan(n, scratch, &tot);
     if (g < P.nseg) segoff[g] = C + inc - n;
@@ -797,81 +792,55 @@ __device__ __forceinline__ void resolve_block(const TopkProblem& P, int b, float
   }
   if (tid == 0) segoff[P.nseg] = C;
   __syncthreads();
-  uint32_t* bits = P.bits + (size_t)b * P.nwords;
 
   if (need > 0u && C > 0u) {
-    // contiguous candidate list, index order
-    uint2* cs = (C <= (uint32_t)kCandCap)
-                    ? lc
-                    : P.cand + (size_t)P.batch * P.nseg * kSegElems + (size_t)b * P.N;
     const uint2* src = P.cand + (size_t)b * P.nseg * kSegElems;
-    constexpr int UG = 16;   // candidates in flight per thread
-    for (uint32_t c0 = 0; c0 < C; c0 += kThreads * UG) {
-      uint2 v[UG];
-#pragma unroll
-      for (int u = 0; u < UG; ++u) {
-        const uint32_t c = c0 + u * kThreads + tid;
-        if (c < C) {
-          // segment of candidate c: the last g with segoff[g] <= c
-          int lo = 0, hi = P.nseg - 1;
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (segoff[mid] <= c) lo = mid; else hi = mid - 1;
-          }
-          v[u] = src[(size_t)lo * kSegElems + (c - segoff[lo])];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UG; ++u) {
-        const uint32_t c = c0 + u * kThreads + tid;
-        if (c < C) cs[c] = v[u];
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // radix over the low 21 bits: [20:10] then [9:0]
-    uint32_t T = cs[0].x & 0xffe00000u;    // all candidates share the top 11 bits
+    const int ntiles = (int)((C + kCandTile - 1) / kCandTile);
+    uint32_t key[kCandPerThread], ix[kCandPerThread];
+    if (ntiles == 1) load_cand_tile(src, segoff, P.nseg, C, 0u, key, ix);
+    // radix over the low 20 bits: [19:10] then [9:0]
+    uint32_t T = D1 << kTopShift;
     uint32_t remaining = need;
-    int hi = 21;
+    int hi = kTopShift;
     for (int pass = 0; pass < 2; ++pass) {
-      const int width = (pass == 0) ? 11 : 10;
-      const int shift = hi - width;
-      const int nbins = 1 << width;
+      const int shift = hi - 10;
       __syncthreads();
-      for (int i = tid; i < nbins; i += kThreads) lh[i] = 0u;
+      for (int i = tid; i < kLowBins; i += kThreads) lh[i] = 0u;
       __syncthreads();
-      for (uint32_t c = tid; c < C; c += kThreads) {
-        const uint32_t key = cs[c].x;
-        if ((key >> hi) == (T >> hi)) atomicAdd(&lh[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+      for (int t = 0; t < ntiles; ++t) {
+        if (ntiles > 1) load_cand_tile(src, segoff, P.nseg, C, (uint32_t)t * kCandTile, key, ix);
+#pragma unroll
+        for (int e = 0; e < kCandPerThread; ++e)
+          if (ix[e] != 0xffffffffu && (key[e] >> hi) == (T >> hi))
+            atomicAdd(&lh[(key[e] >> shift) & (uint32_t)(kLowBins - 1)], 1u);
       }
       __syncthreads();
+      constexpr int PT = kLowBins / kThreads;
+      uint32_t hv[PT];
+#pragma unroll
+      for (int j = 0; j < PT; ++j) hv[j] = lh[kLowBins - 1 - tid * PT - j];
       uint32_t D, above;
-      find_digit(lh, nbins, remaining, scratch, bcast, &D, &above);
+      find_digit<PT>(hv, remaining, scratch, bcast, &D, &above);
       T |= D << shift;
       remaining -= above;
       hi = shift;
     }
     const uint32_t take = remaining;
     // index-ordered pass: keep key > T and the first `take` keys equal to T
-    constexpr int E = 16;
     uint32_t carry_eq = 0u;
-    for (uint32_t base = 0; base < C; base += kThreads * E) {
-      const uint32_t c0 = base + tid * E;
+    for (int t = 0; t < ntiles; ++t) {
+      if (ntiles > 1) load_cand_tile(src, segoff, P.nseg, C, (uint32_t)t * kCandTile, key, ix);
       uint32_t n_eq = 0u;
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (c0 + e < C && cs[c0 + e].x == T) ++n_eq;
+      for (int e = 0; e < kCandPerThread; ++e) n_eq += (ix[e] != 0xffffffffu && key[e] == T) ? 1u : 0u;
       uint32_t tot;
       uint32_t eq_before = block_incl_scan(n_eq, scratch, &tot) - n_eq + carry_eq;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (c0 + e < C) {
-          const uint2 kv = cs[c0 + e];
-          bool sel = kv.x > T;
-          if (kv.x == T) { sel = eq_before < take; ++eq_before; }
-          if (sel)
-            __hip_atomic_fetch_or(&bits[kv.y >> 5], 1u << (kv.y & 31u), __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
+      for (int e = 0; e < kCandPerThread; ++e) {
+        if (ix[e] != 0xffffffffu) {
+          bool sel = key[e] > T;
+          if (key[e] == T) { sel = eq_before < take; ++eq_before; }
+          if (sel) atomicOr(&words[ix[e] >> 5], 1u << (ix[e] & 31u));
         }
       }
       carry_eq += tot;
@@ -880,23 +849,81 @@ __device__ __forceinline__ void resolve_block(const TopkProblem& P, int b, float
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (!P.unite) {
-    const uint32_t n = compact_bits(bits, 1, P.nwords, P.idx + (size_t)b * P.k, scratch);
+    const uint32_t n = words_in_lds
+        ? compact_bits<false>(words, 1, nwords, P.idx + (size_t)b * P.k, scratch)
+        : compact_bits<true>(words, 1, nwords, P.idx + (size_t)b * P.k, scratch);
     if (tid == 0) P.count[b] = (int32_t)n;
     return;
   }
+  // batch union: publish this row's words, the last row to be resolved ORs all rows
+  if (words_in_lds)
+    for (int w = tid; w < nwords; w += kThreads) st_dev_u32(&gbits[w], lw[w]);
   if (!arrive_last(P.ticket, (uint32_t)P.batch, flag)) return;
-  const uint32_t n = compact_bits(P.bits, P.batch, P.nwords, P.idx, scratch);
+  const uint32_t n = compact_bits<true>(P.bits, P.batch, nwords, P.idx, scratch);
   if (tid == 0) P.count[0] = (int32_t)n;
 }
 
-__device__ __forceinline__ void topk_task(int stage, const TopkTask& T, int blk, float* lds) {
-  if (stage == T_RESOLVE) {
-    const int per0 = T.p[0].batch;
-    int lb;
-    if (topk_problem(T, blk, per0, &lb) == 0) resolve_block(T.p[0], lb, lds);
-    else resolve_block(T.p[1], lb, lds);
-    return;
+// classify: one block per (row, segment of kSegElems scores, 8 per thread).
+__device__ __forceinline__ void classify_block(const TopkProblem& P, int lb, float* lds) {
+  const int tid = threadIdx.x;
+  const int g = lb % P.nseg, b = lb / P.nseg;
+  uint32_t* scratch = reinterpret_cast<uint32_t*>(lds);   // [8]
+  uint32_t* bcast = scratch + 8;                          // [4]
+  int* flag = reinterpret_cast<int*>(bcast + 4);          // [4]
+  const int N = P.N;
+  const int k = min(max(P.k, 0), N);
+
+  // digit D1 of the k-th key from the top, and how many keys of that digit are needed
+  int D1;
+  uint32_t need = 0u;
+  if (k == 0) {
+    D1 = kHistBins;          // nothing above, nothing equal
+  } else if (k == N) {
+    D1 = -1;                 // everything above
+  } else {
+    const uint32_t* gh = P.hist + (size_t)b * kHistBins;
+    constexpr int PT = kHistBins / kThreads;
+    uint32_t hv[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) hv[j] = gh[kHistBins - 1 - tid * PT - j];
+    uint32_t D, above;
+    find_digit<PT>(hv, (uint32_t)k, scratch, bcast, &D, &above);
+    D1 = (int)D;
+    need = (uint32_t)k - above;
   }
+
+  const float* s = P.scores + (size_t)b * P.ld;
+  const int j0 = g * kSegElems + tid * 8;
+  uint32_t keys[8];
+  uint32_t m8 = 0u, n_cand = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = j0 + e;
+    keys[e] = (j < N) ? score_key(s[j]) : 0u;
+    const int dig = (int)(keys[e] >> kTopShift);
+    if (j < N && dig > D1) m8 |= 1u << e;
+    if (j < N && dig == D1) ++n_cand;
+  }
+  uint32_t tot;
+  uint32_t pos = block_incl_scan(n_cand, scratch, &tot) - n_cand;
+  uint2* cand = P.cand + ((size_t)b * P.nseg + g) * kSegElems;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = j0 + e;
+    if (j < N && (int)(keys[e] >> kTopShift) == D1) st_dev_u64(&cand[pos++], make_uint2(keys[e], (uint32_t)j));
+  }
+  // four threads fill one 32-bit word (8 elements each)
+  uint32_t w = m8 << ((tid & 3) * 8);
+  w |= __shfl_xor(w, 1);
+  w |= __shfl_xor(w, 2);
+  const int word = j0 >> 5;
+  if ((tid & 3) == 0 && word < P.nwords) st_dev_u32(&P.bits[(size_t)b * P.nwords + word], w);
+  if (tid == 0) st_dev_u32(reinterpret_cast<uint32_t*>(&P.ccount[(size_t)b * P.nseg + g]), tot);
+  if (!arrive_last(&P.row_tickets[b], (uint32_t)P.nseg, flag)) return;
+  resolve_row(P, b, (uint32_t)D1, need, lds);
+}
+
+__device__ __forceinline__ void topk_task(int stage, const TopkTask& T, int blk, float* lds) {
   const int per0 = T.p[0].batch * T.p[0].nseg;
   int lb;
   const int pi = topk_problem(T, blk, per0, &lb);
@@ -927,9 +954,9 @@ __global__ __launch_bounds__(kThreads) void phase_kernel(PhaseArgs a) {
       return;
     }
   }
-  if constexpr ((FLAGS & (T_HIST | T_CLASSIFY | T_RESOLVE)) != 0) {
+  if constexpr ((FLAGS & (T_HIST | T_CLASSIFY)) != 0) {
     if (blk >= a.b_topk && blk < a.b_topk + a.topk.blocks) {
-      topk_task(FLAGS & (T_HIST | T_CLASSIFY | T_RESOLVE), a.topk, blk - a.b_topk, lds);
+      topk_task(FLAGS & (T_HIST | T_CLASSIFY), a.topk, blk - a.b_topk, lds);
       return;
     }
   }
@@ -974,7 +1001,6 @@ int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes,
     case T_ZERO: return launch_t<T_ZERO, 1>(a, grid, lds_bytes, stream);
     case T_HIST: return launch_t<T_HIST, 1>(a, grid, lds_bytes, stream);
     case T_CLASSIFY: return launch_t<T_CLASSIFY, 1>(a, grid, lds_bytes, stream);
-    case T_RESOLVE: return launch_t<T_RESOLVE, 1>(a, grid, lds_bytes, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }
