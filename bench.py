@@ -80,6 +80,10 @@ def main():
     ap.add_argument("--replicas", type=int, default=6)
     ap.add_argument("--cpu-layers", type=int, default=4,
                     help="decode layers the CPU oracle times (0 = skip)")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="run one plain 1 GiB device copy first (counter calibration)")
+    ap.add_argument("--lookahead-only", action="store_true",
+                    help="skip the per-launch event pass and the sparse-only pass")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -104,6 +108,16 @@ def main():
     B, R = args.batch, max(2, args.replicas)
     k_m, k_a = cfg.k_m, cfg.k_a
     cap_m, cap_a = min(cfg.F, B * k_m), min(cfg.h, B * k_a)
+
+    if args.copy_calibrate:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the counters
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy: 1073741824 bytes read, 1073741824 bytes written")
 
     log(f"generating {R} replicas of the c4 layer (batch {B}) on the GPU")
     layers, ys = [], []
@@ -166,6 +180,9 @@ def main():
     full_bytes = acc.step_bytes(**shape)
     log(f"timing {args.steps} steps (|S_M|={u_m}, |S_A|={u_a})")
     ms_step, ev_step = timed(args.steps)
+    if args.lookahead_only:
+        print(json.dumps({"us_per_layer": round(ms_step * 1e3, 2), "steps": args.steps}), flush=True)
+        return
 
     # Per-launch durations with HIP events recorded around each launch on its stream.
     dv.timing_enable(True)

@@ -1,0 +1,127 @@
+"""Summaries of rocprofv3 output for the decode-layer benchmark.
+
+    python -m contextual_sparsity_mlp_amd.profsum stats <kernel_stats.csv> <kernel_trace.csv> <out.md> "<command>"
+    python -m contextual_sparsity_mlp_amd.profsum traffic <fetch counter_collection.csv>
+        <write counter_collection.csv> <out.json> "<command>"
+
+`stats` turns a --kernel-trace --stats kernel summary into a short table, and adds
+the per-launch durations of the decode kernels from the trace (the phase kernel is
+one template per launch mix, so its launches are told apart by grid size).
+`traffic` reads two --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) of the
+benchmark with --copy-calibrate: the plain 1 GiB copy calibrates each counter
+(bytes per counted KiB), and the decode launches (phase kernels) are averaged per
+launch slot of the look-ahead step: 0 row dots, 1 attention + row sums, 2 output
+row sums + top-k.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+COPY_BYTES = 1 << 30
+# template flags of the phase kernel for each launch slot of the look-ahead step
+SLOT_FLAGS = {0: "1", 1: "6", 2: "20"}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "contextual_sparsity_mlp_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stats(src: str, trace: str, out: str, command: str):
+    rows = list(csv.DictReader(open(src)))
+    lines = ["# rocprofv3 kernel summary: OPT-175B-shaped decode layer, batch 1", "",
+             f"Command: `{command}`", "",
+             "## Per kernel (rocprofv3 --stats)", "",
+             "| kernel | calls | avg us | min us | max us | % time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        short = re.sub(r"\(.*", "", r["Name"])
+        if len(short) > 70:
+            short = short[:67] + "..."
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    groups = {}
+    for r in csv.DictReader(open(trace)):
+        m = re.search(r"phase_kernel<(\d+), (\d+)>", r["Kernel_Name"])
+        if not m:
+            continue
+        blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((m.group(1), m.group(2), blocks), []).append(dur)
+    lines += ["", "## Decode launches by configuration (from the kernel trace)", "",
+              "flags: 1 row dots, 2 attention, 4 row sums, 8 histogram, 16 top-k classify, "
+              "64 zero fill (sums of these for a mixed launch)", "",
+              "| phase_kernel<flags, batch tile> | blocks | launches | avg us | median us | min us |",
+              "|---|---|---|---|---|---|"]
+    for (fl, bt, blocks), v in sorted(groups.items(), key=lambda kv: -len(kv[1])):
+        lines.append(f"| <{fl}, {bt}> | {blocks} | {len(v)} | {statistics.mean(v):.2f} | "
+                     f"{statistics.median(v):.2f} | {min(v):.2f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def _counter_rows(path, counter):
+    rows = list(csv.DictReader(open(path)))
+    out = []
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        out.append((r["Kernel_Name"], int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0),
+                    float(r["Counter_Value"])))
+    return out
+
+
+def _per_slot(rows):
+    copy = [v for n, g, v in rows if "copyBuffer" in n]
+    slots = {}
+    for slot, flags in SLOT_FLAGS.items():
+        vals = [(g, v) for n, g, v in rows if re.search(rf"phase_kernel<{flags}, 1>", n)]
+        if not vals:
+            continue
+        # the decode launches are the most frequent grid size of that kernel
+        grids = [g for g, _ in vals]
+        common = max(set(grids), key=grids.count)
+        slots[slot] = statistics.median([v for g, v in vals if g == common])
+    return (max(copy) if copy else None), slots
+
+
+def traffic(fetch_csv: str, write_csv: str, out: str, command: str):
+    f_copy, f_slots = _per_slot(_counter_rows(fetch_csv, "FETCH_SIZE"))
+    w_copy, w_slots = _per_slot(_counter_rows(write_csv, "WRITE_SIZE"))
+    f_scale = COPY_BYTES / f_copy if f_copy else None
+    w_scale = COPY_BYTES / w_copy if w_copy else None
+    per = {}
+    for slot in sorted(set(f_slots) | set(w_slots)):
+        fb = f_slots.get(slot, 0.0) * (f_scale or 0)
+        wb = w_slots.get(slot, 0.0) * (w_scale or 0)
+        per[str(slot)] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                          "bytes": round(fb + wb)}
+    res = {"workload": "OPT-175B-shaped decode layer, batch 1, look-ahead predictor",
+           "command": command, "source_hash": source_hash(),
+           "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": f_copy, "write_kib": w_copy,
+                                "fetch_bytes_per_count": f_scale,
+                                "write_bytes_per_count": w_scale},
+           "per_launch": {k: v["bytes"] for k, v in per.items()},
+           "per_launch_detail": per}
+    json.dump(res, open(out, "w"), indent=1)
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    elif sys.argv[1] == "traffic":
+        traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    else:
+        raise SystemExit(__doc__)
