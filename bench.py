@@ -193,7 +193,8 @@ def main():
     dv.timing_enable(False)
     ph_bytes = acc.phase_bytes(**shape)
     phases = []
-    names = ["rowdot (W1, Wq, A rows)", "attn + rowsum (W2, KV, B)", "rowsum W^O + top-k"]
+    names = ["row dots (W1, W^Q, A rows)", "attention + predictor B rows",
+             "row sum W2 + W^O rows, combine, top-k"]
     for i, (ms, n) in enumerate(zip(ph_ms, ph_n)):
         avg_us = ms * 1e3 / max(n, 1)
         b = ph_bytes[i] if i < len(ph_bytes) else 0
@@ -206,6 +207,16 @@ def main():
     log("timing the sparse MLP+MHA part alone")
     ms_sparse, ev_sparse = timed(args.steps, lookahead=False)
     sel_bytes = acc.step_bytes(**shape, with_predictor=False).selected
+    dv.timing_enable(True)
+    for t in range(args.steps):
+        step(t, lookahead=False)
+    torch.cuda.synchronize()
+    sp_ms, sp_n = dv.timing_read(8)
+    dv.timing_enable(False)
+    sp_bytes = acc.phase_bytes(**shape, with_predictor=False)
+    sparse_phases = [dict(launch=i, avg_us=round(ms * 1e3 / max(n, 1), 2), bytes=sp_bytes[i],
+                          GBps=round(sp_bytes[i] / (ms * 1e-3 / max(n, 1)) / 1e9, 1))
+                     for i, (ms, n) in enumerate(zip(sp_ms, sp_n)) if i < len(sp_bytes)]
 
     src = source_hash()
     traffic = load_traffic(src)
@@ -247,7 +258,8 @@ def main():
                            "bytes": sel_bytes,
                            "GBps": round(sel_bytes / (ms_sparse * 1e-3) / 1e9, 1),
                            "frac_of_peak": round(sel_bytes / (ms_sparse * 1e-3) / 1e9 / PEAK_GBPS,
-                                                 4)},
+                                                 4),
+                           "phases": sparse_phases},
         "frac_of_peak": round(full_bytes.total / (ms_step * 1e-3) / 1e9 / PEAK_GBPS, 4),
         "phases": phases,
         "roofline": roofline,

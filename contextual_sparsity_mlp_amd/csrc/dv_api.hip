@@ -199,9 +199,9 @@ MhaWs plan_mha(int batch, int d, int dh, int n_ctx, int cap, dv_dtype wdt) {
 // Zero region first: all tickets, both score histograms, row and union tickets.
 struct LayerWs {
   size_t zero, tickets, hist_m, hist_a, rtick_m, rtick_a, uticket;
-  size_t a, q, o, part, zm, za, mlp_out, sm, sa;
-  size_t p_mlp, p_bm, p_ba, p_wo, total;
-  int t_attn, t_mlp, t_bm, t_ba, t_wo, t_total, zero_words;
+  size_t a, q, o, part, zm, za, sm, sa;
+  size_t p_bm, p_ba, p_wo, total;
+  int t_attn, t_bm, t_ba, t_wo, t_total, zero_words;
   TopkWs tm, ta;
 };
 LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int cap_m, int cap_a,
@@ -209,16 +209,14 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   LayerWs p; Ws w;
   cap_m = std::max(cap_m, 1);
   cap_a = std::max(cap_a, 1);
-  const AxGeo g_mlp = ax_geo(batch, d, d, wdt, cap_m);
   const AxGeo g_bm = ax_geo(batch, F, F, wdt, r);
   const AxGeo g_ba = ax_geo(batch, h, h, wdt, r);
-  const AxGeo g_wo = ax_geo(batch, d, d, wdt, cap_a * dh);
+  const AxGeo g_wo = ax_geo(batch, d, d, wdt, cap_a * dh + cap_m);   // W2 and W^O rows
   p.t_attn = batch * cap_a;
-  p.t_mlp = (int)ax_tickets(g_mlp);
   p.t_bm = (int)ax_tickets(g_bm);
   p.t_ba = (int)ax_tickets(g_ba);
   p.t_wo = (int)ax_tickets(g_wo);
-  p.t_total = p.t_attn + p.t_mlp + p.t_bm + p.t_ba + p.t_wo;
+  p.t_total = p.t_attn + p.t_bm + p.t_ba + p.t_wo;
   // zero region: tickets | hist_m | hist_a | union tickets (2)
   p.zero = w.off;
   p.tickets = p.zero;
@@ -235,10 +233,8 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   p.part = w.take((size_t)batch * cap_a * attn_nsplit_max(n_ctx) * (dh + 2) * 4);
   p.zm = w.take((size_t)batch * r * 4);
   p.za = w.take((size_t)batch * r * 4);
-  p.mlp_out = w.take((size_t)batch * d * 4);
   p.sm = w.take((size_t)batch * F * 4);
   p.sa = w.take((size_t)batch * h * 4);
-  p.p_mlp = w.take(ax_partial_floats(batch, d, g_mlp) * 4);
   p.p_bm = w.take(ax_partial_floats(batch, F, g_bm) * 4);
   p.p_ba = w.take(ax_partial_floats(batch, h, g_ba) * 4);
   p.p_wo = w.take(ax_partial_floats(batch, d, g_wo) * 4);
@@ -279,16 +275,20 @@ void finish_rowdot(RowdotTask& T, const float* y, int batch, int d, uint32_t* ze
 }
 int rowdot_lds(const RowdotTask& T) { return T.bt_lds * T.d * 4; }
 
-// Axpy segment; `chunk_bytes` steers how many row chunks (blocks) it gets.
-void add_axpy(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype wdt, RowList L,
-              const float* coef, int coef_ld, int relu, int ncols, float* partial, uint32_t* tickets,
-              float* out, int out_ld, const float* add0, const float* add1, int add_ld,
-              int accumulate) {
+// Axpy segment over one row source, or two sources summed into the same columns
+// (second source: W2 != nullptr; same stride and dtype, rows after the first's).
+void add_axpy2(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype wdt, RowList L,
+               const float* coef, int coef_ld, int relu, const void* W2, RowList L2,
+               const float* coef2, int coef2_ld, int relu2, int ncols, float* partial,
+               uint32_t* tickets, float* out, int out_ld, const float* add0, const float* add1,
+               int add_ld, int accumulate) {
   AxpySeg& S = T.seg[T.nseg];
-  const int cap_rows = std::max(1, L.host_count * L.expand);
+  int cap_rows = L.host_count * L.expand + (W2 ? L2.host_count * L2.expand : 0);
+  cap_rows = std::max(1, cap_rows);
   const AxGeo g = ax_geo(batch, ncols, stride, wdt, cap_rows);
   S.W = W; S.row_stride = stride; S.wdt = (wdt == DV_BF16) ? W_BF16 : W_F32;
   S.rows = L; S.coef = coef; S.coef_ld = coef_ld; S.relu = relu; S.ncols = ncols;
+  S.W2 = W2; S.rows2 = L2; S.coef2 = coef2; S.coef2_ld = coef2_ld; S.relu2 = relu2;
   S.vec = g.vec; S.nslices = g.nslices; S.nbt = g.nbt;
   // About six blocks per CU for the segment (512-byte row slices need that many
   // loads in flight to stream well); at most kMaxChunks chunk partials per slice
@@ -304,6 +304,14 @@ void add_axpy(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype 
   T.blocks += S.nbt * S.nslices * S.nchunks;
   T.nseg++;
 }
+
+void add_axpy(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype wdt, RowList L,
+              const float* coef, int coef_ld, int relu, int ncols, float* partial, uint32_t* tickets,
+              float* out, int out_ld, const float* add0, const float* add1, int add_ld,
+              int accumulate) {
+  add_axpy2(T, batch, W, stride, wdt, L, coef, coef_ld, relu, nullptr, RowList{}, nullptr, 0, 0,
+            ncols, partial, tickets, out, out_ld, add0, add1, add_ld, accumulate);
+}
 int axpy_lds(int bt) {
   return std::max((kAxpyTileRows * (1 + bt) + kAxGroups * bt * kAxSliceLanes * 8) * 4,
                   (16 + kHistBins) * 4);
@@ -315,11 +323,12 @@ void setup_attn(AttnTask& A, const float* q, int q_ld, const void* K, const void
   A.q = q; A.q_ld = q_ld; A.K = K; A.V = V; A.kvdt = (kvdt == DV_BF16) ? W_BF16 : W_F32;
   A.batch = batch; A.h = h; A.n = n; A.dh = dh; A.heads = heads; A.scale = scale;
   const int cap = heads.host_count;
-  // Enough (token, head, split) blocks to spread the cache over the chip when the
-  // launch has little else to run, splits of at least 64 keys.
+  // Splits of about 128 keys keep each block's chain of dependent loads short;
+  // with few (token, head) pairs and nothing else in the launch, more splits
+  // spread the cache over the chip.
+  (void)other_blocks;
   const int base = std::max(1, batch * cap);
-  const int want = std::max(device_cus() * 2 - other_blocks / 2, device_cus() / 2);
-  int ns = cdiv(want, base);
+  int ns = std::max(cdiv(n, 128), other_blocks > 0 ? 1 : cdiv(device_cus(), base));
   ns = std::max(1, std::min(ns, attn_nsplit_max(n)));
   A.nsplit = ns;
   A.per = cdiv(n, ns);
@@ -649,8 +658,7 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   const int cap_m = std::max(max_count_m, 1), cap_a = std::max(max_count_a, 1);
   uint32_t* tk = up(P.tickets);
   uint32_t* t_attn = tk;
-  uint32_t* t_mlp = t_attn + P.t_attn;
-  uint32_t* t_bm = t_mlp + P.t_mlp;
+  uint32_t* t_bm = t_attn + P.t_attn;
   uint32_t* t_ba = t_bm + P.t_bm;
   uint32_t* t_wo = t_ba + P.t_ba;
   const int bt = pick_bt(batch);
@@ -671,11 +679,9 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   finish_rowdot(a1.rowdot, y_in, batch, d, up(P.zero), P.zero_words);
   if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
 
-  // Phase 2: attention over the cache for S_A; ReLU(a) W2 rows; predictor scores
+  // Phase 2: attention over the cache for S_A; the next layer's predictor scores
   // (with their top-digit histograms).
   PhaseArgs a2 = zero_args();
-  add_axpy(a2.axpy, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, 1, d, fp(P.p_mlp), t_mlp,
-           fp(P.mlp_out), d, nullptr, nullptr, 0, 0);
   if (nx) {
     add_axpy(a2.axpy, batch, nx->B_M, Fn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r, 0,
              Fn, fp(P.p_bm), t_bm, fp(P.sm), Fn, nullptr, nullptr, 0, 0);
@@ -685,7 +691,7 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     a2.axpy.seg[a2.axpy.nseg - 1].hist = up(P.hist_a);
   }
   a2.axpy.batch = batch;
-  int flags2 = T_AXPY;
+  int flags2 = a2.axpy.nseg > 0 ? T_AXPY : 0;
   if (max_count_a > 0) {
     setup_attn(a2.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n, dh, LH, L->scale,
                fp(P.part), t_attn, fp(P.o), cap_a * dh, a2.axpy.blocks);
@@ -693,15 +699,21 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     a2.b_attn = 0;
     a2.b_axpy = a2.attn.blocks;
   }
-  const int lds2 = std::max(axpy_lds(bt), (flags2 & T_ATTN) ? attn_lds() : 0);
-  if (int e = launch(flags2, bt, a2, a2.attn.blocks + a2.axpy.blocks, lds2, stream, fn)) return e;
+  if (flags2 != 0) {
+    const int lds2 = std::max((flags2 & T_AXPY) ? axpy_lds(bt) : 0, (flags2 & T_ATTN) ? attn_lds() : 0);
+    const int fl = (flags2 == T_ATTN) ? T_ATTN : (flags2 == T_AXPY ? T_AXPY : (T_ATTN | T_AXPY));
+    if (int e = launch(fl, fl == T_ATTN ? 1 : bt, a2, a2.attn.blocks + a2.axpy.blocks, lds2, stream,
+                       fn))
+      return e;
+  }
 
-  // Phase 3: W^O rows scaled by the head outputs, added to y_in + MLP; beside it the
-  // next layer's top-k classifies its scores, and the last block of each row
-  // resolves that row (and, for a batch, the union).
+  // Phase 3: one row sum over the W2 rows of S_M (scaled by ReLU(a)) and the W^O rows
+  // of S_A (scaled by the head outputs), added to y_in: y_out = y_in + MLP + MHA.
+  // Beside it the next layer's top-k classifies its scores, and the last block of
+  // each row resolves that row (and, for a batch, the union).
   PhaseArgs a3 = zero_args();
-  add_axpy(a3.axpy, batch, L->Wo, d, wdt, LQ, fp(P.o), cap_a * dh, 0, d, fp(P.p_wo), t_wo, y_out, d,
-           y_in, fp(P.mlp_out), d, 0);
+  add_axpy2(a3.axpy, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, 1, L->Wo, LQ, fp(P.o), cap_a * dh, 0,
+            d, fp(P.p_wo), t_wo, y_out, d, y_in, nullptr, d, 0);
   a3.axpy.batch = batch;
   int flags3 = T_AXPY;
   TopkTask tk3;

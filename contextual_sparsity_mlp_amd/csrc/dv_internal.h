@@ -77,6 +77,13 @@ struct AxpySeg {
   const float* coef;       // coef[b * coef_ld + s*expand + e]
   int coef_ld;
   int relu;                // use max(coef, 0)
+  // Optional second row source summed into the same columns (same stride and
+  // dtype): its rows follow the first source's rows in the row order.
+  const void* W2;          // nullptr: one source
+  RowList rows2;
+  const float* coef2;
+  int coef2_ld;
+  int relu2;
   int ncols;               // output columns
   int vec;                 // elements per thread per row (8 bf16 / 4 f32 / 1 scalar)
   int nslices, nchunks, nbt;

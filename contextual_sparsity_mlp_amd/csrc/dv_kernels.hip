@@ -37,6 +37,9 @@
 
 namespace dv {
 
+// The launch descriptor travels as the kernel argument; HIP allows 4 KiB.
+static_assert(sizeof(PhaseArgs) <= 4096, "PhaseArgs exceeds the kernel-argument limit");
+
 // --------------------------------------------------------------------------- //
 // helpers                                                                      //
 // --------------------------------------------------------------------------- //
@@ -369,12 +372,13 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
   const int col0 = slice * SW + hl * VEC;
   const bool active = col0 < S.ncols;
 
-  const int nrows = list_slots(S.rows) * S.rows.expand;
+  const int nrows_a = list_slots(S.rows) * S.rows.expand;
+  const int nrows = nrows_a + (S.W2 ? list_slots(S.rows2) * S.rows2.expand : 0);
   const int per = (nrows + S.nchunks - 1) / S.nchunks;
   const int r0 = min(chunk * per, nrows);
   const int r1 = min(r0 + per, nrows);
 
-  int* lrow = reinterpret_cast<int*>(lds);               // [kAxpyTile] row or -1
+  int* lrow = reinterpret_cast<int*>(lds);               // [kAxpyTile] row (bit 30: source 2) or -1
   float* lcoef = lds + kAxpyTile;                        // [BT][kAxpyTile]
   float* red = lds + kAxpyTile * (1 + BT);               // [kAxGroups][BT][SW]
 
@@ -384,23 +388,28 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[b][v] = 0.f;
 
-  const int ex = S.rows.expand;
   for (int t0 = r0; t0 < r1; t0 += kAxpyTile) {
     const int tn = min(kAxpyTile, r1 - t0);
     __syncthreads();
     for (int i = tid; i < tn; i += kThreads) {
-      const int rr = t0 + i;
+      const bool second = t0 + i >= nrows_a;
+      const int rr = second ? t0 + i - nrows_a : t0 + i;
+      const RowList& L = second ? S.rows2 : S.rows;
+      const int ex = L.expand;
       const int slot = (ex == 1) ? rr : rr / ex;
       const int e = (ex == 1) ? 0 : rr - slot * ex;
-      const int item = S.rows.idx ? S.rows.idx[slot] : slot;
-      const bool ok = (unsigned)item < (unsigned)S.rows.items;
-      lrow[i] = ok ? item * ex + e : -1;
+      const int item = L.idx ? L.idx[slot] : slot;
+      const bool ok = (unsigned)item < (unsigned)L.items;
+      lrow[i] = ok ? ((item * ex + e) | (second ? (1 << 30) : 0)) : -1;
+      const float* cf = second ? S.coef2 : S.coef;
+      const int cld = second ? S.coef2_ld : S.coef_ld;
+      const int rl = second ? S.relu2 : S.relu;
 #pragma unroll
       for (int b = 0; b < BT; ++b) {
         float c = 0.f;
         if (ok && b < nb) {
-          c = S.coef[(size_t)(b0 + b) * S.coef_ld + rr];
-          if (S.relu) c = fmaxf(c, 0.f);
+          c = cf[(size_t)(b0 + b) * cld + rr];
+          if (rl) c = fmaxf(c, 0.f);
         }
         lcoef[b * kAxpyTile + i] = c;
       }
@@ -415,7 +424,8 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
           const int i = i0 + u * kAxGroups;
           const int row = (i < tn) ? lrow[i] : -1;
           if (row >= 0) {
-            load_cols<VEC, WT>(S.W, (long long)row * S.row_stride + col0, w[u]);
+            const void* W = (row & (1 << 30)) ? S.W2 : S.W;
+            load_cols<VEC, WT>(W, (long long)(row & ((1 << 30) - 1)) * S.row_stride + col0, w[u]);
           } else {
 #pragma unroll
             for (int v = 0; v < VEC; ++v) w[u][v] = 0.f;
@@ -632,16 +642,33 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
   if (tid < dh) st_dev(&P[2 + tid], O);
   if (tid == 0) { st_dev(&P[0], M); st_dev(&P[1], L); }
   if (!arrive_last(&T.tickets[(size_t)b * cap + slot], (uint32_t)T.nsplit, flag)) return;
+  // merge the splits: (max, sum) of every split staged in LDS with one parallel load,
+  // the p.V partials fetched in batches of independent loads, summed in split order
+  const float* P0 = T.part + ((size_t)b * cap + slot) * T.nsplit * w2;
+  if (tid < T.nsplit) {
+    gm[tid] = ld_dev(&P0[(size_t)tid * w2]);
+    gl[tid] = ld_dev(&P0[(size_t)tid * w2 + 1]);
+  }
+  __syncthreads();
+  float MM = -INFINITY;
+  for (int sp = 0; sp < T.nsplit; ++sp) MM = fmaxf(MM, gm[sp]);
   if (tid < dh) {
-    const float* P0 = T.part + ((size_t)b * cap + slot) * T.nsplit * w2;
-    float MM = -INFINITY;
-    for (int s = 0; s < T.nsplit; ++s) MM = fmaxf(MM, ld_dev(&P0[(size_t)s * w2]));
     float LL = 0.f, OO = 0.f;
-    for (int s = 0; s < T.nsplit; ++s) {
-      const float ms = ld_dev(&P0[(size_t)s * w2]);
-      const float wgt = (ms == -INFINITY) ? 0.f : expf(ms - MM);
-      LL = fmaf(wgt, ld_dev(&P0[(size_t)s * w2 + 1]), LL);
-      OO = fmaf(wgt, ld_dev(&P0[(size_t)s * w2 + 2 + tid]), OO);
+    constexpr int UB = 16;
+    for (int s0 = 0; s0 < T.nsplit; s0 += UB) {
+      float ov[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        ov[u] = ld_dev(&P0[(size_t)min(s0 + u, T.nsplit - 1) * w2 + 2 + tid]);
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        if (s0 + u < T.nsplit) {
+          const float ms = gm[s0 + u];
+          const float wgt = (ms == -INFINITY) ? 0.f : expf(ms - MM);
+          LL = fmaf(wgt, gl[s0 + u], LL);
+          OO = fmaf(wgt, ov[u], OO);
+        }
+      }
     }
     outp[tid] = OO / LL;
   }

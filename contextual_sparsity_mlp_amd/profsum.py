@@ -54,13 +54,23 @@ def stats(src: str, trace: str, out: str, command: str):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
     groups = {}
-    for r in csv.DictReader(open(trace)):
+    seq = []
+    for r in sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"])):
         m = re.search(r"phase_kernel<(\d+), (\d+)>", r["Kernel_Name"])
         if not m:
             continue
         blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         groups.setdefault((m.group(1), m.group(2), blocks), []).append(dur)
+        seq.append((m.group(1), dur))
+    # launches of the look-ahead step: a row-dot launch directly followed by the
+    # attention + row-sum launch and the row-sum + top-k launch
+    order = [SLOT_FLAGS[k] for k in sorted(SLOT_FLAGS)]
+    slot_durs = {k: [] for k in SLOT_FLAGS}
+    for i in range(len(seq) - len(order) + 1):
+        if all(seq[i + j][0] == order[j] for j in range(len(order))):
+            for j in range(len(order)):
+                slot_durs[j].append(seq[i + j][1])
     lines += ["", "## Decode launches by configuration (from the kernel trace)", "",
               "flags: 1 row dots, 2 attention, 4 row sums, 8 histogram, 16 top-k classify, "
               "64 zero fill (sums of these for a mixed launch)", "",
@@ -69,6 +79,16 @@ def stats(src: str, trace: str, out: str, command: str):
     for (fl, bt, blocks), v in sorted(groups.items(), key=lambda kv: -len(kv[1])):
         lines.append(f"| <{fl}, {bt}> | {blocks} | {len(v)} | {statistics.mean(v):.2f} | "
                      f"{statistics.median(v):.2f} | {min(v):.2f} |")
+    if slot_durs[0]:
+        names = {0: "row dots (W1, W^Q, A rows)", 1: "attention + predictor B rows",
+                 2: "row sum W2 + W^O rows, combine, top-k"}
+        lines += ["", "## Look-ahead decode step, per launch (from the kernel trace)", "",
+                  "| launch | phase_kernel<flags> | launches | avg us | median us | min us |",
+                  "|---|---|---|---|---|---|"]
+        for k in sorted(slot_durs):
+            v = slot_durs[k]
+            lines.append(f"| {k}: {names[k]} | <{SLOT_FLAGS[k]}, 1> | {len(v)} | "
+                         f"{statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} |")
     open(out, "w").write("\n".join(lines) + "\n")
 
 
