@@ -964,8 +964,7 @@ __device__ __forceinline__ void topk_task(int stage, const TopkTask& T, int blk,
 // --------------------------------------------------------------------------- //
 
 template <int FLAGS, int BT>
-__global__ __launch_bounds__(kThreads) void phase_kernel(PhaseArgs a) {
-  extern __shared__ float lds[];
+__device__ __forceinline__ void phase_body(const PhaseArgs& a, float* lds) {
   const int blk = blockIdx.x;
   if constexpr ((FLAGS & T_ZERO) != 0) {
     if (blk >= a.b_zero && blk < a.b_zero + a.zero.blocks) {
@@ -1002,10 +1001,32 @@ __global__ __launch_bounds__(kThreads) void phase_kernel(PhaseArgs a) {
   }
 }
 
+// Residency is also bounded by scalar registers: measured on MI355X with 256-thread
+// blocks of <= 64 VGPRs, a kernel of at most 80 SGPRs keeps 8 blocks per CU resident,
+// one of 84 only 7.  The launch descriptor would otherwise take about 85, so every
+// launch mix is capped at 80 except the row dots, whose vector registers hold them
+// to 3 waves per SIMD anyway (they get a kernel of their own without the cap).
+template <int FLAGS, int BT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80)))
+void phase_kernel(PhaseArgs a) {
+  extern __shared__ float lds[];
+  phase_body<FLAGS, BT>(a, lds);
+}
+
+template <int FLAGS, int BT>
+__global__ __launch_bounds__(kThreads) void rowdot_kernel(PhaseArgs a) {
+  extern __shared__ float lds[];
+  phase_body<FLAGS, BT>(a, lds);
+}
+
 template <int FLAGS, int BT>
 static int launch_t(const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
-  hipLaunchKernelGGL((phase_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
-                     static_cast<hipStream_t>(stream), a);
+  if constexpr (FLAGS == T_ROWDOT)
+    hipLaunchKernelGGL((rowdot_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
+                       static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL((phase_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
+                       static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 

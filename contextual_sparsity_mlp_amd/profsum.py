@@ -56,7 +56,7 @@ def stats(src: str, trace: str, out: str, command: str):
     groups = {}
     seq = []
     for r in sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"])):
-        m = re.search(r"phase_kernel<(\d+), (\d+)>", r["Kernel_Name"])
+        m = re.search(r"(?:phase|rowdot)_kernel<(\d+), (\d+)>", r["Kernel_Name"])
         if not m:
             continue
         blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
@@ -107,7 +107,7 @@ def _per_slot(rows):
     copy = [v for n, g, v in rows if "copyBuffer" in n]
     slots = {}
     for slot, flags in SLOT_FLAGS.items():
-        vals = [(g, v) for n, g, v in rows if re.search(rf"phase_kernel<{flags}, 1>", n)]
+        vals = [(g, v) for n, g, v in rows if re.search(rf"(?:phase|rowdot)_kernel<{flags}, 1>", n)]
         if not vals:
             continue
         # the decode launches are the most frequent grid size of that kernel

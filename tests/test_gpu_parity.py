@@ -399,3 +399,42 @@ def test_decode_layer_c4(batch):
     for got, ref_s, k, bound in r["sets"]:
         swaps += check_sets_certified(got, ref_s, k, True, bound, f"c4 B={batch} next sets")
     print(f"c4 B={batch}: certified boundary swaps {swaps}")
+
+
+def test_workspace_shared_across_calls():
+    """One workspace serves different entry points in turn (its contents left by one
+    call are never read by the next): results equal those of fresh workspaces."""
+    cfg = cfg_of("c2")
+    banner("shared workspace c2")
+    L = synth.make_layer(cfg, DEV)
+    y = synth.make_y(cfg, DEV)
+    S_M = synth.random_index_set(cfg.F, cfg.k_m, seed=5).numpy()
+    S_A = synth.random_index_set(cfg.h, cfg.k_a, seed=6).numpy()
+    idx_m, cnt_m = put_set(S_M, len(S_M))
+    idx_a, cnt_a = put_set(S_A, len(S_A))
+    shared = torch.full((max(
+        dv.workspace_bytes(dv.OP_SPARSE_MLP, batch=1, d=cfg.d, max_count_m=len(S_M)),
+        dv.workspace_bytes(dv.OP_SPARSE_MHA, batch=1, d=cfg.d, dh=cfg.dh, n_ctx=cfg.n_ctx,
+                           max_count_a=len(S_A)),
+        dv.workspace_bytes(dv.OP_PREDICT, batch=1, d=cfg.d, r=cfg.r, N=cfg.F)),), 0xA5,
+        dtype=torch.uint8, device=DEV)
+    outs = {}
+    for tag, ws_of in (("fresh", None), ("shared", shared)):
+        for rep in range(2):
+            o_m = torch.empty((1, cfg.d), dtype=torch.float32, device=DEV)
+            ws = ws_of if ws_of is not None else dv.workspace(dv.OP_SPARSE_MLP, batch=1, d=cfg.d,
+                                                              max_count_m=len(S_M))
+            dv.sparse_mlp(y, L.W1t, L.W2t, idx_m, cnt_m, len(S_M), o_m, 0, ws)
+            o_a = torch.empty((1, cfg.d), dtype=torch.float32, device=DEV)
+            ws = ws_of if ws_of is not None else dv.workspace(
+                dv.OP_SPARSE_MHA, batch=1, d=cfg.d, dh=cfg.dh, n_ctx=cfg.n_ctx,
+                max_count_a=len(S_A))
+            dv.sparse_mha(y, L.Wq, L.Wo, L.K, L.V, idx_a, cnt_a, len(S_A), cfg.scale, o_a, 0, ws,
+                          h=cfg.h, dh=cfg.dh)
+            sc = torch.empty((1, cfg.F), dtype=torch.float32, device=DEV)
+            ws = ws_of if ws_of is not None else dv.workspace(dv.OP_PREDICT, batch=1, d=cfg.d,
+                                                              r=cfg.r, N=cfg.F)
+            dv.predict(y, L.A_M, L.B_M, sc, ws)
+            outs[(tag, rep)] = (o_m, o_a, sc)
+    for a, b in zip(outs[("fresh", 0)], outs[("shared", 1)]):
+        assert torch.equal(a, b)
