@@ -60,16 +60,17 @@ def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: i
     """Bytes each launch of the look-ahead decode layer must move.
 
     launch 1 (gathered row dots): W1 rows, W^Q rows, predictor A factors, y.
-    launch 2 (attention; predictor second factors): K/V of the selected heads,
+    launch 2 (attention beside the MLP's output rows; predictor second factors):
+             W2 rows, K/V of the selected heads, y_in read, y_out written,
              predictor B factors.
-    launch 3 (one row sum over W2 and W^O rows, combine; next layer's top-k): W2
-             rows, W^O rows, y_in read, y_out written, scores read by the top-k.
+    launch 3 (W^O rows added into y_out; next layer's top-k): W^O rows, y_out read
+             and written, scores read by the top-k.
     Small intermediates handed between launches (row dots, q, head outputs,
     scores written: under 1 MB at batch 1) are not counted.
     """
     p1 = u_m * d * w_bytes + u_a * dh * d * w_bytes + batch * d * 4
-    p2 = batch * u_a * 2 * n_ctx * dh * kv_bytes
-    p3 = u_m * d * w_bytes + u_a * dh * d * w_bytes + 2 * batch * d * 4
+    p2 = u_m * d * w_bytes + batch * u_a * 2 * n_ctx * dh * kv_bytes + 2 * batch * d * 4
+    p3 = u_a * dh * d * w_bytes + 2 * batch * d * 4
     if with_predictor:
         p1 += 2 * r * d * w_bytes
         p2 += (r * F + r * h) * w_bytes

@@ -198,7 +198,7 @@ MhaWs plan_mha(int batch, int d, int dh, int n_ctx, int cap, dv_dtype wdt) {
 
 // Zero region first: all tickets, both score histograms, row and union tickets.
 struct LayerWs {
-  size_t zero, tickets, hist_m, hist_a, rtick_m, rtick_a, uticket;
+  size_t zero, tickets, hist_m, hist_a, rtick_m, rtick_a, uticket, done;
   size_t a, q, o, part, zm, za, sm, sa;
   size_t p_bm, p_ba, p_wo, total;
   int t_attn, t_bm, t_ba, t_wo, t_total, zero_words;
@@ -211,7 +211,7 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   cap_a = std::max(cap_a, 1);
   const AxGeo g_bm = ax_geo(batch, F, F, wdt, r);
   const AxGeo g_ba = ax_geo(batch, h, h, wdt, r);
-  const AxGeo g_wo = ax_geo(batch, d, d, wdt, cap_a * dh + cap_m);   // W2 and W^O rows
+  const AxGeo g_wo = ax_geo(batch, d, d, wdt, cap_m + cap_a * dh);   // W2 and W^O rows
   p.t_attn = batch * cap_a;
   p.t_bm = (int)ax_tickets(g_bm);
   p.t_ba = (int)ax_tickets(g_ba);
@@ -225,8 +225,9 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   p.rtick_m = p.hist_a + (size_t)batch * kHistBins * 4;
   p.rtick_a = p.rtick_m + (size_t)batch * 4;
   p.uticket = p.rtick_a + (size_t)batch * 4;
-  w.off = align256(p.uticket + 8);
-  p.zero_words = (int)((p.uticket + 8 - p.zero) / 4);
+  p.done = p.uticket + 8;                 // attention blocks done (single-launch path)
+  w.off = align256(p.done + 4);
+  p.zero_words = (int)((p.done + 4 - p.zero) / 4);
   p.a = w.take((size_t)batch * cap_m * 4);
   p.q = w.take((size_t)batch * cap_a * dh * 4);
   p.o = w.take((size_t)batch * cap_a * dh * 4);
@@ -281,7 +282,7 @@ void add_axpy2(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype
                const float* coef, int coef_ld, int relu, const void* W2, RowList L2,
                const float* coef2, int coef2_ld, int relu2, int ncols, float* partial,
                uint32_t* tickets, float* out, int out_ld, const float* add0, const float* add1,
-               int add_ld, int accumulate) {
+               int add_ld, int accumulate, int target_blocks) {
   AxpySeg& S = T.seg[T.nseg];
   int cap_rows = L.host_count * L.expand + (W2 ? L2.host_count * L2.expand : 0);
   cap_rows = std::max(1, cap_rows);
@@ -290,11 +291,11 @@ void add_axpy2(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype
   S.rows = L; S.coef = coef; S.coef_ld = coef_ld; S.relu = relu; S.ncols = ncols;
   S.W2 = W2; S.rows2 = L2; S.coef2 = coef2; S.coef2_ld = coef2_ld; S.relu2 = relu2;
   S.vec = g.vec; S.nslices = g.nslices; S.nbt = g.nbt;
-  // About six blocks per CU for the segment (512-byte row slices need that many
-  // loads in flight to stream well); at most kMaxChunks chunk partials per slice
-  // (a short, fixed-order final sum) and at least one row per row group.
+  // About target_blocks blocks for the segment (512-byte row slices need many loads
+  // in flight to stream well); at most kMaxChunks chunk partials per slice (a short,
+  // fixed-order final sum) and at least one row per row group.
   const int per_chunk = g.nslices * g.nbt;
-  int chunks = cdiv(device_cus() * 6, per_chunk);
+  int chunks = std::max(1, target_blocks / per_chunk);
   chunks = std::min(chunks, std::max(1, cap_rows / kAxGroups));
   S.nchunks = std::max(1, std::min(chunks, g.chunks_max));
   S.block0 = T.blocks;
@@ -308,10 +309,18 @@ void add_axpy2(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype
 void add_axpy(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype wdt, RowList L,
               const float* coef, int coef_ld, int relu, int ncols, float* partial, uint32_t* tickets,
               float* out, int out_ld, const float* add0, const float* add1, int add_ld,
-              int accumulate) {
+              int accumulate, int target_blocks) {
   add_axpy2(T, batch, W, stride, wdt, L, coef, coef_ld, relu, nullptr, RowList{}, nullptr, 0, 0,
-            ncols, partial, tickets, out, out_ld, add0, add1, add_ld, accumulate);
+            ncols, partial, tickets, out, out_ld, add0, add1, add_ld, accumulate, target_blocks);
 }
+
+// Blocks that are resident at once for the light launch mixes: measured 8 per CU
+// for 256-thread blocks of <= 64 VGPRs, <= 80 SGPRs and <= 20 KB of LDS.
+int resident_blocks() { return 8 * device_cus(); }
+
+// Row-sum grid of a launch that runs the segment alone: six blocks per CU.
+int default_axpy_blocks() { return 6 * device_cus(); }
+
 int axpy_lds(int bt) {
   return std::max((kAxpyTileRows * (1 + bt) + kAxGroups * bt * kAxSliceLanes * 8) * 4,
                   (16 + kHistBins) * 4);
@@ -326,7 +335,6 @@ void setup_attn(AttnTask& A, const float* q, int q_ld, const void* K, const void
   // Splits of about 128 keys keep each block's chain of dependent loads short;
   // with few (token, head) pairs and nothing else in the launch, more splits
   // spread the cache over the chip.
-  (void)other_blocks;
   const int base = std::max(1, batch * cap);
   int ns = std::max(cdiv(n, 128), other_blocks > 0 ? 1 : cdiv(device_cus(), base));
   ns = std::max(1, std::min(ns, attn_nsplit_max(n)));
@@ -344,7 +352,7 @@ int classify_lds() { return (16 + kLowBins + kResolveWords + kMaxSegs + 1) * 4; 
 TopkProblem make_topk(const float* scores, int ld, int N, int k, int batch, int unite,
                       int32_t* idx, int32_t* count, uint32_t* hist, uint32_t* row_tickets,
                       uint32_t* ticket, char* ws, const TopkWs& t) {
-  TopkProblem P;
+  TopkProblem P{};
   P.scores = scores; P.ld = ld; P.N = N; P.k = k; P.batch = batch;
   P.unite = (unite && batch > 1) ? 1 : 0;
   P.idx = idx; P.count = count; P.hist = hist; P.row_tickets = row_tickets; P.ticket = ticket;
@@ -484,7 +492,7 @@ int dv_predict(const float* y, int batch, int d, const void* A, const void* Bm, 
 
   PhaseArgs a2 = zero_args();
   add_axpy(a2.axpy, batch, Bm, N, wdt, make_list(nullptr, nullptr, r, 1, r), z, r, 0, N,
-           reinterpret_cast<float*>(w + P.partial), tickets, scores, N, nullptr, nullptr, 0, 0);
+           reinterpret_cast<float*>(w + P.partial), tickets, scores, N, nullptr, nullptr, 0, 0, default_axpy_blocks());
   a2.axpy.batch = batch;
   return launch(T_AXPY, bt, a2, a2.axpy.blocks, axpy_lds(bt), stream, fn);
 }
@@ -551,7 +559,7 @@ int dv_sparse_mlp(const float* y, int batch, int d, const void* W1t, const void*
 
   PhaseArgs a2 = zero_args();
   add_axpy(a2.axpy, batch, W2t, d, wdt, L, act, cap, 1, d, reinterpret_cast<float*>(w + P.partial),
-           tickets, out, d, nullptr, nullptr, 0, accumulate);
+           tickets, out, d, nullptr, nullptr, 0, accumulate, default_axpy_blocks());
   a2.axpy.batch = batch;
   return launch(T_AXPY, bt, a2, a2.axpy.blocks, axpy_lds(bt), stream, fn);
 }
@@ -581,6 +589,7 @@ int dv_sparse_mha(const float* y, int batch, int d, int h, int dh, const void* W
   const int cap = std::max(max_count, 1);
   float* q = reinterpret_cast<float*>(w + P.q);
   float* o = reinterpret_cast<float*>(w + P.o);
+  float* part = reinterpret_cast<float*>(w + P.part);
   uint32_t* t_attn = reinterpret_cast<uint32_t*>(w + P.tickets);
   uint32_t* t_ax = t_attn + P.nt_attn;
   const int bt = pick_bt(batch);
@@ -593,15 +602,14 @@ int dv_sparse_mha(const float* y, int batch, int d, int h, int dh, const void* W
 
   PhaseArgs a2 = zero_args();
   setup_attn(a2.attn, q, cap * dh, K, V, kvdt, batch, h, n_ctx, dh,
-             make_list(heads, count, max_count, 1, h), scale, reinterpret_cast<float*>(w + P.part),
-             t_attn, o, cap * dh, 0);
+             make_list(heads, count, max_count, 1, h), scale, part, t_attn, o, cap * dh, 0);
   if (max_count > 0) {
     if (int e = launch(T_ATTN, 1, a2, a2.attn.blocks, attn_lds(), stream, fn)) return e;
   }
 
   PhaseArgs a3 = zero_args();
   add_axpy(a3.axpy, batch, Wo, d, wdt, L, o, cap * dh, 0, d, reinterpret_cast<float*>(w + P.partial),
-           t_ax, out, d, nullptr, nullptr, 0, accumulate);
+           t_ax, out, d, nullptr, nullptr, 0, accumulate, default_axpy_blocks());
   a3.axpy.batch = batch;
   return launch(T_AXPY, bt, a3, a3.axpy.blocks, axpy_lds(bt), stream, fn);
 }
@@ -656,8 +664,7 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   auto fp = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
   auto up = [&](size_t off) { return reinterpret_cast<uint32_t*>(w + off); };
   const int cap_m = std::max(max_count_m, 1), cap_a = std::max(max_count_a, 1);
-  uint32_t* tk = up(P.tickets);
-  uint32_t* t_attn = tk;
+  uint32_t* t_attn = up(P.tickets);
   uint32_t* t_bm = t_attn + P.t_attn;
   uint32_t* t_ba = t_bm + P.t_bm;
   uint32_t* t_wo = t_ba + P.t_ba;
@@ -679,60 +686,82 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   finish_rowdot(a1.rowdot, y_in, batch, d, up(P.zero), P.zero_words);
   if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
 
-  // Phase 2: attention over the cache for S_A; the next layer's predictor scores
-  // (with their top-digit histograms).
+  // After the row dots, the rest of the layer: attention over the cache for S_A; one
+  // row sum y_out = y_in + sum_{S_M} ReLU(a) W2 rows + sum_{S_A} o W^O rows; and for
+  // the next layer its predictor scores (with top-digit histograms) and top-k.
+  const long long wb = (wdt == DV_BF16) ? 2 : 4;
+  auto add_out = [&](AxpyTask& T, int target, const float* coef2, int nsplit) {
+    add_axpy2(T, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, 1, L->Wo, LQ, coef2, cap_a * dh, 0,
+              d, fp(P.p_wo), t_wo, y_out, d, y_in, nullptr, d, 0, target);
+    T.seg[T.nseg - 1].coef2_nsplit = nsplit;
+  };
+
+  // Without a next layer, one launch when its blocks fit one resident round: every
+  // row-sum block streams its W2 rows, then waits for the attention blocks (which come
+  // first in block order) and combines their split pieces into the head outputs as it
+  // stages the coefficients of its W^O rows.  The attention hides under the W2 stream.
+  if (!nx && max_count_a > 0) {
+    PhaseArgs f = zero_args();
+    setup_attn(f.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n, dh, LH, L->scale,
+               fp(P.part), nullptr, nullptr, 0, 1);
+    f.attn.done_ctr = up(P.done);
+    f.b_attn = 0;
+    f.b_axpy = f.attn.blocks;
+    add_out(f.axpy, std::max(1, resident_blocks() - f.attn.blocks), fp(P.part), f.attn.nsplit);
+    AxpySeg& S = f.axpy.seg[0];
+    S.wait_ctr = up(P.done);
+    S.wait_target = (uint32_t)f.attn.blocks;
+    f.axpy.batch = batch;
+    const int grid = f.attn.blocks + f.axpy.blocks;
+    const int lds = std::max(axpy_lds(bt), attn_lds());
+    const int fit = std::min(resident_blocks(),
+                             phase_occupancy(T_ATTN | T_AXPY | T_WAIT, bt, lds) * device_cus());
+    if (grid <= fit) return launch(T_ATTN | T_AXPY | T_WAIT, bt, f, grid, lds, stream, fn);
+  }
+
+  // Otherwise two launches: the attention (its last split of each head combines the
+  // pieces into o) beside the next layer's predictor scores; then the row sum beside
+  // the next layer's top-k, whose last classify block of each row resolves it.
   PhaseArgs a2 = zero_args();
+  if (max_count_a > 0)
+    setup_attn(a2.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n, dh, LH, L->scale,
+               fp(P.part), t_attn, fp(P.o), cap_a * dh, nx ? 1 : 0);
+  a2.b_attn = 0;
+  a2.b_axpy = a2.attn.blocks;
   if (nx) {
-    add_axpy(a2.axpy, batch, nx->B_M, Fn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r, 0,
-             Fn, fp(P.p_bm), t_bm, fp(P.sm), Fn, nullptr, nullptr, 0, 0);
+    add_axpy(a2.axpy, batch, nx->B_M, Fn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r,
+             0, Fn, fp(P.p_bm), t_bm, fp(P.sm), Fn, nullptr, nullptr, 0, 0, default_axpy_blocks());
     a2.axpy.seg[a2.axpy.nseg - 1].hist = up(P.hist_m);
-    add_axpy(a2.axpy, batch, nx->B_A, hn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r, 0,
-             hn, fp(P.p_ba), t_ba, fp(P.sa), hn, nullptr, nullptr, 0, 0);
+    add_axpy(a2.axpy, batch, nx->B_A, hn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r,
+             0, hn, fp(P.p_ba), t_ba, fp(P.sa), hn, nullptr, nullptr, 0, 0, default_axpy_blocks());
     a2.axpy.seg[a2.axpy.nseg - 1].hist = up(P.hist_a);
   }
   a2.axpy.batch = batch;
-  int flags2 = a2.axpy.nseg > 0 ? T_AXPY : 0;
-  if (max_count_a > 0) {
-    setup_attn(a2.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n, dh, LH, L->scale,
-               fp(P.part), t_attn, fp(P.o), cap_a * dh, a2.axpy.blocks);
-    flags2 |= T_ATTN;
-    a2.b_attn = 0;
-    a2.b_axpy = a2.attn.blocks;
-  }
-  if (flags2 != 0) {
-    const int lds2 = std::max((flags2 & T_AXPY) ? axpy_lds(bt) : 0, (flags2 & T_ATTN) ? attn_lds() : 0);
-    const int fl = (flags2 == T_ATTN) ? T_ATTN : (flags2 == T_AXPY ? T_AXPY : (T_ATTN | T_AXPY));
-    if (int e = launch(fl, fl == T_ATTN ? 1 : bt, a2, a2.attn.blocks + a2.axpy.blocks, lds2, stream,
-                       fn))
+  const int flags2 = (a2.attn.blocks ? T_ATTN : 0) | (a2.axpy.nseg ? T_AXPY : 0);
+  if (flags2) {
+    const int lds2 = std::max((flags2 & T_AXPY) ? axpy_lds(bt) : 0, a2.attn.blocks ? attn_lds() : 0);
+    if (int e = launch(flags2, flags2 == T_ATTN ? 1 : bt, a2, a2.attn.blocks + a2.axpy.blocks, lds2,
+                       stream, fn))
       return e;
   }
-
-  // Phase 3: one row sum over the W2 rows of S_M (scaled by ReLU(a)) and the W^O rows
-  // of S_A (scaled by the head outputs), added to y_in: y_out = y_in + MLP + MHA.
-  // Beside it the next layer's top-k classifies its scores, and the last block of
-  // each row resolves that row (and, for a batch, the union).
   PhaseArgs a3 = zero_args();
-  add_axpy2(a3.axpy, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, 1, L->Wo, LQ, fp(P.o), cap_a * dh, 0,
-            d, fp(P.p_wo), t_wo, y_out, d, y_in, nullptr, d, 0);
+  add_out(a3.axpy, default_axpy_blocks(), fp(P.o), 0);
   a3.axpy.batch = batch;
   int flags3 = T_AXPY;
-  TopkTask tk3;
-  memset(&tk3, 0, sizeof tk3);
   if (nx) {
-    tk3.np = 2;
-    tk3.p[0] = make_topk(fp(P.sm), Fn, Fn, km, batch, 1, next_idx_m, next_count_m, up(P.hist_m),
-                         up(P.rtick_m), up(P.uticket), w, P.tm);
-    tk3.p[1] = make_topk(fp(P.sa), hn, hn, ka, batch, 1, next_idx_a, next_count_a, up(P.hist_a),
-                         up(P.rtick_a), up(P.uticket) + 1, w, P.ta);
-    tk3.blocks = topk_seg_blocks(tk3);
-    a3.topk = tk3;
+    TopkTask& tk = a3.topk;
+    tk.np = 2;
+    tk.p[0] = make_topk(fp(P.sm), Fn, Fn, km, batch, 1, next_idx_m, next_count_m, up(P.hist_m),
+                        up(P.rtick_m), up(P.uticket), w, P.tm);
+    tk.p[1] = make_topk(fp(P.sa), hn, hn, ka, batch, 1, next_idx_a, next_count_a, up(P.hist_a),
+                        up(P.rtick_a), up(P.uticket) + 1, w, P.ta);
+    tk.blocks = topk_seg_blocks(tk);
     flags3 |= T_CLASSIFY;
     a3.b_topk = 0;
-    a3.b_axpy = tk3.blocks;
+    a3.b_axpy = tk.blocks;
   }
-  const int lds3 = std::max(axpy_lds(bt), (flags3 & T_CLASSIFY) ? classify_lds() : 0);
+  const int lds3 = std::max(axpy_lds(bt), nx ? classify_lds() : 0);
   if (int e = launch(flags3, bt, a3, a3.topk.blocks + a3.axpy.blocks, lds3, stream, fn)) return e;
-
   return DV_OK;
 }
 

@@ -84,6 +84,9 @@ struct AxpySeg {
   const float* coef2;
   int coef2_ld;
   int relu2;
+  int coef2_nsplit;        // > 0: coef2 holds attention pieces [batch][rows2.host_count]
+                           //   [coef2_nsplit][rows2.expand + 2] that are combined per
+                           //   row (rows2.expand = dh); 0: plain coefficients
   int ncols;               // output columns
   int vec;                 // elements per thread per row (8 bf16 / 4 f32 / 1 scalar)
   int nslices, nchunks, nbt;
@@ -97,6 +100,10 @@ struct AxpySeg {
   const float* add1;
   int add_ld;
   int accumulate;          // add the previous value of out
+  // Hand-off inside one launch (all blocks resident): before its second-source rows a
+  // block waits until *wait_ctr >= wait_target; coef2 is then read coherently.
+  const uint32_t* wait_ctr;
+  uint32_t wait_target;
 };
 
 struct AxpyTask {
@@ -116,11 +123,14 @@ struct AttnTask {
   RowList heads;           // expand = 1, items = h
   float scale;
   int nsplit, per;         // key splits per (token, slot), keys per split
-  float* part;             // [batch][cap][nsplit][dh + 2]: m, l, o[dh]
-  uint32_t* tickets;       // [batch][cap], zero on entry
-  float* o;                // o[b * o_ld + s*dh + c]
+  float* part;             // [batch][cap][nsplit][dh + 2]: m, l, o[dh] of each split
+                           //   (stored coherently)
+  uint32_t* tickets;       // [batch][cap], zero on entry: the last split combines the
+                           //   pieces into o; nullptr: the consumer combines them
+  float* o;                // o[b * o_ld + s*dh + c] (with tickets), stored coherently
   int o_ld;
   int blocks;              // batch * cap * nsplit
+  uint32_t* done_ctr;      // optional: +1 per finished block, after its stores
 };
 
 // Exact top-k of score rows, in two steps that each spread over many blocks:
@@ -161,7 +171,10 @@ struct ZeroTask {
   int blocks;
 };
 
-enum : int { T_ROWDOT = 1, T_ATTN = 2, T_AXPY = 4, T_HIST = 8, T_CLASSIFY = 16, T_ZERO = 64 };
+// T_WAIT: the row sums of the launch may wait for in-launch producers before their
+// second source (see AxpySeg::wait_ctr) and combine attention pieces while staging.
+enum : int { T_ROWDOT = 1, T_ATTN = 2, T_AXPY = 4, T_HIST = 8, T_CLASSIFY = 16, T_WAIT = 32,
+             T_ZERO = 64 };
 
 struct PhaseArgs {
   RowdotTask rowdot;
@@ -174,5 +187,8 @@ struct PhaseArgs {
 
 // Host-side launcher implemented in dv_kernels.hip.  Returns a hipError_t as int.
 int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream);
+// Blocks per CU of the kernel behind (flags, bt) that the runtime keeps resident with
+// lds_bytes of dynamic LDS (0 for mixes it does not cover or on error).
+int phase_occupancy(int flags, int bt, int lds_bytes);
 
 }  // namespace dv

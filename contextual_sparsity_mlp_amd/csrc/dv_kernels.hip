@@ -30,6 +30,7 @@
 // a later launch reads use plain stores (a launch boundary orders them).  There are
 // no floating-point atomics; only integer tickets and histograms.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <math.h>
 #include <stdint.h>
 
@@ -39,6 +40,10 @@ namespace dv {
 
 // The launch descriptor travels as the kernel argument; HIP allows 4 KiB.
 static_assert(sizeof(PhaseArgs) <= 4096, "PhaseArgs exceeds the kernel-argument limit");
+// A row sum combining attention pieces keeps (weight, l) pairs of up to 9 head slots x
+// kMaxSplit splits per token where its row groups are later reduced (the LDS of a row
+// sum reserves kAxGroups * kAxSliceLanes * 8 floats per token there).
+static_assert(9 * kMaxSplit * 2 <= kAxGroups * kAxSliceLanes * 8, "attention-piece staging");
 
 // --------------------------------------------------------------------------- //
 // helpers                                                                      //
@@ -125,6 +130,30 @@ __device__ __forceinline__ bool arrive_last(uint32_t* ticket, uint32_t expected,
   }
   __syncthreads();
   return *flag != 0;
+}
+
+// Waits until *ctr >= target, where other blocks of the same launch raise *ctr.
+// Launches that wait are sized so all their blocks are resident at once and the
+// raising blocks come first in block order; the wait is still bounded (about a
+// quarter of a second), so it ends even if that ever failed to hold.
+constexpr uint32_t kWaitSpins = 1u << 20;
+__device__ __forceinline__ void wait_count(const uint32_t* ctr, uint32_t target) {
+  if (threadIdx.x == 0) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
+           spins < kWaitSpins) {
+      __builtin_amdgcn_s_sleep(8);
+      ++spins;
+    }
+  }
+  __syncthreads();
+}
+
+// Raises *ctr by one once every thread's stores of this block are complete.
+__device__ __forceinline__ void signal_done(uint32_t* ctr) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Order-preserving map of a float to uint32 (larger float -> larger key);
@@ -356,7 +385,7 @@ __device__ __forceinline__ void hist_flush_one(float score, bool active, uint32_
 }
 
 // One block: a slice of kAxSliceLanes*VEC output columns and a chunk of the row list.
-template <int BT, int VEC, int WT>
+template <int BT, int VEC, int WT, bool WAIT>
 __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, float* lds) {
   constexpr int U = 4;
   constexpr int SW = kAxSliceLanes * VEC;    // columns per slice
@@ -372,13 +401,7 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
   const int col0 = slice * SW + hl * VEC;
   const bool active = col0 < S.ncols;
 
-  const int nrows_a = list_slots(S.rows) * S.rows.expand;
-  const int nrows = nrows_a + (S.W2 ? list_slots(S.rows2) * S.rows2.expand : 0);
-  const int per = (nrows + S.nchunks - 1) / S.nchunks;
-  const int r0 = min(chunk * per, nrows);
-  const int r1 = min(r0 + per, nrows);
-
-  int* lrow = reinterpret_cast<int*>(lds);               // [kAxpyTile] row (bit 30: source 2) or -1
+  int* lrow = reinterpret_cast<int*>(lds);               // [kAxpyTile] row or -1 (see below)
   float* lcoef = lds + kAxpyTile;                        // [BT][kAxpyTile]
   float* red = lds + kAxpyTile * (1 + BT);               // [kAxGroups][BT][SW]
 
@@ -388,58 +411,199 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[b][v] = 0.f;
 
-  for (int t0 = r0; t0 < r1; t0 += kAxpyTile) {
-    const int tn = min(kAxpyTile, r1 - t0);
-    __syncthreads();
-    for (int i = tid; i < tn; i += kThreads) {
-      const bool second = t0 + i >= nrows_a;
-      const int rr = second ? t0 + i - nrows_a : t0 + i;
-      const RowList& L = second ? S.rows2 : S.rows;
-      const int ex = L.expand;
-      const int slot = (ex == 1) ? rr : rr / ex;
-      const int e = (ex == 1) ? 0 : rr - slot * ex;
-      const int item = L.idx ? L.idx[slot] : slot;
-      const bool ok = (unsigned)item < (unsigned)L.items;
-      lrow[i] = ok ? ((item * ex + e) | (second ? (1 << 30) : 0)) : -1;
-      const float* cf = second ? S.coef2 : S.coef;
-      const int cld = second ? S.coef2_ld : S.coef_ld;
-      const int rl = second ? S.relu2 : S.relu;
-#pragma unroll
-      for (int b = 0; b < BT; ++b) {
-        float c = 0.f;
-        if (ok && b < nb) {
-          c = cf[(size_t)(b0 + b) * cld + rr];
-          if (rl) c = fmaxf(c, 0.f);
+  if constexpr (!WAIT) {
+    // The rows of both sources form one list, the first source's rows first; chunk
+    // c takes a contiguous share of it.  lrow marks second-source rows with bit 30.
+    const int nrows_a = list_slots(S.rows) * S.rows.expand;
+    const int nrows = nrows_a + (S.W2 ? list_slots(S.rows2) * S.rows2.expand : 0);
+    const int per = (nrows + S.nchunks - 1) / S.nchunks;
+    const int r0 = min(chunk * per, nrows);
+    const int r1 = min(r0 + per, nrows);
+
+    for (int t0 = r0; t0 < r1; t0 += kAxpyTile) {
+      const int tn = min(kAxpyTile, r1 - t0);
+      __syncthreads();
+      for (int i = tid; i < tn; i += kThreads) {
+        const bool second = t0 + i >= nrows_a;
+        const int rr = second ? t0 + i - nrows_a : t0 + i;
+        const RowList& L = second ? S.rows2 : S.rows;
+        const int ex = L.expand;
+        const int slot = (ex == 1) ? rr : rr / ex;
+        const int e = (ex == 1) ? 0 : rr - slot * ex;
+        const int item = L.idx ? L.idx[slot] : slot;
+        const bool ok = (unsigned)item < (unsigned)L.items;
+        lrow[i] = ok ? ((item * ex + e) | (second ? (1 << 30) : 0)) : -1;
+        const float* cf = second ? S.coef2 : S.coef;
+        const int cld = second ? S.coef2_ld : S.coef_ld;
+        const int rl = second ? S.relu2 : S.relu;
+  #pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          float c = 0.f;
+          if (ok && b < nb) {
+            c = cf[(size_t)(b0 + b) * cld + rr];
+            if (rl) c = fmaxf(c, 0.f);
+          }
+          lcoef[b * kAxpyTile + i] = c;
         }
-        lcoef[b * kAxpyTile + i] = c;
+      }
+      __syncthreads();
+      if (active) {
+        for (int i0 = grp; i0 < tn; i0 += kAxGroups * U) {
+          float w[U][VEC];
+          float c[U][BT];
+  #pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kAxGroups;
+            const int row = (i < tn) ? lrow[i] : -1;
+            if (row >= 0) {
+              const void* W = (row & (1 << 30)) ? S.W2 : S.W;
+              load_cols<VEC, WT>(W, (long long)(row & ((1 << 30) - 1)) * S.row_stride + col0, w[u]);
+            } else {
+  #pragma unroll
+              for (int v = 0; v < VEC; ++v) w[u][v] = 0.f;
+            }
+  #pragma unroll
+            for (int b = 0; b < BT; ++b) c[u][b] = (i < tn) ? lcoef[b * kAxpyTile + i] : 0.f;
+          }
+  #pragma unroll
+          for (int u = 0; u < U; ++u)
+  #pragma unroll
+            for (int b = 0; b < BT; ++b)
+  #pragma unroll
+              for (int v = 0; v < VEC; ++v) acc[b][v] = fmaf(c[u][b], w[u][v], acc[b][v]);
+        }
       }
     }
-    __syncthreads();
-    if (active) {
-      for (int i0 = grp; i0 < tn; i0 += kAxGroups * U) {
-        float w[U][VEC];
-        float c[U][BT];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int i = i0 + u * kAxGroups;
-          const int row = (i < tn) ? lrow[i] : -1;
-          if (row >= 0) {
-            const void* W = (row & (1 << 30)) ? S.W2 : S.W;
-            load_cols<VEC, WT>(W, (long long)(row & ((1 << 30) - 1)) * S.row_stride + col0, w[u]);
-          } else {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) w[u][v] = 0.f;
+  } else {
+    // Chunk c takes its share of the first source's rows, then its share of the
+    // second's; a block may wait between the two for coefficients of the second source
+    // produced in the same launch.
+    const int n1 = list_slots(S.rows) * S.rows.expand;
+    const int n2 = S.W2 ? list_slots(S.rows2) * S.rows2.expand : 0;
+
+    // one source's share of rows: coefficients staged in LDS a tile at a time, then the
+    // row slices streamed by the row groups
+    auto rows_of = [&](auto merge, const RowList& L, const void* W, const float* cf, int cld,
+                       int rl, bool coherent, int nsplit, int nr) {
+      constexpr bool kMerge = decltype(merge)::value;
+      const int per = (nr + S.nchunks - 1) / S.nchunks;
+      const int r0 = min(chunk * per, nr);
+      const int r1 = min(r0 + per, nr);
+      const int ex = L.expand;
+      // with attention pieces a tile spans at most 9 head slots (ex = dh >= 32)
+      const int tile = kMerge ? min(kAxpyTile, 8 * ex) : kAxpyTile;
+      for (int t0 = r0; t0 < r1; t0 += tile) {
+        const int tn = min(tile, r1 - t0);
+        __syncthreads();
+        int s_lo = 0, ns_t = 0;
+        if constexpr (kMerge) {
+          // Combine the key splits of the tile's head slots (Eq. (2)'s softmax over all
+          // keys): every split's (max, sum) loaded in one parallel pass, then per
+          // (token, slot) the weights exp(m_sp - max) and the denominator sum w l, in
+          // split order; wl[] holds (weight, l) pairs, the denominator replaces split
+          // 0's l.
+          s_lo = t0 / ex;
+          ns_t = (t0 + tn - 1) / ex - s_lo + 1;
+          float2* wl = reinterpret_cast<float2*>(red);     // [BT][ns_t][nsplit]
+          const int w2 = ex + 2;
+          for (int q = tid; q < BT * ns_t * nsplit; q += kThreads) {
+            const int sp = q % nsplit, j = (q / nsplit) % ns_t, b = q / (nsplit * ns_t);
+            float2 v = make_float2(-INFINITY, 0.f);
+            if (b < nb) {
+              const float* P = cf + (((size_t)(b0 + b) * L.host_count + s_lo + j) * nsplit + sp) * w2;
+              v = make_float2(ld_dev(P), ld_dev(P + 1));
+            }
+            wl[q] = v;
           }
-#pragma unroll
-          for (int b = 0; b < BT; ++b) c[u][b] = (i < tn) ? lcoef[b * kAxpyTile + i] : 0.f;
+          __syncthreads();
+          for (int q = tid; q < BT * ns_t; q += kThreads) {
+            float2* W = wl + (size_t)q * nsplit;
+            float MM = -INFINITY;
+            for (int sp = 0; sp < nsplit; ++sp) MM = fmaxf(MM, W[sp].x);
+            float LL = 0.f;
+            for (int sp = 0; sp < nsplit; ++sp) {
+              const float wgt = (W[sp].x == -INFINITY) ? 0.f : expf(W[sp].x - MM);
+              LL = fmaf(wgt, W[sp].y, LL);
+              W[sp].x = wgt;
+            }
+            W[0].y = LL;
+          }
+          __syncthreads();
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int b = 0; b < BT; ++b)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[b][v] = fmaf(c[u][b], w[u][v], acc[b][v]);
+        for (int i = tid; i < tn; i += kThreads) {
+          const int rr = t0 + i;
+          const int slot = (ex == 1) ? rr : rr / ex;
+          const int e = (ex == 1) ? 0 : rr - slot * ex;
+          const int item = L.idx ? L.idx[slot] : slot;
+          const bool ok = (unsigned)item < (unsigned)L.items;
+          lrow[i] = ok ? item * ex + e : -1;
+  #pragma unroll
+          for (int b = 0; b < BT; ++b) {
+            float c = 0.f;
+            if (ok && b < nb) {
+              if constexpr (kMerge) {
+                // head output (slot, e): sum over splits of weight * p.V, over the
+                // denominator; the p.V pieces fetched in batches of independent loads
+                const float2* W = reinterpret_cast<const float2*>(red) +
+                                  ((size_t)b * ns_t + (slot - s_lo)) * nsplit;
+                const float* P = cf + ((size_t)(b0 + b) * L.host_count + slot) * nsplit * (ex + 2) + 2 + e;
+                constexpr int UB = 16;
+                float OO = 0.f;
+                for (int s0 = 0; s0 < nsplit; s0 += UB) {
+                  float ov[UB];
+  #pragma unroll
+                  for (int u = 0; u < UB; ++u) ov[u] = ld_dev(&P[(size_t)min(s0 + u, nsplit - 1) * (ex + 2)]);
+  #pragma unroll
+                  for (int u = 0; u < UB; ++u)
+                    if (s0 + u < nsplit) OO = fmaf(W[s0 + u].x, ov[u], OO);
+                }
+                c = OO / W[0].y;
+              } else {
+                const float* cp = &cf[(size_t)(b0 + b) * cld + rr];
+                c = coherent ? ld_dev(cp) : *cp;
+              }
+              if (rl) c = fmaxf(c, 0.f);
+            }
+            lcoef[b * kAxpyTile + i] = c;
+          }
+        }
+        __syncthreads();
+        if (active) {
+          for (int i0 = grp; i0 < tn; i0 += kAxGroups * U) {
+            float w[U][VEC];
+            float c[U][BT];
+  #pragma unroll
+            for (int u = 0; u < U; ++u) {
+              const int i = i0 + u * kAxGroups;
+              const int row = (i < tn) ? lrow[i] : -1;
+              if (row >= 0) {
+                load_cols<VEC, WT>(W, (long long)row * S.row_stride + col0, w[u]);
+              } else {
+  #pragma unroll
+                for (int v = 0; v < VEC; ++v) w[u][v] = 0.f;
+              }
+  #pragma unroll
+              for (int b = 0; b < BT; ++b) c[u][b] = (i < tn) ? lcoef[b * kAxpyTile + i] : 0.f;
+            }
+  #pragma unroll
+            for (int u = 0; u < U; ++u)
+  #pragma unroll
+              for (int b = 0; b < BT; ++b)
+  #pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[b][v] = fmaf(c[u][b], w[u][v], acc[b][v]);
+          }
+        }
       }
+    };
+    rows_of(std::false_type{}, S.rows, S.W, S.coef, S.coef_ld, S.relu, false, 0, n1);
+    if (n2 > 0) {
+      if (S.wait_ctr) wait_count(S.wait_ctr, S.wait_target);
+      if (S.coef2_nsplit > 0)
+        rows_of(std::true_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.relu2, true,
+                S.coef2_nsplit, n2);
+      else
+        rows_of(std::false_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.relu2,
+                S.wait_ctr != nullptr, 0, n2);
     }
   }
 
@@ -509,7 +673,7 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
   }
 }
 
-template <int BT>
+template <int BT, bool WAIT>
 __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds) {
   int s = 0;
 #pragma unroll
@@ -518,11 +682,11 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
   const AxpySeg S = ax_seg(T, s);
   const int lb = blk - S.block0;
   if (S.wdt == W_BF16) {
-    if (S.vec == 8) axpy_block<BT, 8, W_BF16>(S, lb, T.batch, lds);
-    else axpy_block<BT, 1, W_BF16>(S, lb, T.batch, lds);
+    if (S.vec == 8) axpy_block<BT, 8, W_BF16, WAIT>(S, lb, T.batch, lds);
+    else axpy_block<BT, 1, W_BF16, WAIT>(S, lb, T.batch, lds);
   } else {
-    if (S.vec == 4) axpy_block<BT, 4, W_F32>(S, lb, T.batch, lds);
-    else axpy_block<BT, 1, W_F32>(S, lb, T.batch, lds);
+    if (S.vec == 4) axpy_block<BT, 4, W_F32, WAIT>(S, lb, T.batch, lds);
+    else axpy_block<BT, 1, W_F32, WAIT>(S, lb, T.batch, lds);
   }
 }
 
@@ -560,7 +724,6 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
   float* gm = lds;                   // [NG <= 64] group max
   float* gl = lds + 64;              // [NG] group sum
   float* go = lds + 128;             // [NG][dh] group p.V; NG * dh = 256 * VEC <= 2048
-  int* flag = reinterpret_cast<int*>(lds + 128 + 2048);
 
   const size_t row0 = ((size_t)b * T.h + head) * (size_t)T.n + k0;   // first key row
   float qv[VEC];
@@ -632,18 +795,22 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
       O = fmaf(w, go[g * dh + tid], O);
     }
   }
-  float* outp = T.o + (size_t)b * T.o_ld + (size_t)slot * dh;
-  if (T.nsplit == 1) {
-    if (tid < dh) outp[tid] = O / L;
+  // Without tickets, this split's softmax piece (max, sum, p.V) is the result: the
+  // consumer of the head outputs combines the splits.  With tickets, the last split
+  // of each (token, head) to finish combines them here and stores o.
+  const int w2 = dh + 2;
+  if (T.tickets != nullptr && T.nsplit == 1) {
+    if (tid < dh) st_dev(&T.o[(size_t)b * T.o_ld + (size_t)slot * dh + tid], O / L);
     return;
   }
-  const int w2 = dh + 2;
   float* P = T.part + (((size_t)b * cap + slot) * T.nsplit + split) * w2;
   if (tid < dh) st_dev(&P[2 + tid], O);
   if (tid == 0) { st_dev(&P[0], M); st_dev(&P[1], L); }
+  if (T.tickets == nullptr) return;
+  int* flag = reinterpret_cast<int*>(lds + 128 + 2048);
   if (!arrive_last(&T.tickets[(size_t)b * cap + slot], (uint32_t)T.nsplit, flag)) return;
-  // merge the splits: (max, sum) of every split staged in LDS with one parallel load,
-  // the p.V partials fetched in batches of independent loads, summed in split order
+  // combine the splits: (max, sum) of every split staged in LDS with one parallel load,
+  // the p.V pieces fetched in batches of independent loads, summed in split order
   const float* P0 = T.part + ((size_t)b * cap + slot) * T.nsplit * w2;
   if (tid < T.nsplit) {
     gm[tid] = ld_dev(&P0[(size_t)tid * w2]);
@@ -670,7 +837,7 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
         }
       }
     }
-    outp[tid] = OO / LL;
+    st_dev(&T.o[(size_t)b * T.o_ld + (size_t)slot * dh + tid], OO / LL);
   }
 }
 
@@ -990,12 +1157,13 @@ __device__ __forceinline__ void phase_body(const PhaseArgs& a, float* lds) {
     if (blk >= a.b_attn && blk < a.b_attn + a.attn.blocks) {
       if (a.attn.kvdt == W_BF16) attn_task<W_BF16>(a.attn, blk - a.b_attn, lds);
       else attn_task<W_F32>(a.attn, blk - a.b_attn, lds);
+      if (a.attn.done_ctr) signal_done(a.attn.done_ctr);
       return;
     }
   }
   if constexpr ((FLAGS & T_AXPY) != 0) {
     if (blk >= a.b_axpy && blk < a.b_axpy + a.axpy.blocks) {
-      axpy_task<BT>(a.axpy, blk - a.b_axpy, lds);
+      axpy_task<BT, (FLAGS & T_WAIT) != 0>(a.axpy, blk - a.b_axpy, lds);
       return;
     }
   }
@@ -1005,10 +1173,19 @@ __device__ __forceinline__ void phase_body(const PhaseArgs& a, float* lds) {
 // blocks of <= 64 VGPRs, a kernel of at most 80 SGPRs keeps 8 blocks per CU resident,
 // one of 84 only 7.  The launch descriptor would otherwise take about 85, so every
 // launch mix is capped at 80 except the row dots, whose vector registers hold them
-// to 3 waves per SIMD anyway (they get a kernel of their own without the cap).
+// to 3 waves per SIMD anyway (they get a kernel of their own without the cap).  With
+// one token per block the mixes are also held to 64 VGPRs (8 waves per SIMD); with
+// 2 or 4 tokens per block they need more and get a kernel without that target.
+template <int FLAGS, int BT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80), amdgpu_waves_per_eu(8, 8)))
+void phase_kernel(PhaseArgs a) {
+  extern __shared__ float lds[];
+  phase_body<FLAGS, BT>(a, lds);
+}
+
 template <int FLAGS, int BT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80)))
-void phase_kernel(PhaseArgs a) {
+void phase_kernel_bt(PhaseArgs a) {
   extern __shared__ float lds[];
   phase_body<FLAGS, BT>(a, lds);
 }
@@ -1024,8 +1201,11 @@ static int launch_t(const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
   if constexpr (FLAGS == T_ROWDOT)
     hipLaunchKernelGGL((rowdot_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
                        static_cast<hipStream_t>(stream), a);
-  else
+  else if constexpr (BT == 1)
     hipLaunchKernelGGL((phase_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
+                       static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL((phase_kernel_bt<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
                        static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
@@ -1044,12 +1224,44 @@ int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes,
     case T_ROWDOT: return launch_bt<T_ROWDOT>(bt, a, grid, lds_bytes, stream);
     case T_AXPY: return launch_bt<T_AXPY>(bt, a, grid, lds_bytes, stream);
     case T_ATTN | T_AXPY: return launch_bt<T_ATTN | T_AXPY>(bt, a, grid, lds_bytes, stream);
+    case T_ATTN | T_AXPY | T_WAIT: return launch_bt<T_ATTN | T_AXPY | T_WAIT>(bt, a, grid, lds_bytes, stream);
     case T_AXPY | T_CLASSIFY: return launch_bt<T_AXPY | T_CLASSIFY>(bt, a, grid, lds_bytes, stream);
     case T_ATTN: return launch_t<T_ATTN, 1>(a, grid, lds_bytes, stream);
     case T_ZERO: return launch_t<T_ZERO, 1>(a, grid, lds_bytes, stream);
     case T_HIST: return launch_t<T_HIST, 1>(a, grid, lds_bytes, stream);
     case T_CLASSIFY: return launch_t<T_CLASSIFY, 1>(a, grid, lds_bytes, stream);
     default: return (int)hipErrorInvalidValue;
+  }
+}
+
+// Blocks of the kernel that runs (flags, bt) with lds_bytes of LDS that one CU holds
+// at once, as the runtime computes it from the kernel's registers and LDS.
+template <int FLAGS, int BT>
+static int occupancy_t(int lds_bytes) {
+  int n = 0;
+  hipError_t e;
+  if constexpr (FLAGS == T_ROWDOT)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rowdot_kernel<FLAGS, BT>, kThreads, lds_bytes);
+  else if constexpr (BT == 1)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, phase_kernel<FLAGS, BT>, kThreads, lds_bytes);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, phase_kernel_bt<FLAGS, BT>, kThreads, lds_bytes);
+  return e == hipSuccess ? n : 0;
+}
+
+template <int FLAGS>
+static int occupancy_bt(int bt, int lds_bytes) {
+  switch (bt) {
+    case 1: return occupancy_t<FLAGS, 1>(lds_bytes);
+    case 2: return occupancy_t<FLAGS, 2>(lds_bytes);
+    default: return occupancy_t<FLAGS, 4>(lds_bytes);
+  }
+}
+
+int phase_occupancy(int flags, int bt, int lds_bytes) {
+  switch (flags) {
+    case T_ATTN | T_AXPY | T_WAIT: return occupancy_bt<T_ATTN | T_AXPY | T_WAIT>(bt, lds_bytes);
+    default: return 0;
   }
 }
 

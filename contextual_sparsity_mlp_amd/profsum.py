@@ -80,8 +80,8 @@ def stats(src: str, trace: str, out: str, command: str):
         lines.append(f"| <{fl}, {bt}> | {blocks} | {len(v)} | {statistics.mean(v):.2f} | "
                      f"{statistics.median(v):.2f} | {min(v):.2f} |")
     if slot_durs[0]:
-        names = {0: "row dots (W1, W^Q, A rows)", 1: "attention + predictor B rows",
-                 2: "row sum W2 + W^O rows, combine, top-k"}
+        names = {0: "row dots (W1, W^Q, A rows)", 1: "attention + W2 rows + predictor B rows",
+                 2: "W^O rows into y_out + top-k"}
         lines += ["", "## Look-ahead decode step, per launch (from the kernel trace)", "",
                   "| launch | phase_kernel<flags> | launches | avg us | median us | min us |",
                   "|---|---|---|---|---|---|"]

@@ -27,9 +27,10 @@ def test_c4_batch1_bytes():
     assert b.kv == A.kv_bytes_per_token(c.dh, 1) * c.n_ctx * c.k_a
     ph = A.phase_bytes(batch=1, d=c.d, F=c.F, h=c.h, dh=c.dh, n_ctx=c.n_ctx, r=c.r, u_m=c.k_m,
                        u_a=c.k_a)
-    # the three launches together move every algorithmic byte of the step once,
-    # plus y read a second time and the scores read by the top-k
-    assert sum(ph) == b.total + 1 * c.d * 4 + (c.F + c.h) * 4
+    # the three launches together move every algorithmic byte of the step once, plus
+    # y read a second time, y_out read and written once more (the W^O rows are added
+    # in a later launch) and the scores read by the top-k
+    assert sum(ph) == b.total + 3 * c.d * 4 + (c.F + c.h) * 4
 
 
 def test_flops_intensity_batch1():
