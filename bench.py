@@ -193,8 +193,8 @@ def main():
     dv.timing_enable(False)
     ph_bytes = acc.phase_bytes(**shape)
     phases = []
-    names = ["row dots (W1, W^Q, A rows)", "attention + W2 rows + predictor B rows",
-             "W^O rows into y_out + top-k"]
+    names = ["row dots (W1, W^Q, A rows)", "attention + predictor B rows",
+             "row sum W2 + W^O rows, combine, top-k"]
     for i, (ms, n) in enumerate(zip(ph_ms, ph_n)):
         avg_us = ms * 1e3 / max(n, 1)
         b = ph_bytes[i] if i < len(ph_bytes) else 0

@@ -57,22 +57,27 @@ def step_flops(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: in
 
 def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
                 u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True):
-    """Bytes each launch of the look-ahead decode layer must move.
+    """Bytes each launch of the decode layer must move.
 
-    launch 1 (gathered row dots): W1 rows, W^Q rows, predictor A factors, y.
-    launch 2 (attention beside the MLP's output rows; predictor second factors):
-             W2 rows, K/V of the selected heads, y_in read, y_out written,
-             predictor B factors.
-    launch 3 (W^O rows added into y_out; next layer's top-k): W^O rows, y_out read
-             and written, scores read by the top-k.
-    Small intermediates handed between launches (row dots, q, head outputs,
-    scores written: under 1 MB at batch 1) are not counted.
+    With the predictor (the look-ahead step), three launches:
+      1 gathered row dots: W1 rows, W^Q rows, predictor A factors, y;
+      2 attention beside the predictor's second factors: K/V of the selected heads,
+        predictor B factors;
+      3 one row sum over W2 and W^O rows, combined with y_in into y_out, beside the
+        next layer's top-k: W2 rows, W^O rows, y_in read, y_out written, scores read.
+    Without it (the sparse MLP + MHA alone at small batch), two launches:
+      1 gathered row dots: W1 rows, W^Q rows, y;
+      2 attention, and the row sum over W2 then W^O rows: K/V, W2 rows, W^O rows,
+        y_in read, y_out written.
+    Small intermediates handed between launches (row dots, q, head outputs, attention
+    pieces, scores written: under 1 MB at batch 1) are not counted.
     """
     p1 = u_m * d * w_bytes + u_a * dh * d * w_bytes + batch * d * 4
-    p2 = u_m * d * w_bytes + batch * u_a * 2 * n_ctx * dh * kv_bytes + 2 * batch * d * 4
-    p3 = u_a * dh * d * w_bytes + 2 * batch * d * 4
-    if with_predictor:
-        p1 += 2 * r * d * w_bytes
-        p2 += (r * F + r * h) * w_bytes
-        p3 += batch * (F + h) * 4
+    kv = batch * u_a * 2 * n_ctx * dh * kv_bytes
+    out = u_m * d * w_bytes + u_a * dh * d * w_bytes + 2 * batch * d * 4
+    if not with_predictor:
+        return [p1, kv + out]
+    p1 += 2 * r * d * w_bytes
+    p2 = kv + (r * F + r * h) * w_bytes
+    p3 = out + batch * (F + h) * 4
     return [p1, p2, p3]

@@ -73,21 +73,39 @@ def stats(src: str, trace: str, out: str, command: str):
                 slot_durs[j].append(seq[i + j][1])
     lines += ["", "## Decode launches by configuration (from the kernel trace)", "",
               "flags: 1 row dots, 2 attention, 4 row sums, 8 histogram, 16 top-k classify, "
-              "64 zero fill (sums of these for a mixed launch)", "",
+              "32 row sums that wait for in-launch attention, 64 zero fill (sums of these "
+              "for a mixed launch)", "",
               "| phase_kernel<flags, batch tile> | blocks | launches | avg us | median us | min us |",
               "|---|---|---|---|---|---|"]
     for (fl, bt, blocks), v in sorted(groups.items(), key=lambda kv: -len(kv[1])):
         lines.append(f"| <{fl}, {bt}> | {blocks} | {len(v)} | {statistics.mean(v):.2f} | "
                      f"{statistics.median(v):.2f} | {min(v):.2f} |")
+    # launches of the sparse MLP + MHA step: row dots, then the single launch of
+    # attention and the waiting row sum
+    sp_order = ["1", "38"]
+    sp_durs = {k: [] for k in range(len(sp_order))}
+    for i in range(len(seq) - 1):
+        if seq[i][0] == sp_order[0] and seq[i + 1][0] == sp_order[1]:
+            for j in range(2):
+                sp_durs[j].append(seq[i + j][1])
     if slot_durs[0]:
-        names = {0: "row dots (W1, W^Q, A rows)", 1: "attention + W2 rows + predictor B rows",
-                 2: "W^O rows into y_out + top-k"}
+        names = {0: "row dots (W1, W^Q, A rows)", 1: "attention + predictor B rows",
+                 2: "row sum W2 + W^O rows, combine, top-k"}
         lines += ["", "## Look-ahead decode step, per launch (from the kernel trace)", "",
                   "| launch | phase_kernel<flags> | launches | avg us | median us | min us |",
                   "|---|---|---|---|---|---|"]
         for k in sorted(slot_durs):
             v = slot_durs[k]
             lines.append(f"| {k}: {names[k]} | <{SLOT_FLAGS[k]}, 1> | {len(v)} | "
+                         f"{statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} |")
+    if sp_durs[0]:
+        names = {0: "row dots (W1, W^Q rows)", 1: "attention + row sum W2 then W^O rows"}
+        lines += ["", "## Sparse MLP + MHA step, per launch (from the kernel trace)", "",
+                  "| launch | phase_kernel<flags> | launches | avg us | median us | min us |",
+                  "|---|---|---|---|---|---|"]
+        for k in sorted(sp_durs):
+            v = sp_durs[k]
+            lines.append(f"| {k}: {names[k]} | <{sp_order[k]}, 1> | {len(v)} | "
                          f"{statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} |")
     open(out, "w").write("\n".join(lines) + "\n")
 

@@ -28,9 +28,12 @@ def test_c4_batch1_bytes():
     ph = A.phase_bytes(batch=1, d=c.d, F=c.F, h=c.h, dh=c.dh, n_ctx=c.n_ctx, r=c.r, u_m=c.k_m,
                        u_a=c.k_a)
     # the three launches together move every algorithmic byte of the step once, plus
-    # y read a second time, y_out read and written once more (the W^O rows are added
-    # in a later launch) and the scores read by the top-k
-    assert sum(ph) == b.total + 3 * c.d * 4 + (c.F + c.h) * 4
+    # y read a second time and the scores read by the top-k
+    assert sum(ph) == b.total + 1 * c.d * 4 + (c.F + c.h) * 4
+    sp = A.phase_bytes(batch=1, d=c.d, F=c.F, h=c.h, dh=c.dh, n_ctx=c.n_ctx, r=c.r, u_m=c.k_m,
+                       u_a=c.k_a, with_predictor=False)
+    # the sparse layer alone: two launches, y read twice
+    assert len(sp) == 2 and sum(sp) == b.selected + 1 * c.d * 4
 
 
 def test_flops_intensity_batch1():
