@@ -25,7 +25,9 @@ beyond what the definitions state.  Sources, cited by page title and section:
   lower index winning ties.
 
 Readings where the pages are silent (each is listed in the design notes):
-  sigma is ReLU; no biases (Eq. 1/2 have none); the logit scale is a parameter,
+  sigma is ReLU unless GeLU is asked for (the page names both, section 2.3 under
+  Eq. (1)); GeLU is the exact x Phi(x) = x (1 + erf(x / sqrt 2)) / 2, Phi the
+  standard normal CDF (the page gives no approximation); no biases (Eq. 1/2 have none); the logit scale is a parameter,
   1.0 by default (Eq. 2 has no 1/sqrt(d_h)); exp is evaluated after subtracting
   the row maximum, an exact identity in real arithmetic that keeps fp64 finite;
   the cache holds exactly n rows K = X W^K, V = X W^V and the current token is
@@ -139,8 +141,24 @@ def relu(x):
     return np.maximum(x, 0.0)
 
 
-def sparse_mlp(y, W1t, W2t, S_M) -> np.ndarray:
-    """MLP_{S_M}(y) = sigma(y W1_{S_M}) (W2_{S_M})^T with sigma = ReLU.
+def gelu(x):
+    """GeLU(x) = x Phi(x), Phi(x) = (1 + erf(x / sqrt(2))) / 2 (float64 erf)."""
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def activation(name: str):
+    """sigma by name: "relu" or "gelu"."""
+    if name == "relu":
+        return relu
+    if name == "gelu":
+        return gelu
+    raise ValueError(f"unknown activation {name!r}")
+
+
+def sparse_mlp(y, W1t, W2t, S_M, act: str = "relu") -> np.ndarray:
+    """MLP_{S_M}(y) = sigma(y W1_{S_M}) (W2_{S_M})^T, sigma = ReLU or GeLU.
 
     W1t/W2t are stored neuron-major [F][d]: row i is the column W1_i / W2_i.
     Returns float64 [B][d].  An empty set gives exactly zero.
@@ -149,8 +167,8 @@ def sparse_mlp(y, W1t, W2t, S_M) -> np.ndarray:
     S = as_set(S_M)
     W1_S = rows(W1t, S).T          # d x |S|   (columns W1_i, i in S)
     W2_S = rows(W2t, S).T          # d x |S|
-    act = relu(y @ W1_S)           # [B][|S|]
-    return act @ W2_S.T            # [B][d]
+    h = activation(act)(y @ W1_S)  # [B][|S|]
+    return h @ W2_S.T              # [B][d]
 
 
 # --------------------------------------------------------------------------- #
@@ -202,11 +220,12 @@ def decode_layer(y, layer: dict, S_M, S_A, next_layer: dict | None, scale: float
     The sets of layer l+1 are predicted from y_l (the layer's input, not its
     output) with layer l+1's predictor: the asynchronous look-ahead.
     ``layer`` / ``next_layer`` hold W1t, W2t, Wq, Wo, K, V and, for the
-    predictor, A_M, B_M, A_A, B_A, k_m, k_a, union.
+    predictor, A_M, B_M, A_A, B_A, k_m, k_a, union; "act" (default "relu") names
+    the MLP's activation.
     Returns (y_next float64 [B][d], (S_M_next, S_A_next) or None).
     """
     yy = widen(y)
-    mlp = sparse_mlp(yy, layer["W1t"], layer["W2t"], S_M)
+    mlp = sparse_mlp(yy, layer["W1t"], layer["W2t"], S_M, layer.get("act", "relu"))
     mha = sparse_mha(yy, layer["Wq"], layer["Wo"], layer["K"], layer["V"], S_A, scale)
     y_next = yy + mlp + mha
     sets = None

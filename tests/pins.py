@@ -253,6 +253,75 @@ def check_mlp_set_order_irrelevant(O):
                  "set order")
 
 
+# GeLU (the page names it beside ReLU as sigma; section 2.3 under Eq. (1)).
+# Standard normal CDF values as tabulated (e.g. Abramowitz & Stegun, table 26.1):
+# GeLU(x) = x Phi(x).
+PHI_TABLE = {0.5: 0.6914624612740131, 1.0: 0.8413447460685429, 2.0: 0.9772498680518208,
+             -1.0: 0.15865525393145707, -2.5: 0.006209665325776159}
+
+
+def check_gelu_values(O):
+    for x, phi in PHI_TABLE.items():
+        got = float(O.gelu(np.array([x]))[0])
+        assert abs(got - x * phi) <= 1e-15 * max(1.0, abs(x)), f"gelu({x}) = {got} vs {x * phi}"
+    assert float(O.gelu(np.array([0.0]))[0]) == 0.0, "gelu(0) must be 0"
+    big = float(O.gelu(np.array([40.0]))[0])
+    assert big == 40.0, "gelu(x) = x for large x"
+
+
+def check_mlp_gelu_dense_library(O):
+    y, W1t, W2t = _mlp_data(16)
+    F, d = W1t.shape
+    ffn = torch.nn.Sequential(torch.nn.Linear(d, F), torch.nn.GELU(approximate="none"),
+                              torch.nn.Linear(F, d)).double()
+    with torch.no_grad():
+        ffn[0].weight.copy_(torch.from_numpy(W1t))
+        ffn[0].bias.zero_()
+        ffn[2].weight.copy_(torch.from_numpy(W2t.T.copy()))
+        ffn[2].bias.zero_()
+        ref = ffn(torch.from_numpy(y)).numpy()
+    out = O.sparse_mlp(y, W1t, W2t, np.arange(F), "gelu")
+    assert_close(out, ref, 1e-12, "gelu mlp S=all vs nn FFN")
+
+
+def check_mlp_gelu_loops_and_additive(O):
+    import math
+    y, W1t, W2t = _mlp_data(17, B=2, d=5, F=7)
+    S = [1, 2, 4, 6]
+    ref = np.zeros_like(y)
+    for b in range(2):
+        for i in S:
+            a = sum(y[b, j] * W1t[i, j] for j in range(5))
+            h = a * 0.5 * (1.0 + math.erf(a / math.sqrt(2.0)))
+            for j in range(5):
+                ref[b, j] += h * W2t[i, j]
+    assert_close(O.sparse_mlp(y, W1t, W2t, S, "gelu"), ref, 1e-13, "gelu mlp loops")
+    both = O.sparse_mlp(y, W1t, W2t, S, "gelu")
+    parts = O.sparse_mlp(y, W1t, W2t, S[:2], "gelu") + O.sparse_mlp(y, W1t, W2t, S[2:], "gelu")
+    assert_close(both, parts, 1e-13, "gelu mlp additivity")
+    assert np.array_equal(O.sparse_mlp(y, W1t, W2t, [], "gelu"), np.zeros_like(y))
+
+
+def check_layer_gelu(O):
+    r = _rng(18)
+    B, d, F, h, dh, n = 2, 8, 12, 2, 4, 3
+    layer = dict(W1t=r.standard_normal((F, d)), W2t=r.standard_normal((F, d)),
+                 Wq=r.standard_normal((h, dh, d)), Wo=r.standard_normal((h, dh, d)),
+                 K=r.standard_normal((B, h, n, dh)), V=r.standard_normal((B, h, n, dh)), act="gelu")
+    y = r.standard_normal((B, d))
+    S_M, S_A = [0, 3, 5, 11], [1]
+    got, _ = O.decode_layer(y, layer, S_M, S_A, None)
+    want = y + O.sparse_mlp(y, layer["W1t"], layer["W2t"], S_M, "gelu") + \
+        O.sparse_mha(y, layer["Wq"], layer["Wo"], layer["K"], layer["V"], S_A)
+    assert_close(got, want, 1e-13, "layer with gelu")
+    relu_out, _ = O.decode_layer(y, dict(layer, act="relu"), S_M, S_A, None)
+    assert rel_diff(got, relu_out) > 1e-3, "layer ignores its activation"
+
+
+def rel_diff(a, b):
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) / max(1e-300, float(np.max(np.abs(b))))
+
+
 # --------------------------------------------------------------------------- #
 # A4 sparse MHA                                                               #
 # --------------------------------------------------------------------------- #
@@ -381,6 +450,8 @@ ALL_CHECKS = [
     check_topk_bruteforce, check_topk_lexsort, check_topk_special,
     check_mlp_dense_library, check_mlp_empty_and_additive, check_mlp_relu_support,
     check_mlp_loops, check_mlp_set_order_irrelevant,
+    check_gelu_values, check_mlp_gelu_dense_library, check_mlp_gelu_loops_and_additive,
+    check_layer_gelu,
     check_mha_dense_library, check_mha_empty_and_additive, check_head_closed_forms,
     check_head_mean_shift, check_layer_composition, check_stack_lookahead,
 ]

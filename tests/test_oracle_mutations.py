@@ -22,19 +22,40 @@ def _mutant(**overrides):
     return m
 
 
-def _mlp_no_relu(y, W1t, W2t, S_M):
+def _mlp_no_relu(y, W1t, W2t, S_M, act="relu"):
     y = O.widen(y); S = O.as_set(S_M)
     return (y @ O.rows(W1t, S).T) @ O.rows(W2t, S)
 
 
-def _mlp_swapped(y, W1t, W2t, S_M):
+def _mlp_swapped(y, W1t, W2t, S_M, act="relu"):
     y = O.widen(y); S = O.as_set(S_M)
-    return O.relu(y @ O.rows(W2t, S).T) @ O.rows(W1t, S)
+    return O.activation(act)(y @ O.rows(W2t, S).T) @ O.rows(W1t, S)
 
 
-def _mlp_dropped_last(y, W1t, W2t, S_M):
+def _mlp_dropped_last(y, W1t, W2t, S_M, act="relu"):
     S = O.as_set(S_M)
-    return O.sparse_mlp(y, W1t, W2t, S[:-1]) if len(S) > 1 else O.sparse_mlp(y, W1t, W2t, S)
+    return O.sparse_mlp(y, W1t, W2t, S[:-1], act) if len(S) > 1 else O.sparse_mlp(y, W1t, W2t, S, act)
+
+
+def _gelu_tanh(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+
+
+def _gelu_no_half(x):
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def _gelu_no_sqrt2(x):
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x))
+
+
+def _mlp_act_ignored(y, W1t, W2t, S_M, act="relu"):
+    return O.sparse_mlp(y, W1t, W2t, S_M, "relu")
 
 
 def _head_div_n(y_b, WQ_i, K_bi, V_bi, scale=1.0):
@@ -151,6 +172,10 @@ MUTANTS = {
     "mlp drops a neuron": dict(sparse_mlp=_mlp_dropped_last),
     "relu as identity": dict(relu=lambda x: x),
     "relu keeps negative part": dict(relu=lambda x: np.minimum(x, 0.0)),
+    "gelu tanh approximation": dict(gelu=_gelu_tanh),
+    "gelu without the half": dict(gelu=_gelu_no_half),
+    "gelu erf without sqrt 2": dict(gelu=_gelu_no_sqrt2),
+    "mlp ignores the activation": dict(sparse_mlp=_mlp_act_ignored),
     "head divides by n": dict(head_output=_head_div_n),
     "head uses keys as values": dict(head_output=_head_values_from_keys),
     "head ignores scale": dict(head_output=_head_no_scale),
