@@ -84,6 +84,8 @@ def main():
                     help="run one plain 1 GiB device copy first (counter calibration)")
     ap.add_argument("--lookahead-only", action="store_true",
                     help="skip the per-launch event pass and the sparse-only pass")
+    ap.add_argument("--act", choices=("relu", "gelu"), default="relu",
+                    help="sigma of the MLP (OPT uses ReLU; GeLU is the page's other choice)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -126,7 +128,8 @@ def main():
         ys.append(synth.make_y(cfg, dev, layer=l, batch=B))
     torch.cuda.synchronize()
     dvl = [dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, L.A_M, L.B_M, L.A_A, L.B_A,
-                    k_m=k_m, k_a=k_a, scale=cfg.scale) for L in layers]
+                    k_m=k_m, k_a=k_a, scale=cfg.scale,
+                    act=dv.DV_ACT_GELU if args.act == "gelu" else dv.DV_ACT_RELU) for L in layers]
 
     i32 = lambda n: torch.zeros(n, dtype=torch.int32, device=dev)  # noqa: E731
     sets = [dict(m=i32(cap_m), cm=i32(1), a=i32(cap_a), ca=i32(1)) for _ in range(2)]
@@ -228,7 +231,8 @@ def main():
 
     cpu = None
     if args.cpu_layers > 0:
-        cpu = cpu_baseline(args.cpu_layers, layers, ys, sets, cfg, B, u_m, u_a, full_bytes.total)
+        cpu = cpu_baseline(args.cpu_layers, layers, ys, sets, cfg, B, u_m, u_a, full_bytes.total,
+                           args.act)
 
     out = {
         "metric": METRIC,
@@ -244,7 +248,9 @@ def main():
         "dtype": "f32",
         "weights_dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"opt-175b-shaped decode layer, batch {B}, look-ahead predictor",
+        "config": {"workload": f"opt-175b-shaped decode layer, batch {B}, look-ahead predictor"
+                               + (", GeLU MLP" if args.act == "gelu" else ""),
+                   "act": args.act,
                    "d": cfg.d, "F": cfg.F, "h": cfg.h, "dh": cfg.dh, "n_ctx": cfg.n_ctx,
                    "r": cfg.r, "batch": B, "k_m": k_m, "k_a": k_a, "U_M": u_m, "U_A": u_a,
                    "replicas": R},
@@ -269,7 +275,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(n_layers, layers, ys, sets, cfg, B, u_m, u_a, step_bytes_total):
+def cpu_baseline(n_layers, layers, ys, sets, cfg, B, u_m, u_a, step_bytes_total, act="relu"):
     """The CPU oracle (float64 NumPy, as it stands) on host copies of replica 0."""
     import numpy as np
     import torch
@@ -285,7 +291,7 @@ def cpu_baseline(n_layers, layers, ys, sets, cfg, B, u_m, u_a, step_bytes_total)
     log(f"cpu baseline: {n_layers} oracle decode layers on host copies")
     L, L1 = layers[0], layers[1 % len(layers)]
     layer_h = dict(W1t=host(L.W1t), W2t=host(L.W2t), Wq=host(L.Wq), Wo=host(L.Wo), K=host(L.K),
-                   V=host(L.V))
+                   V=host(L.V), act=act)
     nxt_h = dict(A_M=host(L1.A_M), B_M=host(L1.B_M), A_A=host(L1.A_A), B_A=host(L1.B_A),
                  k_m=cfg.k_m, k_a=cfg.k_a, union=True)
     # replica 0's own sets, as the oracle would predict them from y_0

@@ -36,6 +36,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 size_t esize(dv_dtype t) { return t == DV_BF16 ? 2 : 4; }
 bool valid_dtype(int t) { return t == DV_F32 || t == DV_BF16; }
+bool valid_act(int a) { return a == DV_ACT_RELU || a == DV_ACT_GELU; }
+int act_code(int a) { return a == DV_ACT_GELU ? A_GELU : A_RELU; }
 
 #define CHECK_PTR(p) \
   do { if (!(p)) return fail(DV_EINVAL, "%s: %s is NULL", fn, #p); } while (0)
@@ -279,8 +281,8 @@ int rowdot_lds(const RowdotTask& T) { return T.bt_lds * T.d * 4; }
 // Axpy segment over one row source, or two sources summed into the same columns
 // (second source: W2 != nullptr; same stride and dtype, rows after the first's).
 void add_axpy2(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype wdt, RowList L,
-               const float* coef, int coef_ld, int relu, const void* W2, RowList L2,
-               const float* coef2, int coef2_ld, int relu2, int ncols, float* partial,
+               const float* coef, int coef_ld, int act, const void* W2, RowList L2,
+               const float* coef2, int coef2_ld, int act2, int ncols, float* partial,
                uint32_t* tickets, float* out, int out_ld, const float* add0, const float* add1,
                int add_ld, int accumulate, int target_blocks) {
   AxpySeg& S = T.seg[T.nseg];
@@ -288,8 +290,8 @@ void add_axpy2(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype
   cap_rows = std::max(1, cap_rows);
   const AxGeo g = ax_geo(batch, ncols, stride, wdt, cap_rows);
   S.W = W; S.row_stride = stride; S.wdt = (wdt == DV_BF16) ? W_BF16 : W_F32;
-  S.rows = L; S.coef = coef; S.coef_ld = coef_ld; S.relu = relu; S.ncols = ncols;
-  S.W2 = W2; S.rows2 = L2; S.coef2 = coef2; S.coef2_ld = coef2_ld; S.relu2 = relu2;
+  S.rows = L; S.coef = coef; S.coef_ld = coef_ld; S.act = act; S.ncols = ncols;
+  S.W2 = W2; S.rows2 = L2; S.coef2 = coef2; S.coef2_ld = coef2_ld; S.act2 = act2;
   S.vec = g.vec; S.nslices = g.nslices; S.nbt = g.nbt;
   // About target_blocks blocks for the segment (512-byte row slices need many loads
   // in flight to stream well); at most kMaxChunks chunk partials per slice (a short,
@@ -307,10 +309,10 @@ void add_axpy2(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype
 }
 
 void add_axpy(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype wdt, RowList L,
-              const float* coef, int coef_ld, int relu, int ncols, float* partial, uint32_t* tickets,
+              const float* coef, int coef_ld, int act, int ncols, float* partial, uint32_t* tickets,
               float* out, int out_ld, const float* add0, const float* add1, int add_ld,
               int accumulate, int target_blocks) {
-  add_axpy2(T, batch, W, stride, wdt, L, coef, coef_ld, relu, nullptr, RowList{}, nullptr, 0, 0,
+  add_axpy2(T, batch, W, stride, wdt, L, coef, coef_ld, act, nullptr, RowList{}, nullptr, 0, 0,
             ncols, partial, tickets, out, out_ld, add0, add1, add_ld, accumulate, target_blocks);
 }
 
@@ -418,7 +420,7 @@ extern "C" {
 
 const char* dv_last_error(void) { return g_err.c_str(); }
 
-int dv_version(void) { return 100; }
+int dv_version(void) { return 101; }
 
 static size_t ws_bytes_for(int op, const dv_shape* s, dv_dtype wdt) {
   const int B = s->batch;
@@ -531,7 +533,7 @@ int dv_select_topk(const float* scores, int batch, int N, int k, int union_rows,
 
 int dv_sparse_mlp(const float* y, int batch, int d, const void* W1t, const void* W2t, int F,
                   dv_dtype wdt, const int32_t* idx, const int32_t* count, int max_count, float* out,
-                  int accumulate, void* ws, size_t ws_bytes, void* stream) {
+                  int accumulate, int act, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "dv_sparse_mlp";
   t_slot = 0;
   CHECK_PTR(y); CHECK_PTR(W1t); CHECK_PTR(W2t); CHECK_PTR(idx); CHECK_PTR(count); CHECK_PTR(out);
@@ -539,6 +541,7 @@ int dv_sparse_mlp(const float* y, int batch, int d, const void* W1t, const void*
   if (F <= 0) return fail(DV_EINVAL, "%s: F = %d", fn, F);
   if (max_count < 0 || max_count > F) return fail(DV_EINVAL, "%s: max_count = %d not in [0, F]", fn, max_count);
   if (!valid_dtype(wdt)) return fail(DV_EINVAL, "%s: bad dtype %d", fn, (int)wdt);
+  if (!valid_act(act)) return fail(DV_EINVAL, "%s: bad activation %d", fn, act);
   if (int e = check_d(fn, d)) return e;
   CHECK_ALIGN(y); CHECK_ALIGN(W1t); CHECK_ALIGN(W2t); CHECK_ALIGN(idx); CHECK_ALIGN(count);
   CHECK_ALIGN(out);
@@ -547,18 +550,18 @@ int dv_sparse_mlp(const float* y, int batch, int d, const void* W1t, const void*
   if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
   char* w = static_cast<char*>(ws);
   const int cap = std::max(max_count, 1);
-  float* act = reinterpret_cast<float*>(w + P.a);
+  float* hbuf = reinterpret_cast<float*>(w + P.a);
   uint32_t* tickets = reinterpret_cast<uint32_t*>(w + P.tickets);
   const int bt = pick_bt(batch);
   const RowList L = make_list(idx, count, max_count, 1, F);
 
   PhaseArgs a1 = zero_args();
-  add_rowdot(a1.rowdot, W1t, d, wdt, L, act, cap);
+  add_rowdot(a1.rowdot, W1t, d, wdt, L, hbuf, cap);
   finish_rowdot(a1.rowdot, y, batch, d, tickets, P.nt);
   if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
 
   PhaseArgs a2 = zero_args();
-  add_axpy(a2.axpy, batch, W2t, d, wdt, L, act, cap, 1, d, reinterpret_cast<float*>(w + P.partial),
+  add_axpy(a2.axpy, batch, W2t, d, wdt, L, hbuf, cap, act_code(act), d, reinterpret_cast<float*>(w + P.partial),
            tickets, out, d, nullptr, nullptr, 0, accumulate, default_axpy_blocks());
   a2.axpy.batch = batch;
   return launch(T_AXPY, bt, a2, a2.axpy.blocks, axpy_lds(bt), stream, fn);
@@ -628,6 +631,7 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   if (F <= 0 || h <= 0) return fail(DV_EINVAL, "%s: F = %d, h = %d", fn, F, h);
   if (int e = check_nctx(fn, n)) return e;
   if (!valid_dtype(L->wdt) || !valid_dtype(L->kvdt)) return fail(DV_EINVAL, "%s: bad dtype", fn);
+  if (!valid_act(L->act)) return fail(DV_EINVAL, "%s: bad activation %d", fn, L->act);
   if (!(L->scale == L->scale)) return fail(DV_EINVAL, "%s: scale is NaN", fn);
   if (int e = check_d(fn, d)) return e;
   if (int e = check_dh(fn, dh)) return e;
@@ -691,7 +695,8 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   // the next layer its predictor scores (with top-digit histograms) and top-k.
   const long long wb = (wdt == DV_BF16) ? 2 : 4;
   auto add_out = [&](AxpyTask& T, int target, const float* coef2, int nsplit) {
-    add_axpy2(T, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, 1, L->Wo, LQ, coef2, cap_a * dh, 0,
+    add_axpy2(T, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, act_code(L->act), L->Wo, LQ, coef2,
+              cap_a * dh, A_NONE,
               d, fp(P.p_wo), t_wo, y_out, d, y_in, nullptr, d, 0, target);
     T.seg[T.nseg - 1].coef2_nsplit = nsplit;
   };

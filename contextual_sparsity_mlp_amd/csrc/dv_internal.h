@@ -38,6 +38,7 @@ constexpr int kMaxSegs = 256;            // classify segments per row (N <= 5242
 constexpr int kWordsPerThread = 4;       // bitmask words per thread when compacting
 
 enum : int { W_F32 = 0, W_BF16 = 1 };
+enum : int { A_NONE = 0, A_RELU = 1, A_GELU = 2 };   // row-sum coefficient activations
 
 // A logical list of rows: slot s < count expands to rows idx[s]*expand + e, e < expand.
 struct RowList {
@@ -76,14 +77,14 @@ struct AxpySeg {
   RowList rows;
   const float* coef;       // coef[b * coef_ld + s*expand + e]
   int coef_ld;
-  int relu;                // use max(coef, 0)
+  int act;                 // activation applied to each coefficient: A_NONE, A_RELU, A_GELU
   // Optional second row source summed into the same columns (same stride and
   // dtype): its rows follow the first source's rows in the row order.
   const void* W2;          // nullptr: one source
   RowList rows2;
   const float* coef2;
   int coef2_ld;
-  int relu2;
+  int act2;
   int coef2_nsplit;        // > 0: coef2 holds attention pieces [batch][rows2.host_count]
                            //   [coef2_nsplit][rows2.expand + 2] that are combined per
                            //   row (rows2.expand = dh); 0: plain coefficients

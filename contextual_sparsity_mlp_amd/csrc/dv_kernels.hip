@@ -156,6 +156,14 @@ __device__ __forceinline__ void signal_done(uint32_t* ctr) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// sigma of Eq. (1) applied to a row-sum coefficient: ReLU, or GeLU x Phi(x) with
+// Phi(x) = (1 + erf(x / sqrt 2)) / 2 (the device library's erff).
+__device__ __forceinline__ float activate(float c, int act) {
+  if (act == A_RELU) return fmaxf(c, 0.f);
+  if (act == A_GELU) return 0.5f * c * (1.f + erff(c * 0.70710678118654752f));
+  return c;
+}
+
 // Order-preserving map of a float to uint32 (larger float -> larger key);
 // -0.0 is mapped like +0.0.
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -435,13 +443,13 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
         lrow[i] = ok ? ((item * ex + e) | (second ? (1 << 30) : 0)) : -1;
         const float* cf = second ? S.coef2 : S.coef;
         const int cld = second ? S.coef2_ld : S.coef_ld;
-        const int rl = second ? S.relu2 : S.relu;
+        const int rl = second ? S.act2 : S.act;
   #pragma unroll
         for (int b = 0; b < BT; ++b) {
           float c = 0.f;
           if (ok && b < nb) {
             c = cf[(size_t)(b0 + b) * cld + rr];
-            if (rl) c = fmaxf(c, 0.f);
+            c = activate(c, rl);
           }
           lcoef[b * kAxpyTile + i] = c;
         }
@@ -562,7 +570,7 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
                 const float* cp = &cf[(size_t)(b0 + b) * cld + rr];
                 c = coherent ? ld_dev(cp) : *cp;
               }
-              if (rl) c = fmaxf(c, 0.f);
+              c = activate(c, rl);
             }
             lcoef[b * kAxpyTile + i] = c;
           }
@@ -595,14 +603,14 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
         }
       }
     };
-    rows_of(std::false_type{}, S.rows, S.W, S.coef, S.coef_ld, S.relu, false, 0, n1);
+    rows_of(std::false_type{}, S.rows, S.W, S.coef, S.coef_ld, S.act, false, 0, n1);
     if (n2 > 0) {
       if (S.wait_ctr) wait_count(S.wait_ctr, S.wait_target);
       if (S.coef2_nsplit > 0)
-        rows_of(std::true_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.relu2, true,
+        rows_of(std::true_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, true,
                 S.coef2_nsplit, n2);
       else
-        rows_of(std::false_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.relu2,
+        rows_of(std::false_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2,
                 S.wait_ctr != nullptr, 0, n2);
     }
   }

@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libdv.so")
 
 DV_F32, DV_BF16 = 0, 1
+DV_ACT_RELU, DV_ACT_GELU = 0, 1
 DV_OK, DV_EINVAL, DV_EALIGN, DV_EUNSUPPORTED, DV_EWORKSPACE, DV_EHIP = 0, -1, -2, -3, -4, -5
 OP_PREDICT, OP_SELECT_TOPK, OP_SPARSE_MLP, OP_SPARSE_MHA, OP_DECODE_LAYER = 1, 2, 3, 4, 5
 
@@ -43,7 +44,8 @@ class LayerStruct(ctypes.Structure):
                                              "wdt", "kvdt")] + \
                [("scale", ctypes.c_float)] + \
                [(n, ctypes.c_void_p) for n in ("W1t", "W2t", "Wq", "Wo", "K", "V",
-                                                "A_M", "B_M", "A_A", "B_A")]
+                                                "A_M", "B_M", "A_A", "B_A")] + \
+               [("act", ctypes.c_int)]
 
 
 _lib = None
@@ -64,7 +66,7 @@ def lib() -> ctypes.CDLL:
         L.dv_workspace_bytes.argtypes = [i, ctypes.POINTER(Shape)]
         L.dv_predict.argtypes = [vp, i, i, vp, vp, i, i, i, vp, vp, sz, vp]
         L.dv_select_topk.argtypes = [vp, i, i, i, i, vp, vp, vp, sz, vp]
-        L.dv_sparse_mlp.argtypes = [vp, i, i, vp, vp, i, i, vp, vp, i, vp, i, vp, sz, vp]
+        L.dv_sparse_mlp.argtypes = [vp, i, i, vp, vp, i, i, vp, vp, i, vp, i, i, vp, sz, vp]
         L.dv_sparse_mha.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, i, i, vp, vp, i, f, vp, i,
                                     vp, sz, vp]
         L.dv_decode_layer.argtypes = [ctypes.POINTER(LayerStruct), ctypes.POINTER(LayerStruct), i,
@@ -153,14 +155,14 @@ def select_topk(scores, k, union_rows, idx, count, ws, stream=None, *, batch=Non
 
 
 def sparse_mlp(y, W1t, W2t, idx, count, max_count, out, accumulate, ws, stream=None, *,
-               batch=None, d=None, F=None, wdt=None):
+               batch=None, d=None, F=None, wdt=None, act=DV_ACT_RELU):
     batch = y.shape[0] if batch is None else batch
     d = y.shape[1] if d is None else d
     F = W1t.shape[0] if F is None else F
     wdt = _dtype(W1t) if wdt is None else wdt
     _check(lib().dv_sparse_mlp(_ptr(y), batch, d, _ptr(W1t), _ptr(W2t), F, wdt, _ptr(idx),
-                               _ptr(count), int(max_count), _ptr(out), int(accumulate), _ptr(ws),
-                               _nbytes(ws), _stream(stream)))
+                               _ptr(count), int(max_count), _ptr(out), int(accumulate), int(act),
+                               _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def sparse_mha(y, Wq, Wo, K, V, heads, count, max_count, scale, out, accumulate, ws, stream=None,
@@ -181,14 +183,15 @@ class Layer:
     """A dv_layer built from a layer's tensors; keeps them alive while in use."""
 
     def __init__(self, W1t, W2t, Wq, Wo, K, V, A_M=None, B_M=None, A_A=None, B_A=None, *,
-                 k_m=0, k_a=0, scale=1.0):
+                 k_m=0, k_a=0, scale=1.0, act=DV_ACT_RELU):
         self.tensors = (W1t, W2t, Wq, Wo, K, V, A_M, B_M, A_A, B_A)
         r = A_M.shape[0] if A_M is not None else 0
         self.s = LayerStruct(d=W1t.shape[1], F=W1t.shape[0], h=Wq.shape[0], dh=Wq.shape[1],
                              n_ctx=K.shape[2], r=r, k_m=int(k_m), k_a=int(k_a),
                              wdt=_dtype(W1t), kvdt=_dtype(K), scale=float(scale),
                              W1t=_ptr(W1t), W2t=_ptr(W2t), Wq=_ptr(Wq), Wo=_ptr(Wo), K=_ptr(K),
-                             V=_ptr(V), A_M=_ptr(A_M), B_M=_ptr(B_M), A_A=_ptr(A_A), B_A=_ptr(B_A))
+                             V=_ptr(V), A_M=_ptr(A_M), B_M=_ptr(B_M), A_A=_ptr(A_A), B_A=_ptr(B_A),
+                             act=int(act))
 
 
 def decode_layer(layer: Layer, next_layer, y_in, y_out, idx_m, count_m, max_count_m, idx_a, count_a,

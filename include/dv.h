@@ -53,6 +53,10 @@ extern "C" {
 
 typedef enum { DV_F32 = 0, DV_BF16 = 1 } dv_dtype;
 
+/* sigma of Eq. (1): the page names ReLU or GeLU (section 2.3, under Eq. (1)).  GeLU is
+ * the exact x Phi(x) = x (1 + erf(x / sqrt 2)) / 2 (the page gives no approximation). */
+typedef enum { DV_ACT_RELU = 0, DV_ACT_GELU = 1 } dv_act;
+
 enum {
   DV_OK = 0,
   DV_EINVAL = -1,        /* bad argument: null pointer, size out of range, k not in [0, N] */
@@ -119,14 +123,15 @@ int dv_predict(const float* y, int batch, int d,
 int dv_select_topk(const float* scores, int batch, int N, int k, int union_rows,
                    int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
 
-/* A3 - sparse MLP, Deja Vu page section 2.3 Eq. (1), sigma = ReLU, no bias:
- *   out[b] (+)= sum_{s < count} max(y[b] . W1t[idx[s]], 0) * W2t[idx[s]].
- * The set is shared by every token of the batch.  accumulate != 0 adds to `out`,
- * otherwise `out` is overwritten.  `out` must not alias `y`. */
+/* A3 - sparse MLP, Deja Vu page section 2.3 Eq. (1), no bias:
+ *   out[b] (+)= sum_{s < count} sigma(y[b] . W1t[idx[s]]) * W2t[idx[s]],
+ * sigma = ReLU (act = DV_ACT_RELU) or GeLU (DV_ACT_GELU; any other value is
+ * DV_EINVAL).  The set is shared by every token of the batch.  accumulate != 0 adds
+ * to `out`, otherwise `out` is overwritten.  `out` must not alias `y`. */
 int dv_sparse_mlp(const float* y, int batch, int d,
                   const void* W1t, const void* W2t, int F, dv_dtype wdt,
                   const int32_t* idx, const int32_t* count, int max_count,
-                  float* out, int accumulate, void* ws, size_t ws_bytes, void* stream);
+                  float* out, int accumulate, int act, void* ws, size_t ws_bytes, void* stream);
 
 /* A4 - head-sparse decode attention, Deja Vu page section 2.3 Eq. (2):
  *   q = y[b] W_i^Q,  t_j = scale * q . K[b][i][j],  p = softmax(t) over j < n_ctx,
@@ -150,6 +155,7 @@ typedef struct {
   const void *K, *V;       /* [batch][h][n_ctx][dh] */
   const void *A_M, *B_M;   /* neuron predictor: [r][d], [r][F] */
   const void *A_A, *B_A;   /* head predictor:   [r][d], [r][h] */
+  int act;                 /* sigma of this layer's MLP: dv_act (DV_ACT_RELU = 0) */
 } dv_layer;
 
 /* A5 - one decode layer with the look-ahead predictor (Deja Vu page, section 1 and

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(dv.EXPORTS), f"header {names} vs binding {dv.EXPORTS}"
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.dv_version() == 100
+    assert lib.dv_version() == 101
 
 
 def test_library_has_gfx950_code():
@@ -63,11 +63,12 @@ def test_workspace_bad_shape():
 
 def call_mlp(**over):
     a = dict(y=P, batch=1, d=256, W1t=P, W2t=P, F=1024, wdt=dv.DV_BF16, idx=P, count=P,
-             max_count=10, out=P + 4096, acc=0, ws=P, ws_bytes=1 << 30, stream=None)
+             max_count=10, out=P + 4096, acc=0, act=dv.DV_ACT_RELU, ws=P, ws_bytes=1 << 30,
+             stream=None)
     a.update(over)
     return dv.lib().dv_sparse_mlp(a["y"], a["batch"], a["d"], a["W1t"], a["W2t"], a["F"], a["wdt"],
-                                  a["idx"], a["count"], a["max_count"], a["out"], a["acc"], a["ws"],
-                                  a["ws_bytes"], a["stream"])
+                                  a["idx"], a["count"], a["max_count"], a["out"], a["acc"], a["act"],
+                                  a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("over,code", [
@@ -78,6 +79,7 @@ def call_mlp(**over):
     (dict(W1t=BAD), dv.DV_EALIGN), (dict(out=BAD), dv.DV_EALIGN), (dict(idx=BAD), dv.DV_EALIGN),
     (dict(ws=None), dv.DV_EWORKSPACE), (dict(ws_bytes=100), dv.DV_EWORKSPACE),
     (dict(ws=BAD), dv.DV_EALIGN), (dict(out=P), dv.DV_EINVAL),
+    (dict(act=2), dv.DV_EINVAL), (dict(act=-1), dv.DV_EINVAL),
 ])
 def test_sparse_mlp_rejects(over, code):
     assert call_mlp(**over) == code
@@ -157,6 +159,7 @@ def _layer(**over):
     (dict(K=BAD), dict(), dict(), dv.DV_EALIGN),
     (dict(), dict(), dict(ws_bytes=64), dv.DV_EWORKSPACE),
     (dict(n_ctx=0), dict(), dict(), dv.DV_EINVAL),
+    (dict(act=5), dict(), dict(), dv.DV_EINVAL),
 ])
 def test_decode_layer_rejects(lo, no, args, code):
     a = dict(batch=1, y_in=P, y_out=P, idx_m=P, count_m=P, max_count_m=154, idx_a=P, count_a=P,

@@ -165,17 +165,18 @@ def test_select_topk_gpu_scores():
 # A3 sparse MLP                                                               #
 # --------------------------------------------------------------------------- #
 
-def _mlp_case(cfg, L, y, S, accumulate=False, cap=None):
+def _mlp_case(cfg, L, y, S, accumulate=False, cap=None, act="relu"):
     B = y.shape[0]
     cap = len(S) if cap is None else cap
     idx, cnt = put_set(S, cap)
+    code = dv.DV_ACT_GELU if act == "gelu" else dv.DV_ACT_RELU
     out = torch.full((B, cfg.d), 0.5 if accumulate else np.nan, dtype=torch.float32, device=DEV)
     ws = dv.workspace(dv.OP_SPARSE_MLP, batch=B, d=cfg.d, max_count_m=cap)
-    dv.sparse_mlp(y, L.W1t, L.W2t, idx, cnt, cap, out, accumulate, ws)
-    ref = O.sparse_mlp(host(y), host(L.W1t), host(L.W2t), S) + (0.5 if accumulate else 0.0)
+    dv.sparse_mlp(y, L.W1t, L.W2t, idx, cnt, cap, out, accumulate, ws, act=code)
+    ref = O.sparse_mlp(host(y), host(L.W1t), host(L.W2t), S, act) + (0.5 if accumulate else 0.0)
     got = out.cpu().numpy()
     out2 = torch.full_like(out, 0.5 if accumulate else np.nan)
-    dv.sparse_mlp(y, L.W1t, L.W2t, idx, cnt, cap, out2, accumulate, ws)
+    dv.sparse_mlp(y, L.W1t, L.W2t, idx, cnt, cap, out2, accumulate, ws, act=code)
     assert torch.equal(out, out2), "sparse_mlp not deterministic"
     return got, ref
 
@@ -189,6 +190,20 @@ def test_sparse_mlp_parity(name):
     S = synth.random_index_set(cfg.F, cfg.k_m, seed=cfg.cfg_id).numpy()
     got, ref = _mlp_case(cfg, L, y, S)
     assert_close(got, ref, tol_of(cfg, TIGHT_MLP), f"mlp {name}")
+
+
+@pytest.mark.parametrize("name", ["c1", "bf16-ragged", "f32-ragged", "c2"])
+def test_sparse_mlp_gelu(name):
+    """sigma = GeLU (the page's other named activation)."""
+    cfg = cfg_of(name)
+    banner(f"sparse_mlp gelu {name}")
+    L = synth.make_layer(cfg, DEV, with_kv=False)
+    y = synth.make_y(cfg, DEV)
+    S = synth.random_index_set(cfg.F, cfg.k_m, seed=cfg.cfg_id + 40).numpy()
+    got, ref = _mlp_case(cfg, L, y, S, act="gelu")
+    assert_close(got, ref, tol_of(cfg, TIGHT_MLP), f"gelu mlp {name}")
+    got_a, ref_a = _mlp_case(cfg, L, y, S, accumulate=True, act="gelu")
+    assert_close(got_a, ref_a, tol_of(cfg, TIGHT_MLP), f"gelu mlp accumulate {name}")
 
 
 @pytest.mark.parametrize("name", ["c1", "bf16-ragged", "f32-ragged"])
@@ -292,7 +307,7 @@ def test_sparse_mha_edges(name):
 # A5 decode layer with the look-ahead predictor                               #
 # --------------------------------------------------------------------------- #
 
-def _layer_case(cfg, batch=None, with_next=True, seed_sets=None):
+def _layer_case(cfg, batch=None, with_next=True, seed_sets=None, act="relu"):
     B = cfg.batch if batch is None else batch
     L = synth.make_layer(cfg, DEV, batch=B)
     P1 = synth.make_predictor(cfg, DEV, layer=1)
@@ -306,7 +321,8 @@ def _layer_case(cfg, batch=None, with_next=True, seed_sets=None):
     idx_m, cnt_m = put_set(S_M, cap_m)
     idx_a, cnt_a = put_set(S_A, cap_a)
     layer = dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, L.A_M, L.B_M, L.A_A, L.B_A,
-                     k_m=cfg.k_m, k_a=cfg.k_a, scale=cfg.scale)
+                     k_m=cfg.k_m, k_a=cfg.k_a, scale=cfg.scale,
+                     act=dv.DV_ACT_GELU if act == "gelu" else dv.DV_ACT_RELU)
     nxt = dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, P1["A_M"], P1["B_M"], P1["A_A"], P1["B_A"],
                    k_m=cfg.k_m, k_a=cfg.k_a, scale=cfg.scale) if with_next else None
     n_idx_m = torch.full((cap_m,), -9, dtype=torch.int32, device=DEV)
@@ -319,7 +335,8 @@ def _layer_case(cfg, batch=None, with_next=True, seed_sets=None):
     dv.decode_layer(layer, nxt, y, y_out, idx_m, cnt_m, cap_m, idx_a, cnt_a, cap_a,
                     n_idx_m, n_cnt_m, n_idx_a, n_cnt_a, ws)
     torch.cuda.synchronize()
-    layer_d = dict(W1t=Lh["W1t"], W2t=Lh["W2t"], Wq=Lh["Wq"], Wo=Lh["Wo"], K=Lh["K"], V=Lh["V"])
+    layer_d = dict(W1t=Lh["W1t"], W2t=Lh["W2t"], Wq=Lh["Wq"], Wo=Lh["Wo"], K=Lh["K"], V=Lh["V"],
+                   act=act)
     y_ref, _ = O.decode_layer(yh, layer_d, S_M, S_A, None, cfg.scale)
     res = dict(y_out=y_out.cpu().numpy(), y_ref=y_ref, y=y, layer=layer, ws=ws)
     if with_next:
@@ -347,6 +364,18 @@ def test_decode_layer_parity(name):
     assert_close(r["y_out"], r["y_ref"], tol_of(cfg, TIGHT_ATTN), f"layer {name}")
     for got, ref_s, k, bound in r["sets"]:
         check_sets_certified(got, ref_s, k, True, bound, f"{name} next sets")
+
+
+@pytest.mark.parametrize("name", ["bf16-ragged", "c4"])
+def test_decode_layer_gelu(name):
+    """A layer whose MLP uses GeLU: output and the next layer's sets (the predictor does
+    not depend on the activation); c4 at batch 1 is the benchmarked shape."""
+    cfg = cfg_of(name)
+    banner(f"decode_layer gelu {name}")
+    r = _layer_case(cfg, batch=1 if name == "c4" else None, act="gelu")
+    assert_close(r["y_out"], r["y_ref"], tol_of(cfg, TIGHT_ATTN), f"gelu layer {name}")
+    for got, ref_s, k, bound in r["sets"]:
+        check_sets_certified(got, ref_s, k, True, bound, f"gelu {name} next sets")
 
 
 def test_decode_layer_last_layer_and_alias():
