@@ -187,6 +187,21 @@ def random_index_set(N: int, count: int, seed: int) -> torch.Tensor:
     return torch.sort(perm).values.to(torch.int32)
 
 
+E4M3_MAX = 448.0   # largest finite OCP fp8 E4M3 value
+
+
+def quantize_rows_e4m3(W: torch.Tensor):
+    """Weight-only fp8 input preparation: one float32 scale per row (last axis) so the
+    row's largest magnitude maps to 448, then each element rounded to the nearest
+    E4M3 value (ties to even, torch's float8_e4m3fn cast).  Returns (codes as uint8,
+    scales as float32) on W's device; an all-zero row gets scale 1."""
+    w = W.float()
+    amax = w.abs().amax(dim=-1)
+    scales = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    q = (w / scales.unsqueeze(-1)).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).contiguous(), scales.contiguous()
+
+
 def to_f64_numpy(t: torch.Tensor):
     """Exact widening of a host or device tensor (fp32 or bf16) to a float64 NumPy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()

@@ -37,7 +37,13 @@ Readings where the pages are silent (each is listed in the design notes):
 
 Array conventions: inputs are NumPy arrays in the storage layouts of
 ``contextual_sparsity_mlp_amd.synth``.  Floating arrays may be float32 or float64;
-a uint16 array is read as bfloat16 bit patterns and widened exactly (bits << 16).
+a uint16 array is read as bfloat16 bit patterns and widened exactly (bits << 16);
+weight-only fp8 matrices come as ``Fp8Rows`` (E4M3 codes and one scale per row),
+widened exactly to scale * value.  The pages endorse weight-only quantization for
+decode without fixing a format (the Deja Vu page, section 1, checks the method's
+compatibility with quantization; the survey page's quantization section credits
+weight-only quantization with faster decoding because fewer weight bytes leave
+HBM); the reading here is the OCP E4M3 format with a per-row scale.
 Rows are gathered before widening, so a full OPT-175B-shaped layer needs only its
 selected rows in float64.
 """
@@ -50,8 +56,41 @@ import numpy as np
 # --------------------------------------------------------------------------- #
 
 
+def decode_e4m3(codes) -> np.ndarray:
+    """Value of fp8 E4M3 codes (the OCP 8-bit floating-point format: sign, 4 exponent
+    bits with bias 7, 3 mantissa bits; exponent field 0 is subnormal, m/8 * 2^-6;
+    S.1111.111 is NaN; no infinities), exactly, as float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = sign * val
+    return np.where((e == 15) & (c & 0x7 == 7), np.nan, val)
+
+
+class Fp8Rows:
+    """Weight-only fp8 storage: codes [..., d] (uint8, E4M3) with one scale per row
+    ([...], float); element = scale[row] * decode(code).  Indexing gathers rows."""
+
+    def __init__(self, codes, scales):
+        self.codes = np.asarray(codes, dtype=np.uint8)
+        self.scales = np.asarray(scales)
+        assert self.codes.shape[:-1] == self.scales.shape
+
+    def __getitem__(self, idx):
+        return Fp8Rows(self.codes[idx], self.scales[idx])
+
+    @property
+    def shape(self):
+        return self.codes.shape
+
+
 def widen(a) -> np.ndarray:
-    """Exact value of a stored array as float64 (bf16 bit patterns: bits << 16)."""
+    """Exact value of a stored array as float64 (bf16 bit patterns: bits << 16; fp8
+    rows: scale * decoded code)."""
+    if isinstance(a, Fp8Rows):
+        return decode_e4m3(a.codes) * widen(a.scales)[..., None]
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -62,7 +101,10 @@ def widen(a) -> np.ndarray:
 
 def rows(W, idx) -> np.ndarray:
     """Gather rows ``idx`` (first axis) of a stored array, then widen them."""
-    return widen(np.asarray(W)[np.asarray(idx, dtype=np.int64)])
+    idx = np.asarray(idx, dtype=np.int64)
+    if isinstance(W, Fp8Rows):
+        return widen(W[idx])
+    return widen(np.asarray(W)[idx])
 
 
 def as_set(S) -> np.ndarray:
@@ -200,8 +242,8 @@ def sparse_mha(y, Wq, Wo, K, V, S_A, scale: float = 1.0) -> np.ndarray:
     B, d = y.shape
     out = np.zeros((B, d), dtype=np.float64)
     for i in as_set(S_A):
-        WQ_i = widen(np.asarray(Wq)[i]).T
-        WO_i = widen(np.asarray(Wo)[i])
+        WQ_i = rows(Wq, [i])[0].T
+        WO_i = rows(Wo, [i])[0]
         for b in range(B):
             H = head_output(y[b], WQ_i, widen(np.asarray(K)[b, i]), widen(np.asarray(V)[b, i]),
                             scale)

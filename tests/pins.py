@@ -322,6 +322,59 @@ def rel_diff(a, b):
     return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) / max(1e-300, float(np.max(np.abs(b))))
 
 
+# Weight-only fp8 (E4M3 codes with one scale per row).  Independent references:
+# torch's float8_e4m3fn decoder for all 256 codes, and values of the OCP format
+# worked out by hand from its definition (bias 7, 3 mantissa bits, subnormals at
+# exponent field 0, S.1111.111 = NaN, largest finite 448).
+E4M3_HAND = {0x00: 0.0, 0x80: -0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+             0x38: 1.0, 0x3C: 1.5, 0xB0: -0.5, 0x7E: 448.0, 0xFE: -448.0, 0x77: 240.0}
+
+
+def _torch_e4m3_table():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def check_e4m3_decode(O):
+    got = O.decode_e4m3(np.arange(256, dtype=np.uint8))
+    ref = _torch_e4m3_table()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "E4M3 NaN codes"
+    assert np.array_equal(got[~nan], ref[~nan]), "E4M3 decode vs torch float8_e4m3fn"
+    for c, v in E4M3_HAND.items():
+        g = float(O.decode_e4m3(np.array([c], dtype=np.uint8))[0])
+        assert g == v and np.signbit(g) == np.signbit(v), f"E4M3 code {c:#04x}: {g} vs {v}"
+    assert np.isnan(O.decode_e4m3(np.array([0x7F, 0xFF], dtype=np.uint8))).all()
+
+
+def _fp8_rows(seed, shape):
+    """Random fp8 row storage (no NaN codes) and its dense value, built row by row
+    from torch's decoder: (codes, scales, dense float64)."""
+    r = _rng(seed)
+    codes = r.integers(0, 256, size=shape).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3A
+    scales = r.uniform(0.001, 0.01, size=shape[:-1])
+    table = _torch_e4m3_table()
+    dense = np.zeros(shape)
+    for ix in np.ndindex(*shape[:-1]):
+        dense[ix] = scales[ix] * table[codes[ix]]
+    return codes, scales, dense
+
+
+def check_fp8_rows_mlp_mha(O):
+    y = _rng(20).standard_normal((2, 32))
+    c1, s1, W1 = _fp8_rows(21, (40, 32))
+    c2, s2, W2 = _fp8_rows(22, (40, 32))
+    S = [0, 5, 17, 39]
+    assert_close(O.sparse_mlp(y, O.Fp8Rows(c1, s1), O.Fp8Rows(c2, s2), S),
+                 O.sparse_mlp(y, W1, W2, S), 1e-13, "fp8 rows mlp vs dense dequantized")
+    cq, sq, Wq = _fp8_rows(23, (3, 4, 32))
+    co, so, Wo = _fp8_rows(24, (3, 4, 32))
+    r = _rng(25)
+    K, V = r.standard_normal((2, 3, 5, 4)), r.standard_normal((2, 3, 5, 4))
+    assert_close(O.sparse_mha(y, O.Fp8Rows(cq, sq), O.Fp8Rows(co, so), K, V, [0, 2]),
+                 O.sparse_mha(y, Wq, Wo, K, V, [0, 2]), 1e-13, "fp8 rows mha vs dense dequantized")
+
+
 # --------------------------------------------------------------------------- #
 # A4 sparse MHA                                                               #
 # --------------------------------------------------------------------------- #
@@ -451,7 +504,7 @@ ALL_CHECKS = [
     check_mlp_dense_library, check_mlp_empty_and_additive, check_mlp_relu_support,
     check_mlp_loops, check_mlp_set_order_irrelevant,
     check_gelu_values, check_mlp_gelu_dense_library, check_mlp_gelu_loops_and_additive,
-    check_layer_gelu,
+    check_layer_gelu, check_e4m3_decode, check_fp8_rows_mlp_mha,
     check_mha_dense_library, check_mha_empty_and_additive, check_head_closed_forms,
     check_head_mean_shift, check_layer_composition, check_stack_lookahead,
 ]

@@ -166,6 +166,30 @@ def _widen_wrong_shift(a):
     return a.astype(np.float64)
 
 
+def _e4m3_bias8(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -7, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+    return np.where((e == 15) & (c & 0x7 == 7), np.nan, sign * val)
+
+
+def _e4m3_no_subnormals(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = (1.0 + m / 8.0) * np.exp2(e - 7.0)
+    return np.where((e == 15) & (c & 0x7 == 7), np.nan, sign * val)
+
+
+def _widen_fp8_no_scale(a):
+    if isinstance(a, O.Fp8Rows):
+        return O.decode_e4m3(a.codes)
+    return O.widen(a)
+
+
 MUTANTS = {
     "mlp without ReLU": dict(sparse_mlp=_mlp_no_relu),
     "mlp W1/W2 swapped": dict(sparse_mlp=_mlp_swapped),
@@ -189,6 +213,9 @@ MUTANTS = {
     "scores transposed factor": dict(predict_scores=_scores_transposed_A),
     "union as intersection": dict(select_sets=_union_as_intersection),
     "bf16 widening wrong": dict(widen=_widen_wrong_shift),
+    "e4m3 exponent bias 8": dict(decode_e4m3=_e4m3_bias8),
+    "e4m3 without subnormals": dict(decode_e4m3=_e4m3_no_subnormals),
+    "fp8 rows ignore the scale": dict(widen=_widen_fp8_no_scale),
     "layer predicts from output": dict(decode_layer=_layer_predict_from_output),
     "layer drops residual": dict(decode_layer=_layer_no_residual),
     "layer drops attention": dict(decode_layer=_layer_no_mha),
