@@ -84,6 +84,9 @@ def main():
                     help="run one plain 1 GiB device copy first (counter calibration)")
     ap.add_argument("--lookahead-only", action="store_true",
                     help="skip the per-launch event pass and the sparse-only pass")
+    ap.add_argument("--wdt", choices=("bf16", "fp8"), default="bf16",
+                    help="selected weights (W1, W2, W^Q, W^O): bf16, or weight-only fp8 E4M3 "
+                         "with per-row scales (predictor factors and KV stay bf16)")
     ap.add_argument("--act", choices=("relu", "gelu"), default="relu",
                     help="sigma of the MLP (OPT uses ReLU; GeLU is the page's other choice)")
     args = ap.parse_args()
@@ -124,12 +127,25 @@ def main():
     log(f"generating {R} replicas of the c4 layer (batch {B}) on the GPU")
     layers, ys = [], []
     for l in range(R):
-        layers.append(synth.make_layer(cfg, dev, layer=l, batch=B))
+        Lt = synth.make_layer(cfg, dev, layer=l, batch=B)
+        if args.wdt == "fp8":
+            # weight-only fp8 input preparation: E4M3 codes with one fp32 scale per row
+            for k in ("W1t", "W2t", "Wq", "Wo"):
+                codes, sc = synth.quantize_rows_e4m3(getattr(Lt, k))
+                setattr(Lt, k, codes)
+                Lt.extra[k + "_scale"] = sc
+        layers.append(Lt)
         ys.append(synth.make_y(cfg, dev, layer=l, batch=B))
     torch.cuda.synchronize()
+    def row_scales(L):
+        if args.wdt != "fp8":
+            return None
+        return tuple(L.extra[k + "_scale"] for k in ("W1t", "W2t", "Wq", "Wo"))
+
     dvl = [dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, L.A_M, L.B_M, L.A_A, L.B_A,
                     k_m=k_m, k_a=k_a, scale=cfg.scale,
-                    act=dv.DV_ACT_GELU if args.act == "gelu" else dv.DV_ACT_RELU) for L in layers]
+                    act=dv.DV_ACT_GELU if args.act == "gelu" else dv.DV_ACT_RELU,
+                    row_scales=row_scales(L)) for L in layers]
 
     i32 = lambda n: torch.zeros(n, dtype=torch.int32, device=dev)  # noqa: E731
     sets = [dict(m=i32(cap_m), cm=i32(1), a=i32(cap_a), ca=i32(1)) for _ in range(2)]
@@ -179,7 +195,8 @@ def main():
     u_m = int(sets[0]["cm"].cpu()[0])
     u_a = int(sets[0]["ca"].cpu()[0])
     shape = dict(batch=B, d=cfg.d, F=cfg.F, h=cfg.h, dh=cfg.dh, n_ctx=cfg.n_ctx, r=cfg.r,
-                 u_m=u_m, u_a=u_a)
+                 u_m=u_m, u_a=u_a,
+                 **(dict(w_bytes=1, p_bytes=2, row_scale_bytes=4) if args.wdt == "fp8" else {}))
     full_bytes = acc.step_bytes(**shape)
     log(f"timing {args.steps} steps (|S_M|={u_m}, |S_A|={u_a})")
     ms_step, ev_step = timed(args.steps)
@@ -232,7 +249,7 @@ def main():
     cpu = None
     if args.cpu_layers > 0:
         cpu = cpu_baseline(args.cpu_layers, layers, ys, sets, cfg, B, u_m, u_a, full_bytes.total,
-                           args.act)
+                           args.act, args.wdt == "fp8")
 
     out = {
         "metric": METRIC,
@@ -246,10 +263,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "weights_dtype": "bf16",
+        "weights_dtype": ("fp8 e4m3 rows with fp32 row scales (predictor bf16)"
+                          if args.wdt == "fp8" else "bf16"),
         "data": "synthetic",
         "config": {"workload": f"opt-175b-shaped decode layer, batch {B}, look-ahead predictor"
-                               + (", GeLU MLP" if args.act == "gelu" else ""),
+                               + (", GeLU MLP" if args.act == "gelu" else "")
+                               + (", fp8 weights" if args.wdt == "fp8" else ""),
+                   "wdt": args.wdt,
                    "act": args.act,
                    "d": cfg.d, "F": cfg.F, "h": cfg.h, "dh": cfg.dh, "n_ctx": cfg.n_ctx,
                    "r": cfg.r, "batch": B, "k_m": k_m, "k_a": k_a, "U_M": u_m, "U_A": u_a,
@@ -275,7 +295,8 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(n_layers, layers, ys, sets, cfg, B, u_m, u_a, step_bytes_total, act="relu"):
+def cpu_baseline(n_layers, layers, ys, sets, cfg, B, u_m, u_a, step_bytes_total, act="relu",
+                 fp8=False):
     """The CPU oracle (float64 NumPy, as it stands) on host copies of replica 0."""
     import numpy as np
     import torch
@@ -292,6 +313,9 @@ def cpu_baseline(n_layers, layers, ys, sets, cfg, B, u_m, u_a, step_bytes_total,
     L, L1 = layers[0], layers[1 % len(layers)]
     layer_h = dict(W1t=host(L.W1t), W2t=host(L.W2t), Wq=host(L.Wq), Wo=host(L.Wo), K=host(L.K),
                    V=host(L.V), act=act)
+    if fp8:
+        for k in ("W1t", "W2t", "Wq", "Wo"):
+            layer_h[k] = O.Fp8Rows(layer_h[k], host(L.extra[k + "_scale"]))
     nxt_h = dict(A_M=host(L1.A_M), B_M=host(L1.B_M), A_A=host(L1.A_A), B_A=host(L1.B_A),
                  k_m=cfg.k_m, k_a=cfg.k_a, union=True)
     # replica 0's own sets, as the oracle would predict them from y_0

@@ -38,12 +38,18 @@ class StepBytes:
 
 
 def step_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
-               u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True) -> StepBytes:
-    mlp = u_m * 2 * d * w_bytes
-    attn_w = u_a * 2 * dh * d * w_bytes
+               u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True,
+               p_bytes: int | None = None, row_scale_bytes: int = 0) -> StepBytes:
+    """Algorithmic bytes of one step.  w_bytes per selected weight element (1 for
+    weight-only fp8, whose rows also carry row_scale_bytes of scale each); p_bytes per
+    predictor element (default w_bytes)."""
+    row = d * w_bytes + row_scale_bytes
+    mlp = u_m * 2 * row
+    attn_w = u_a * 2 * dh * row
     kv = batch * u_a * 2 * n_ctx * dh * kv_bytes
     io = 2 * batch * d * 4
-    pred = (2 * d * r + r * F + r * h) * w_bytes if with_predictor else 0
+    pb = w_bytes if p_bytes is None else p_bytes
+    pred = (2 * d * r + r * F + r * h) * pb if with_predictor else 0
     return StepBytes(mlp, attn_w, kv, io, pred)
 
 
@@ -56,7 +62,8 @@ def step_flops(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: in
 
 
 def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
-                u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True):
+                u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True,
+                p_bytes: int | None = None, row_scale_bytes: int = 0):
     """Bytes each launch of the decode layer must move.
 
     With the predictor (the look-ahead step), three launches:
@@ -72,12 +79,14 @@ def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: i
     Small intermediates handed between launches (row dots, q, head outputs, attention
     pieces, scores written: under 1 MB at batch 1) are not counted.
     """
-    p1 = u_m * d * w_bytes + u_a * dh * d * w_bytes + batch * d * 4
+    row = d * w_bytes + row_scale_bytes
+    pb = w_bytes if p_bytes is None else p_bytes
+    p1 = u_m * row + u_a * dh * row + batch * d * 4
     kv = batch * u_a * 2 * n_ctx * dh * kv_bytes
-    out = u_m * d * w_bytes + u_a * dh * d * w_bytes + 2 * batch * d * 4
+    out = u_m * row + u_a * dh * row + 2 * batch * d * 4
     if not with_predictor:
         return [p1, kv + out]
-    p1 += 2 * r * d * w_bytes
-    p2 = kv + (r * F + r * h) * w_bytes
+    p1 += 2 * r * d * pb
+    p2 = kv + (r * F + r * h) * pb
     p3 = out + batch * (F + h) * 4
     return [p1, p2, p3]

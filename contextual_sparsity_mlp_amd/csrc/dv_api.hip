@@ -34,8 +34,9 @@ int fail(int code, const char* fmt, ...) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
-size_t esize(dv_dtype t) { return t == DV_BF16 ? 2 : 4; }
+size_t esize(dv_dtype t) { return t == DV_FP8 ? 1 : (t == DV_BF16 ? 2 : 4); }
 bool valid_dtype(int t) { return t == DV_F32 || t == DV_BF16; }
+int wcode(dv_dtype t) { return t == DV_FP8 ? W_FP8 : (t == DV_BF16 ? W_BF16 : W_F32); }
 bool valid_act(int a) { return a == DV_ACT_RELU || a == DV_ACT_GELU; }
 int act_code(int a) { return a == DV_ACT_GELU ? A_GELU : A_RELU; }
 
@@ -115,7 +116,7 @@ int pick_bt(int batch) { return batch <= 1 ? 1 : (batch == 2 ? 2 : 4); }
 struct AxGeo { int vec, nslices, nbt, chunks_max; };
 AxGeo ax_geo(int batch, int ncols, long long row_stride, dv_dtype wdt, int cap_rows) {
   AxGeo g;
-  const int full = (wdt == DV_BF16) ? 8 : 4;
+  const int full = (wdt == DV_FP8) ? 16 : ((wdt == DV_BF16) ? 8 : 4);
   g.vec = (ncols % full == 0 && row_stride % full == 0) ? full : 1;
   g.nslices = cdiv(ncols, kAxSliceLanes * g.vec);
   const int bt = pick_bt(batch);
@@ -207,12 +208,12 @@ struct LayerWs {
   TopkWs tm, ta;
 };
 LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int cap_m, int cap_a,
-                   dv_dtype wdt) {
+                   dv_dtype wdt, dv_dtype pwdt) {
   LayerWs p; Ws w;
   cap_m = std::max(cap_m, 1);
   cap_a = std::max(cap_a, 1);
-  const AxGeo g_bm = ax_geo(batch, F, F, wdt, r);
-  const AxGeo g_ba = ax_geo(batch, h, h, wdt, r);
+  const AxGeo g_bm = ax_geo(batch, F, F, pwdt, r);
+  const AxGeo g_ba = ax_geo(batch, h, h, pwdt, r);
   const AxGeo g_wo = ax_geo(batch, d, d, wdt, cap_m + cap_a * dh);   // W2 and W^O rows
   p.t_attn = batch * cap_a;
   p.t_bm = (int)ax_tickets(g_bm);
@@ -258,9 +259,10 @@ RowList make_list(const int32_t* idx, const int32_t* count, int host_count, int 
 }
 
 void add_rowdot(RowdotTask& T, const void* W, long long stride, dv_dtype wdt, RowList L, float* out,
-                int out_ld) {
+                int out_ld, const float* scale = nullptr) {
+  T.seg_scale[T.nseg] = scale;
   RowdotSeg& S = T.seg[T.nseg++];
-  S.W = W; S.row_stride = stride; S.wdt = (wdt == DV_BF16) ? W_BF16 : W_F32;
+  S.W = W; S.row_stride = stride; S.wdt = wcode(wdt);
   S.rows = L; S.out = out; S.out_ld = out_ld; S.cap = L.host_count * L.expand;
 }
 
@@ -284,12 +286,15 @@ void add_axpy2(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype
                const float* coef, int coef_ld, int act, const void* W2, RowList L2,
                const float* coef2, int coef2_ld, int act2, int ncols, float* partial,
                uint32_t* tickets, float* out, int out_ld, const float* add0, const float* add1,
-               int add_ld, int accumulate, int target_blocks) {
+               int add_ld, int accumulate, int target_blocks, const float* scale = nullptr,
+               const float* scale2 = nullptr) {
+  T.seg_scale[T.nseg][0] = scale;
+  T.seg_scale[T.nseg][1] = scale2;
   AxpySeg& S = T.seg[T.nseg];
   int cap_rows = L.host_count * L.expand + (W2 ? L2.host_count * L2.expand : 0);
   cap_rows = std::max(1, cap_rows);
   const AxGeo g = ax_geo(batch, ncols, stride, wdt, cap_rows);
-  S.W = W; S.row_stride = stride; S.wdt = (wdt == DV_BF16) ? W_BF16 : W_F32;
+  S.W = W; S.row_stride = stride; S.wdt = wcode(wdt);
   S.rows = L; S.coef = coef; S.coef_ld = coef_ld; S.act = act; S.ncols = ncols;
   S.W2 = W2; S.rows2 = L2; S.coef2 = coef2; S.coef2_ld = coef2_ld; S.act2 = act2;
   S.vec = g.vec; S.nslices = g.nslices; S.nbt = g.nbt;
@@ -323,8 +328,11 @@ int resident_blocks() { return 8 * device_cus(); }
 // Row-sum grid of a launch that runs the segment alone: six blocks per CU.
 int default_axpy_blocks() { return 6 * device_cus(); }
 
-int axpy_lds(int bt) {
-  return std::max((kAxpyTileRows * (1 + bt) + kAxGroups * bt * kAxSliceLanes * 8) * 4,
+// LDS of a row-sum block: row ids and coefficients of a tile, and the row groups'
+// column sums (kAxSliceLanes * vec columns per slice; vec 16 for fp8 rows), or the
+// histogram of a row sum that builds one.
+int axpy_lds(int bt, int vec = 8) {
+  return std::max((kAxpyTileRows * (1 + bt) + kAxGroups * bt * kAxSliceLanes * vec) * 4,
                   (16 + kHistBins) * 4);
 }
 
@@ -420,7 +428,7 @@ extern "C" {
 
 const char* dv_last_error(void) { return g_err.c_str(); }
 
-int dv_version(void) { return 101; }
+int dv_version(void) { return 102; }
 
 static size_t ws_bytes_for(int op, const dv_shape* s, dv_dtype wdt) {
   const int B = s->batch;
@@ -430,8 +438,10 @@ static size_t ws_bytes_for(int op, const dv_shape* s, dv_dtype wdt) {
     case DV_OP_SPARSE_MLP: return plan_mlp(B, s->d, s->max_count_m, wdt).total;
     case DV_OP_SPARSE_MHA: return plan_mha(B, s->d, s->dh, s->n_ctx, s->max_count_a, wdt).total;
     default:
+      // (fp8 weights need no more: their row sums have fewer slices, the predictor
+      // factors are bf16 or fp32)
       return plan_layer(B, s->d, s->F, s->h, s->dh, s->n_ctx, s->r, s->max_count_m, s->max_count_a,
-                        wdt).total;
+                        wdt, wdt).total;
   }
 }
 
@@ -477,6 +487,8 @@ int dv_predict(const float* y, int batch, int d, const void* A, const void* Bm, 
   CHECK_PTR(y); CHECK_PTR(A); CHECK_PTR(Bm); CHECK_PTR(scores);
   if (batch <= 0) return fail(DV_EINVAL, "%s: batch = %d", fn, batch);
   if (r <= 0 || N <= 0) return fail(DV_EINVAL, "%s: r = %d, N = %d", fn, r, N);
+  if (wdt == DV_FP8)
+    return fail(DV_EUNSUPPORTED, "%s: fp8 weights are taken by dv_decode_layer only", fn);
   if (!valid_dtype(wdt)) return fail(DV_EINVAL, "%s: bad dtype %d", fn, (int)wdt);
   if (int e = check_d(fn, d)) return e;
   CHECK_ALIGN(y); CHECK_ALIGN(A); CHECK_ALIGN(Bm); CHECK_ALIGN(scores);
@@ -540,6 +552,8 @@ int dv_sparse_mlp(const float* y, int batch, int d, const void* W1t, const void*
   if (batch <= 0) return fail(DV_EINVAL, "%s: batch = %d", fn, batch);
   if (F <= 0) return fail(DV_EINVAL, "%s: F = %d", fn, F);
   if (max_count < 0 || max_count > F) return fail(DV_EINVAL, "%s: max_count = %d not in [0, F]", fn, max_count);
+  if (wdt == DV_FP8)
+    return fail(DV_EUNSUPPORTED, "%s: fp8 weights are taken by dv_decode_layer only", fn);
   if (!valid_dtype(wdt)) return fail(DV_EINVAL, "%s: bad dtype %d", fn, (int)wdt);
   if (!valid_act(act)) return fail(DV_EINVAL, "%s: bad activation %d", fn, act);
   if (int e = check_d(fn, d)) return e;
@@ -579,6 +593,8 @@ int dv_sparse_mha(const float* y, int batch, int d, int h, int dh, const void* W
   if (h <= 0) return fail(DV_EINVAL, "%s: h = %d", fn, h);
   if (int e = check_nctx(fn, n_ctx)) return e;
   if (max_count < 0 || max_count > h) return fail(DV_EINVAL, "%s: max_count = %d not in [0, h]", fn, max_count);
+  if (wdt == DV_FP8)
+    return fail(DV_EUNSUPPORTED, "%s: fp8 weights are taken by dv_decode_layer only", fn);
   if (!valid_dtype(wdt) || !valid_dtype(kvdt)) return fail(DV_EINVAL, "%s: bad dtype", fn);
   if (!(scale == scale)) return fail(DV_EINVAL, "%s: scale is NaN", fn);
   if (int e = check_d(fn, d)) return e;
@@ -630,8 +646,14 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   const int d = L->d, F = L->F, h = L->h, dh = L->dh, n = L->n_ctx;
   if (F <= 0 || h <= 0) return fail(DV_EINVAL, "%s: F = %d, h = %d", fn, F, h);
   if (int e = check_nctx(fn, n)) return e;
-  if (!valid_dtype(L->wdt) || !valid_dtype(L->kvdt)) return fail(DV_EINVAL, "%s: bad dtype", fn);
+  if (!(valid_dtype(L->wdt) || L->wdt == DV_FP8) || !valid_dtype(L->kvdt))
+    return fail(DV_EINVAL, "%s: bad dtype", fn);
   if (!valid_act(L->act)) return fail(DV_EINVAL, "%s: bad activation %d", fn, L->act);
+  if (L->wdt == DV_FP8) {
+    CHECK_PTR(L->W1s); CHECK_PTR(L->W2s); CHECK_PTR(L->Wqs); CHECK_PTR(L->Wos);
+    CHECK_ALIGN(L->W1s); CHECK_ALIGN(L->W2s); CHECK_ALIGN(L->Wqs); CHECK_ALIGN(L->Wos);
+    if (L->d % 16 != 0) return fail(DV_EALIGN, "%s: fp8 rows need d %% 16 == 0 (d = %d)", fn, L->d);
+  }
   if (!(L->scale == L->scale)) return fail(DV_EINVAL, "%s: scale is NaN", fn);
   if (int e = check_d(fn, d)) return e;
   if (int e = check_dh(fn, dh)) return e;
@@ -651,7 +673,7 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     CHECK_ALIGN(next_count_a);
     CHECK_ALIGN(nx->A_M); CHECK_ALIGN(nx->B_M); CHECK_ALIGN(nx->A_A); CHECK_ALIGN(nx->B_A);
     if (nx->d != d) return fail(DV_EINVAL, "%s: next->d = %d differs from d = %d", fn, nx->d, d);
-    if (nx->wdt != L->wdt) return fail(DV_EUNSUPPORTED, "%s: next layer weight dtype differs", fn);
+    if (!valid_dtype(nx->pwdt)) return fail(DV_EINVAL, "%s: bad predictor dtype %d", fn, (int)nx->pwdt);
     r = nx->r; Fn = nx->F; hn = nx->h; km = nx->k_m; ka = nx->k_a;
     if (r <= 0 || Fn <= 0 || hn <= 0) return fail(DV_EINVAL, "%s: next r/F/h", fn);
     if (km < 0 || km > Fn || ka < 0 || ka > hn)
@@ -660,8 +682,10 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
       return fail(DV_EUNSUPPORTED, "%s: next F = %d exceeds %d", fn, Fn, kMaxSegs * kSegElems);
   }
   const dv_dtype wdt = L->wdt;
+  const dv_dtype pwdt = nx ? nx->pwdt : DV_BF16;   // the next layer's predictor factors
+  const bool fp8 = wdt == DV_FP8;
   const LayerWs P = plan_layer(batch, d, std::max(F, Fn), std::max(h, hn), dh, n, r, max_count_m,
-                               max_count_a, wdt);
+                               max_count_a, wdt, pwdt);
   if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
 
   char* w = static_cast<char*>(ws);
@@ -681,23 +705,25 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   // S_A, and the next layer's predictor factors A_M, A_A); clears the counters and
   // histograms the later phases use.
   PhaseArgs a1 = zero_args();
-  add_rowdot(a1.rowdot, L->W1t, d, wdt, LM, fp(P.a), cap_m);
-  add_rowdot(a1.rowdot, L->Wq, d, wdt, LQ, fp(P.q), cap_a * dh);
+  add_rowdot(a1.rowdot, L->W1t, d, wdt, LM, fp(P.a), cap_m, fp8 ? L->W1s : nullptr);
+  add_rowdot(a1.rowdot, L->Wq, d, wdt, LQ, fp(P.q), cap_a * dh, fp8 ? L->Wqs : nullptr);
   if (nx) {
-    add_rowdot(a1.rowdot, nx->A_M, d, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r);
-    add_rowdot(a1.rowdot, nx->A_A, d, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r);
+    add_rowdot(a1.rowdot, nx->A_M, d, pwdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r);
+    add_rowdot(a1.rowdot, nx->A_A, d, pwdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r);
   }
   finish_rowdot(a1.rowdot, y_in, batch, d, up(P.zero), P.zero_words);
-  if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
+  if (int e = launch(T_ROWDOT | (fp8 ? T_FP8 : 0), bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot),
+                     stream, fn))
+    return e;
 
   // After the row dots, the rest of the layer: attention over the cache for S_A; one
   // row sum y_out = y_in + sum_{S_M} ReLU(a) W2 rows + sum_{S_A} o W^O rows; and for
   // the next layer its predictor scores (with top-digit histograms) and top-k.
-  const long long wb = (wdt == DV_BF16) ? 2 : 4;
   auto add_out = [&](AxpyTask& T, int target, const float* coef2, int nsplit) {
     add_axpy2(T, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, act_code(L->act), L->Wo, LQ, coef2,
               cap_a * dh, A_NONE,
-              d, fp(P.p_wo), t_wo, y_out, d, y_in, nullptr, d, 0, target);
+              d, fp(P.p_wo), t_wo, y_out, d, y_in, nullptr, d, 0, target,
+              fp8 ? L->W2s : nullptr, fp8 ? L->Wos : nullptr);
     T.seg[T.nseg - 1].coef2_nsplit = nsplit;
   };
 
@@ -705,7 +731,7 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   // row-sum block streams its W2 rows, then waits for the attention blocks (which come
   // first in block order) and combines their split pieces into the head outputs as it
   // stages the coefficients of its W^O rows.  The attention hides under the W2 stream.
-  if (!nx && max_count_a > 0) {
+  if (!nx && max_count_a > 0 && !fp8) {
     PhaseArgs f = zero_args();
     setup_attn(f.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n, dh, LH, L->scale,
                fp(P.part), nullptr, nullptr, 0, 1);
@@ -734,10 +760,10 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   a2.b_attn = 0;
   a2.b_axpy = a2.attn.blocks;
   if (nx) {
-    add_axpy(a2.axpy, batch, nx->B_M, Fn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r,
+    add_axpy(a2.axpy, batch, nx->B_M, Fn, pwdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r,
              0, Fn, fp(P.p_bm), t_bm, fp(P.sm), Fn, nullptr, nullptr, 0, 0, default_axpy_blocks());
     a2.axpy.seg[a2.axpy.nseg - 1].hist = up(P.hist_m);
-    add_axpy(a2.axpy, batch, nx->B_A, hn, wdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r,
+    add_axpy(a2.axpy, batch, nx->B_A, hn, pwdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r,
              0, hn, fp(P.p_ba), t_ba, fp(P.sa), hn, nullptr, nullptr, 0, 0, default_axpy_blocks());
     a2.axpy.seg[a2.axpy.nseg - 1].hist = up(P.hist_a);
   }
@@ -752,7 +778,7 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   PhaseArgs a3 = zero_args();
   add_out(a3.axpy, default_axpy_blocks(), fp(P.o), 0);
   a3.axpy.batch = batch;
-  int flags3 = T_AXPY;
+  int flags3 = T_AXPY | (fp8 ? T_FP8 : 0);
   if (nx) {
     TopkTask& tk = a3.topk;
     tk.np = 2;
@@ -765,7 +791,7 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     a3.b_topk = 0;
     a3.b_axpy = tk.blocks;
   }
-  const int lds3 = std::max(axpy_lds(bt), nx ? classify_lds() : 0);
+  const int lds3 = std::max(axpy_lds(bt, fp8 ? 16 : 8), nx ? classify_lds() : 0);
   if (int e = launch(flags3, bt, a3, a3.topk.blocks + a3.axpy.blocks, lds3, stream, fn)) return e;
   return DV_OK;
 }

@@ -37,7 +37,7 @@ constexpr int kResolveWords = 1536;      // bitmask words a resolving block keep
 constexpr int kMaxSegs = 256;            // classify segments per row (N <= 524288)
 constexpr int kWordsPerThread = 4;       // bitmask words per thread when compacting
 
-enum : int { W_F32 = 0, W_BF16 = 1 };
+enum : int { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };   // W_FP8: E4M3 codes, one scale per row
 enum : int { A_NONE = 0, A_RELU = 1, A_GELU = 2 };   // row-sum coefficient activations
 
 // A logical list of rows: slot s < count expands to rows idx[s]*expand + e, e < expand.
@@ -61,6 +61,7 @@ struct RowdotSeg {
 
 struct RowdotTask {
   RowdotSeg seg[kMaxSeg];
+  const float* seg_scale[kMaxSeg];   // W_FP8 segments: scale of row (item*expand + e)
   int nseg;
   const float* y;          // [batch][d]
   int batch, d;
@@ -109,6 +110,10 @@ struct AxpySeg {
 
 struct AxpyTask {
   AxpySeg seg[kMaxSeg];
+  // W_FP8 segments: per-row scales of the first / second source (row item*expand + e),
+  // folded into the coefficients; kept apart from AxpySeg, whose by-value selection
+  // costs scalar registers in every launch mix
+  const float* seg_scale[kMaxSeg][2];
   int nseg;
   int batch;
   int blocks;
@@ -174,8 +179,10 @@ struct ZeroTask {
 
 // T_WAIT: the row sums of the launch may wait for in-launch producers before their
 // second source (see AxpySeg::wait_ctr) and combine attention pieces while staging.
+// T_FP8: the row dots and row sums of the launch may hold fp8 rows; the launches
+// without it carry no fp8 code, which keeps their bf16 loops as tight as before.
 enum : int { T_ROWDOT = 1, T_ATTN = 2, T_AXPY = 4, T_HIST = 8, T_CLASSIFY = 16, T_WAIT = 32,
-             T_ZERO = 64 };
+             T_ZERO = 64, T_FP8 = 128 };
 
 struct PhaseArgs {
   RowdotTask rowdot;

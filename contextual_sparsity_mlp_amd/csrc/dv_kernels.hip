@@ -59,6 +59,20 @@ __device__ __forceinline__ void unpack8(const uint4& x, float (&f)[8]) {
   f[6] = bf16_lo(x.w); f[7] = bf16_hi(x.w);
 }
 
+// 16 fp8 E4M3 codes (one 16-byte load, byte k = element k) to floats; the hardware
+// conversion decodes two codes per instruction.
+__device__ __forceinline__ void unpack4_fp8(uint32_t w, float* f) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
+}
+__device__ __forceinline__ void unpack16_fp8(const uint4& x, float (&f)[16]) {
+  unpack4_fp8(x.x, f);
+  unpack4_fp8(x.y, f + 4);
+  unpack4_fp8(x.z, f + 8);
+  unpack4_fp8(x.w, f + 12);
+}
+
 // Streaming loads of weights and cache rows: each byte is read once per call, so
 // the loads are marked non-temporal (they bypass reuse in the caches).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -216,6 +230,11 @@ __device__ __forceinline__ RowdotSeg rd_seg(const RowdotTask& T, int s) {
     default: return T.seg[3];
   }
 }
+// fp8 row scales of segment s (kept outside RowdotSeg, whose by-value selection the
+// compiler keeps in registers only while the struct stays this size)
+__device__ __forceinline__ const float* rd_scale(const RowdotTask& T, int s) {
+  return s == 0 ? T.seg_scale[0] : s == 1 ? T.seg_scale[1] : s == 2 ? T.seg_scale[2] : T.seg_scale[3];
+}
 
 // acc[b] += row . y_b for the lane's share of one bf16 row of d elements.
 template <int BT, int U>
@@ -254,6 +273,42 @@ __device__ __forceinline__ void rowdot_bf16(const uint4* __restrict__ rp, const 
 }
 
 template <int BT, int U>
+__device__ __forceinline__ void rowdot_fp8(const uint4* __restrict__ rp, const float* ylds, int d,
+                                           int nb, int lane, float (&acc)[BT]) {
+  const int nv = d >> 4;  // 16-byte vectors (16 codes) in the row
+  for (int v0 = 0; v0 < nv; v0 += 64 * U) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * 64 + lane;
+      w[u] = (v < nv) ? ld_stream(rp + v) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * 64 + lane;
+      if (v < nv) {
+        float f[16];
+        unpack16_fp8(w[u], f);
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          if (b < nb) {
+            const float4* yp = reinterpret_cast<const float4*>(ylds + b * d + v * 16);
+            float a = acc[b];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 yq = yp[q];
+              a = fmaf(f[4 * q + 0], yq.x, a); a = fmaf(f[4 * q + 1], yq.y, a);
+              a = fmaf(f[4 * q + 2], yq.z, a); a = fmaf(f[4 * q + 3], yq.w, a);
+            }
+            acc[b] = a;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BT, int U>
 __device__ __forceinline__ void rowdot_f32(const float4* __restrict__ rp, const float* ylds, int d,
                                            int nb, int lane, float (&acc)[BT]) {
   const int nv = d >> 2;
@@ -283,7 +338,7 @@ __device__ __forceinline__ void rowdot_f32(const float4* __restrict__ rp, const 
   }
 }
 
-template <int BT>
+template <int BT, bool FP8>
 __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Counters and histograms used by later launches of the same call start at zero.
@@ -322,12 +377,20 @@ __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float*
       float acc[BT];
 #pragma unroll
       for (int b = 0; b < BT; ++b) acc[b] = 0.f;
+      float rscale = 1.f;   // fp8 rows: the row's scale
       if ((unsigned)item < (unsigned)S.rows.items) {
         const long long row = (long long)item * ex + e;
         if (S.wdt == W_BF16) {
           const uint4* rp = reinterpret_cast<const uint4*>(
               static_cast<const uint16_t*>(S.W) + row * S.row_stride);
           rowdot_bf16<BT, 24>(rp, lds, d, nb, lane, acc);
+        } else if (FP8 && S.wdt == W_FP8) {
+          if constexpr (FP8) {
+            const uint4* rp = reinterpret_cast<const uint4*>(
+                static_cast<const uint8_t*>(S.W) + row * S.row_stride);
+            rowdot_fp8<BT, 12>(rp, lds, d, nb, lane, acc);
+            rscale = rd_scale(T, s)[row];
+          }
         } else {
           const float4* rp = reinterpret_cast<const float4*>(
               static_cast<const float*>(S.W) + row * S.row_stride);
@@ -335,7 +398,7 @@ __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float*
         }
       }
 #pragma unroll
-      for (int b = 0; b < BT; ++b) acc[b] = wave_sum(acc[b]);
+      for (int b = 0; b < BT; ++b) acc[b] = FP8 ? wave_sum(acc[b]) * rscale : wave_sum(acc[b]);
       if (lane == 0) {
 #pragma unroll
         for (int b = 0; b < BT; ++b)
@@ -367,6 +430,8 @@ __device__ __forceinline__ void load_cols(const void* W, long long off, float (&
     unpack8(ld_stream(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + off)), f);
 #pragma unroll
     for (int v = 0; v < 8; ++v) w[v] = f[v];
+  } else if constexpr (WT == W_FP8 && VEC == 16) {
+    unpack16_fp8(ld_stream(reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(W) + off)), w);
   } else if constexpr (WT == W_F32 && VEC == 4) {
     const float4 x = ld_stream(reinterpret_cast<const float4*>(static_cast<const float*>(W) + off));
     w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
@@ -392,9 +457,38 @@ __device__ __forceinline__ void hist_flush_one(float score, bool active, uint32_
   }
 }
 
+// U rows of one fp8 row group: the 16-byte loads (16 columns per lane) are issued
+// together and stay packed until each row is decoded and accumulated, so the row
+// group keeps U rows in flight within the register budget.  `at(row)` gives a row's
+// 16 bytes for this lane.
+template <int BT, int U, class At>
+__device__ __forceinline__ void fp8_rows(const int* lrow, const float* lcoef, int i0, int tn,
+                                         At at, float (&acc)[BT][16]) {
+  uint4 wr[U];
+  float c[U][BT];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = i0 + u * kAxGroups;
+    const int row = (i < tn) ? lrow[i] : -1;
+    wr[u] = (row >= 0) ? ld_stream(at(row)) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int b = 0; b < BT; ++b) c[u][b] = (i < tn) ? lcoef[b * kAxpyTile + i] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float f[16];
+    unpack16_fp8(wr[u], f);
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[b][v] = fmaf(c[u][b], f[v], acc[b][v]);
+  }
+}
+
 // One block: a slice of kAxSliceLanes*VEC output columns and a chunk of the row list.
 template <int BT, int VEC, int WT, bool WAIT>
-__device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, float* lds) {
+__device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, const float* sc2,
+                                           int lb, int batch, float* lds) {
   constexpr int U = 4;
   constexpr int SW = kAxSliceLanes * VEC;    // columns per slice
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -444,12 +538,14 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
         const float* cf = second ? S.coef2 : S.coef;
         const int cld = second ? S.coef2_ld : S.coef_ld;
         const int rl = second ? S.act2 : S.act;
+        const float* sc = second ? sc2 : sc1;
   #pragma unroll
         for (int b = 0; b < BT; ++b) {
           float c = 0.f;
           if (ok && b < nb) {
             c = cf[(size_t)(b0 + b) * cld + rr];
             c = activate(c, rl);
+            if constexpr (WT == W_FP8) c *= sc[item * ex + e];   // row scale folded in
           }
           lcoef[b * kAxpyTile + i] = c;
         }
@@ -457,6 +553,14 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
       __syncthreads();
       if (active) {
         for (int i0 = grp; i0 < tn; i0 += kAxGroups * U) {
+          if constexpr (WT == W_FP8) {
+            fp8_rows<BT, U>(lrow, lcoef, i0, tn, [&](int row) {
+              const void* W = (row & (1 << 30)) ? S.W2 : S.W;
+              return reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(W) +
+                  (long long)(row & ((1 << 30) - 1)) * S.row_stride + col0);
+            }, acc);
+            continue;
+          }
           float w[U][VEC];
           float c[U][BT];
   #pragma unroll
@@ -492,7 +596,7 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
     // one source's share of rows: coefficients staged in LDS a tile at a time, then the
     // row slices streamed by the row groups
     auto rows_of = [&](auto merge, const RowList& L, const void* W, const float* cf, int cld,
-                       int rl, bool coherent, int nsplit, int nr) {
+                       int rl, const float* sc, bool coherent, int nsplit, int nr) {
       constexpr bool kMerge = decltype(merge)::value;
       const int per = (nr + S.nchunks - 1) / S.nchunks;
       const int r0 = min(chunk * per, nr);
@@ -571,6 +675,7 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
                 c = coherent ? ld_dev(cp) : *cp;
               }
               c = activate(c, rl);
+              if constexpr (WT == W_FP8) c *= sc[item * ex + e];
             }
             lcoef[b * kAxpyTile + i] = c;
           }
@@ -578,6 +683,13 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
         __syncthreads();
         if (active) {
           for (int i0 = grp; i0 < tn; i0 += kAxGroups * U) {
+            if constexpr (WT == W_FP8) {
+              fp8_rows<BT, U>(lrow, lcoef, i0, tn, [&](int row) {
+                return reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(W) +
+                                                      (long long)row * S.row_stride + col0);
+              }, acc);
+              continue;
+            }
             float w[U][VEC];
             float c[U][BT];
   #pragma unroll
@@ -603,14 +715,14 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
         }
       }
     };
-    rows_of(std::false_type{}, S.rows, S.W, S.coef, S.coef_ld, S.act, false, 0, n1);
+    rows_of(std::false_type{}, S.rows, S.W, S.coef, S.coef_ld, S.act, sc1, false, 0, n1);
     if (n2 > 0) {
       if (S.wait_ctr) wait_count(S.wait_ctr, S.wait_target);
       if (S.coef2_nsplit > 0)
-        rows_of(std::true_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, true,
+        rows_of(std::true_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, sc2, true,
                 S.coef2_nsplit, n2);
       else
-        rows_of(std::false_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2,
+        rows_of(std::false_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, sc2,
                 S.wait_ctr != nullptr, 0, n2);
     }
   }
@@ -622,66 +734,86 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, int lb, int batch, 
 #pragma unroll
     for (int v = 0; v < VEC; ++v) red[(grp * BT + b) * SW + hl * VEC + v] = acc[b][v];
   __syncthreads();
+  // each thread finalises CPT output columns of the slice (2 for 16-column fp8 lanes)
+  constexpr int CPT = (SW + kThreads - 1) / kThreads;
   const size_t ncols = (size_t)S.ncols;
-  const int col = slice * SW + tid;
-  const bool cact = tid < SW && col < S.ncols;
-  float part[BT];
+  int colv[CPT];
+  bool cactv[CPT];
+  float part[CPT][BT];
 #pragma unroll
-  for (int b = 0; b < BT; ++b) {
-    float t = 0.f;
-    if (cact) {
+  for (int j = 0; j < CPT; ++j) {
+    const int cc = tid + j * kThreads;
+    colv[j] = slice * SW + cc;
+    cactv[j] = cc < SW && colv[j] < S.ncols;
 #pragma unroll
-      for (int g = 0; g < kAxGroups; ++g) t += red[(g * BT + b) * SW + tid];
+    for (int b = 0; b < BT; ++b) {
+      float t = 0.f;
+      if (cactv[j]) {
+#pragma unroll
+        for (int g = 0; g < kAxGroups; ++g) t += red[(g * BT + b) * SW + cc];
+      }
+      part[j][b] = t;
     }
-    part[b] = t;
   }
 
   if (S.nchunks > 1) {
     float* P = S.partial + ((size_t)(bti * S.nchunks + chunk) * BT) * ncols;
-    if (cact) {
 #pragma unroll
-      for (int b = 0; b < BT; ++b)
-        if (b < nb) st_dev(&P[b * ncols + col], part[b]);
+    for (int j = 0; j < CPT; ++j) {
+      if (cactv[j]) {
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+          if (b < nb) st_dev(&P[b * ncols + colv[j]], part[j][b]);
+      }
     }
     int* flag = reinterpret_cast<int*>(lds);
     if (!arrive_last(&S.tickets[bti * S.nslices + slice], (uint32_t)S.nchunks, flag)) return;
     const float* P0 = S.partial + (size_t)bti * S.nchunks * BT * ncols;
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      if (b < nb && cact) {
-        float v[kMaxChunks];
+    for (int j = 0; j < CPT; ++j) {
 #pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c)
-          v[c] = (c < S.nchunks) ? ld_dev(&P0[((size_t)c * BT + b) * ncols + col]) : 0.f;
-        float t = 0.f;
+      for (int b = 0; b < BT; ++b) {
+        if (b < nb && cactv[j]) {
+          float v[kMaxChunks];
 #pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c) t += v[c];
-        part[b] = t;
+          for (int c = 0; c < kMaxChunks; ++c)
+            v[c] = (c < S.nchunks) ? ld_dev(&P0[((size_t)c * BT + b) * ncols + colv[j]]) : 0.f;
+          float t = 0.f;
+#pragma unroll
+          for (int c = 0; c < kMaxChunks; ++c) t += v[c];
+          part[j][b] = t;
+        }
       }
     }
   }
 #pragma unroll
-  for (int b = 0; b < BT; ++b) {
-    if (b < nb && cact) {
-      const size_t bo = (size_t)(b0 + b);
-      float sum = part[b];
-      if (S.add1) sum = S.add1[bo * S.add_ld + col] + sum;
-      if (S.add0) sum = S.add0[bo * S.add_ld + col] + sum;
-      float* o = S.out + bo * S.out_ld + col;
-      if (S.accumulate) sum = *o + sum;
-      *o = sum;
-      part[b] = sum;
+  for (int j = 0; j < CPT; ++j) {
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      if (b < nb && cactv[j]) {
+        const size_t bo = (size_t)(b0 + b);
+        const int col = colv[j];
+        float sum = part[j][b];
+        if (S.add1) sum = S.add1[bo * S.add_ld + col] + sum;
+        if (S.add0) sum = S.add0[bo * S.add_ld + col] + sum;
+        float* o = S.out + bo * S.out_ld + col;
+        if (S.accumulate) sum = *o + sum;
+        *o = sum;
+        part[j][b] = sum;
+      }
     }
   }
-  if (S.hist) {
-    uint32_t* lh = reinterpret_cast<uint32_t*>(lds) + 16;
+  if constexpr (CPT == 1) {
+    if (S.hist) {
+      uint32_t* lh = reinterpret_cast<uint32_t*>(lds) + 16;
 #pragma unroll
-    for (int b = 0; b < BT; ++b)
-      if (b < nb) hist_flush_one(part[b], cact, lh, S.hist + (size_t)(b0 + b) * kHistBins);
+      for (int b = 0; b < BT; ++b)
+        if (b < nb) hist_flush_one(part[0][b], cactv[0], lh, S.hist + (size_t)(b0 + b) * kHistBins);
+    }
   }
 }
 
-template <int BT, bool WAIT>
+template <int BT, bool WAIT, bool FP8>
 __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds) {
   int s = 0;
 #pragma unroll
@@ -690,11 +822,18 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
   const AxpySeg S = ax_seg(T, s);
   const int lb = blk - S.block0;
   if (S.wdt == W_BF16) {
-    if (S.vec == 8) axpy_block<BT, 8, W_BF16, WAIT>(S, lb, T.batch, lds);
-    else axpy_block<BT, 1, W_BF16, WAIT>(S, lb, T.batch, lds);
+    if (S.vec == 8) axpy_block<BT, 8, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
+    else axpy_block<BT, 1, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
+  } else if (FP8 && S.wdt == W_FP8) {
+    // d % 16 == 0 (host check); fp8 layers never take the waiting single launch
+    if constexpr (FP8 && !WAIT) {
+      const float* const* sc = s == 0 ? T.seg_scale[0] : s == 1 ? T.seg_scale[1]
+                             : s == 2 ? T.seg_scale[2] : T.seg_scale[3];
+      axpy_block<BT, 16, W_FP8, false>(S, sc[0], sc[1], lb, T.batch, lds);
+    }
   } else {
-    if (S.vec == 4) axpy_block<BT, 4, W_F32, WAIT>(S, lb, T.batch, lds);
-    else axpy_block<BT, 1, W_F32, WAIT>(S, lb, T.batch, lds);
+    if (S.vec == 4) axpy_block<BT, 4, W_F32, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
+    else axpy_block<BT, 1, W_F32, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
   }
 }
 
@@ -1151,7 +1290,7 @@ __device__ __forceinline__ void phase_body(const PhaseArgs& a, float* lds) {
   }
   if constexpr ((FLAGS & T_ROWDOT) != 0) {
     if (blk >= a.b_rowdot && blk < a.b_rowdot + a.rowdot.blocks) {
-      rowdot_task<BT>(a.rowdot, blk - a.b_rowdot, lds);
+      rowdot_task<BT, (FLAGS & T_FP8) != 0>(a.rowdot, blk - a.b_rowdot, lds);
       return;
     }
   }
@@ -1171,7 +1310,7 @@ __device__ __forceinline__ void phase_body(const PhaseArgs& a, float* lds) {
   }
   if constexpr ((FLAGS & T_AXPY) != 0) {
     if (blk >= a.b_axpy && blk < a.b_axpy + a.axpy.blocks) {
-      axpy_task<BT, (FLAGS & T_WAIT) != 0>(a.axpy, blk - a.b_axpy, lds);
+      axpy_task<BT, (FLAGS & T_WAIT) != 0, (FLAGS & T_FP8) != 0>(a.axpy, blk - a.b_axpy, lds);
       return;
     }
   }
@@ -1206,7 +1345,7 @@ __global__ __launch_bounds__(kThreads) void rowdot_kernel(PhaseArgs a) {
 
 template <int FLAGS, int BT>
 static int launch_t(const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
-  if constexpr (FLAGS == T_ROWDOT)
+  if constexpr ((FLAGS & ~T_FP8) == T_ROWDOT)
     hipLaunchKernelGGL((rowdot_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
                        static_cast<hipStream_t>(stream), a);
   else if constexpr (BT == 1)
@@ -1234,6 +1373,10 @@ int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes,
     case T_ATTN | T_AXPY: return launch_bt<T_ATTN | T_AXPY>(bt, a, grid, lds_bytes, stream);
     case T_ATTN | T_AXPY | T_WAIT: return launch_bt<T_ATTN | T_AXPY | T_WAIT>(bt, a, grid, lds_bytes, stream);
     case T_AXPY | T_CLASSIFY: return launch_bt<T_AXPY | T_CLASSIFY>(bt, a, grid, lds_bytes, stream);
+    case T_ROWDOT | T_FP8: return launch_bt<T_ROWDOT | T_FP8>(bt, a, grid, lds_bytes, stream);
+    case T_AXPY | T_FP8: return launch_bt<T_AXPY | T_FP8>(bt, a, grid, lds_bytes, stream);
+    case T_AXPY | T_CLASSIFY | T_FP8:
+      return launch_bt<T_AXPY | T_CLASSIFY | T_FP8>(bt, a, grid, lds_bytes, stream);
     case T_ATTN: return launch_t<T_ATTN, 1>(a, grid, lds_bytes, stream);
     case T_ZERO: return launch_t<T_ZERO, 1>(a, grid, lds_bytes, stream);
     case T_HIST: return launch_t<T_HIST, 1>(a, grid, lds_bytes, stream);
@@ -1248,7 +1391,7 @@ template <int FLAGS, int BT>
 static int occupancy_t(int lds_bytes) {
   int n = 0;
   hipError_t e;
-  if constexpr (FLAGS == T_ROWDOT)
+  if constexpr ((FLAGS & ~T_FP8) == T_ROWDOT)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rowdot_kernel<FLAGS, BT>, kThreads, lds_bytes);
   else if constexpr (BT == 1)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, phase_kernel<FLAGS, BT>, kThreads, lds_bytes);

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libdv.so")
 
-DV_F32, DV_BF16 = 0, 1
+DV_F32, DV_BF16, DV_FP8 = 0, 1, 2
 DV_ACT_RELU, DV_ACT_GELU = 0, 1
 DV_OK, DV_EINVAL, DV_EALIGN, DV_EUNSUPPORTED, DV_EWORKSPACE, DV_EHIP = 0, -1, -2, -3, -4, -5
 OP_PREDICT, OP_SELECT_TOPK, OP_SPARSE_MLP, OP_SPARSE_MHA, OP_DECODE_LAYER = 1, 2, 3, 4, 5
@@ -45,7 +45,8 @@ class LayerStruct(ctypes.Structure):
                [("scale", ctypes.c_float)] + \
                [(n, ctypes.c_void_p) for n in ("W1t", "W2t", "Wq", "Wo", "K", "V",
                                                 "A_M", "B_M", "A_A", "B_A")] + \
-               [("act", ctypes.c_int)]
+               [("act", ctypes.c_int), ("pwdt", ctypes.c_int)] + \
+               [(n, ctypes.c_void_p) for n in ("W1s", "W2s", "Wqs", "Wos")]
 
 
 _lib = None
@@ -105,6 +106,8 @@ def _dtype(t) -> int:
         return DV_BF16
     if t.dtype == torch.float32:
         return DV_F32
+    if t.dtype == torch.uint8:          # fp8 E4M3 codes (with row scales)
+        return DV_FP8
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -183,15 +186,19 @@ class Layer:
     """A dv_layer built from a layer's tensors; keeps them alive while in use."""
 
     def __init__(self, W1t, W2t, Wq, Wo, K, V, A_M=None, B_M=None, A_A=None, B_A=None, *,
-                 k_m=0, k_a=0, scale=1.0, act=DV_ACT_RELU):
-        self.tensors = (W1t, W2t, Wq, Wo, K, V, A_M, B_M, A_A, B_A)
+                 k_m=0, k_a=0, scale=1.0, act=DV_ACT_RELU, row_scales=None):
+        """row_scales = (W1s, W2s, Wqs, Wos) for fp8 weights (uint8 E4M3 codes)."""
+        self.tensors = (W1t, W2t, Wq, Wo, K, V, A_M, B_M, A_A, B_A, row_scales)
         r = A_M.shape[0] if A_M is not None else 0
+        rs = row_scales if row_scales is not None else (None, None, None, None)
         self.s = LayerStruct(d=W1t.shape[1], F=W1t.shape[0], h=Wq.shape[0], dh=Wq.shape[1],
                              n_ctx=K.shape[2], r=r, k_m=int(k_m), k_a=int(k_a),
                              wdt=_dtype(W1t), kvdt=_dtype(K), scale=float(scale),
                              W1t=_ptr(W1t), W2t=_ptr(W2t), Wq=_ptr(Wq), Wo=_ptr(Wo), K=_ptr(K),
                              V=_ptr(V), A_M=_ptr(A_M), B_M=_ptr(B_M), A_A=_ptr(A_A), B_A=_ptr(B_A),
-                             act=int(act))
+                             act=int(act),
+                             pwdt=_dtype(A_M) if A_M is not None else DV_BF16,
+                             W1s=_ptr(rs[0]), W2s=_ptr(rs[1]), Wqs=_ptr(rs[2]), Wos=_ptr(rs[3]))
 
 
 def decode_layer(layer: Layer, next_layer, y_in, y_out, idx_m, count_m, max_count_m, idx_a, count_a,

@@ -41,7 +41,11 @@ def source_hash() -> str:
 
 def stats(src: str, trace: str, out: str, command: str):
     rows = list(csv.DictReader(open(src)))
-    lines = ["# rocprofv3 kernel summary: OPT-175B-shaped decode layer, batch 1", "",
+    # fp8 weight rows: the row dots and the output row sum carry the fp8 flag (128),
+    # and without a next layer the attention runs alone before the row sum
+    fp8 = any(re.search(r"(?:phase|rowdot)_kernel<129, ", r["Name"]) for r in rows)
+    weights = "fp8 (E4M3) weight rows" if fp8 else "bf16 weights"
+    lines = [f"# rocprofv3 kernel summary: OPT-175B-shaped decode layer, batch 1, {weights}", "",
              f"Command: `{command}`", "",
              "## Per kernel (rocprofv3 --stats)", "",
              "| kernel | calls | avg us | min us | max us | % time |",
@@ -65,16 +69,19 @@ def stats(src: str, trace: str, out: str, command: str):
         seq.append((m.group(1), dur))
     # launches of the look-ahead step: a row-dot launch directly followed by the
     # attention + row-sum launch and the row-sum + top-k launch
-    order = [SLOT_FLAGS[k] for k in sorted(SLOT_FLAGS)]
-    slot_durs = {k: [] for k in SLOT_FLAGS}
+    slot_flags = dict(SLOT_FLAGS)
+    if fp8:
+        slot_flags = {0: "129", 1: "6", 2: "148"}
+    order = [slot_flags[k] for k in sorted(slot_flags)]
+    slot_durs = {k: [] for k in slot_flags}
     for i in range(len(seq) - len(order) + 1):
         if all(seq[i + j][0] == order[j] for j in range(len(order))):
             for j in range(len(order)):
                 slot_durs[j].append(seq[i + j][1])
     lines += ["", "## Decode launches by configuration (from the kernel trace)", "",
               "flags: 1 row dots, 2 attention, 4 row sums, 8 histogram, 16 top-k classify, "
-              "32 row sums that wait for in-launch attention, 64 zero fill (sums of these "
-              "for a mixed launch)", "",
+              "32 row sums that wait for in-launch attention, 64 zero fill, 128 fp8 rows "
+              "(sums of these for a mixed launch)", "",
               "| phase_kernel<flags, batch tile> | blocks | launches | avg us | median us | min us |",
               "|---|---|---|---|---|---|"]
     for (fl, bt, blocks), v in sorted(groups.items(), key=lambda kv: -len(kv[1])):
@@ -82,11 +89,11 @@ def stats(src: str, trace: str, out: str, command: str):
                      f"{statistics.median(v):.2f} | {min(v):.2f} |")
     # launches of the sparse MLP + MHA step: row dots, then the single launch of
     # attention and the waiting row sum
-    sp_order = ["1", "38"]
+    sp_order = ["129", "2", "132"] if fp8 else ["1", "38"]
     sp_durs = {k: [] for k in range(len(sp_order))}
-    for i in range(len(seq) - 1):
-        if seq[i][0] == sp_order[0] and seq[i + 1][0] == sp_order[1]:
-            for j in range(2):
+    for i in range(len(seq) - len(sp_order) + 1):
+        if all(seq[i + j][0] == sp_order[j] for j in range(len(sp_order))):
+            for j in range(len(sp_order)):
                 sp_durs[j].append(seq[i + j][1])
     if slot_durs[0]:
         names = {0: "row dots (W1, W^Q, A rows)", 1: "attention + predictor B rows",
@@ -96,10 +103,12 @@ def stats(src: str, trace: str, out: str, command: str):
                   "|---|---|---|---|---|---|"]
         for k in sorted(slot_durs):
             v = slot_durs[k]
-            lines.append(f"| {k}: {names[k]} | <{SLOT_FLAGS[k]}, 1> | {len(v)} | "
+            lines.append(f"| {k}: {names[k]} | <{slot_flags[k]}, 1> | {len(v)} | "
                          f"{statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} |")
     if sp_durs[0]:
-        names = {0: "row dots (W1, W^Q rows)", 1: "attention + row sum W2 then W^O rows"}
+        names = ({0: "row dots (W1, W^Q rows)", 1: "attention, split pieces combined per head",
+                  2: "row sum W2 + W^O rows"} if fp8 else
+                 {0: "row dots (W1, W^Q rows)", 1: "attention + row sum W2 then W^O rows"})
         lines += ["", "## Sparse MLP + MHA step, per launch (from the kernel trace)", "",
                   "| launch | phase_kernel<flags> | launches | avg us | median us | min us |",
                   "|---|---|---|---|---|---|"]

@@ -51,7 +51,12 @@
 extern "C" {
 #endif
 
-typedef enum { DV_F32 = 0, DV_BF16 = 1 } dv_dtype;
+/* Element types.  DV_FP8: weight-only fp8, the OCP E4M3 format (1 byte; sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits), with one fp32 scale per row: element =
+ * scale[row] * value(code).  The pages endorse weight-only quantization for decode
+ * (Deja Vu page, section 1; the survey page's quantization section) without naming a
+ * format.  Only dv_decode_layer takes fp8 weights (W1t, W2t, Wq, Wo). */
+typedef enum { DV_F32 = 0, DV_BF16 = 1, DV_FP8 = 2 } dv_dtype;
 
 /* sigma of Eq. (1): the page names ReLU or GeLU (section 2.3, under Eq. (1)).  GeLU is
  * the exact x Phi(x) = x (1 + erf(x / sqrt 2)) / 2 (the page gives no approximation). */
@@ -156,6 +161,10 @@ typedef struct {
   const void *A_M, *B_M;   /* neuron predictor: [r][d], [r][F] */
   const void *A_A, *B_A;   /* head predictor:   [r][d], [r][h] */
   int act;                 /* sigma of this layer's MLP: dv_act (DV_ACT_RELU = 0) */
+  dv_dtype pwdt;           /* A_M, B_M, A_A, B_A: DV_BF16 or DV_F32 (read from `next`) */
+  /* wdt == DV_FP8: one fp32 scale per row of W1t [F], W2t [F], Wq [h*dh], Wo [h*dh]
+   * (16-byte aligned; NULL otherwise) */
+  const float *W1s, *W2s, *Wqs, *Wos;
 } dv_layer;
 
 /* A5 - one decode layer with the look-ahead predictor (Deja Vu page, section 1 and
@@ -165,7 +174,10 @@ typedef struct {
  *   S_M' = union_b topk(predict(y_in; next->A_M, next->B_M), next->k_m), likewise S_A'.
  * (idx_m, count_m), (idx_a, count_a): this layer's sets (device), capacities max_count_m,
  * max_count_a.  next_idx_m needs capacity min(next->F, batch * next->k_m), next_idx_a
- * min(next->h, batch * next->k_a).  `next` must have the same d as `L`.
+ * min(next->h, batch * next->k_a).  `next` must have the same d as `L`; its predictor
+ * factors have type next->pwdt.  With L->wdt == DV_FP8 the layer's W1t, W2t, Wq, Wo are
+ * fp8 rows with scales L->W1s, W2s, Wqs, Wos and d must be a multiple of 16
+ * (DV_EALIGN otherwise); the KV cache stays L->kvdt.
  * y_out may equal y_in. */
 int dv_decode_layer(const dv_layer* L, const dv_layer* next, int batch,
                     const float* y_in, float* y_out,

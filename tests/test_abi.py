@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(dv.EXPORTS), f"header {names} vs binding {dv.EXPORTS}"
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.dv_version() == 101
+    assert lib.dv_version() == 102
 
 
 def test_library_has_gfx950_code():
@@ -80,6 +80,7 @@ def call_mlp(**over):
     (dict(ws=None), dv.DV_EWORKSPACE), (dict(ws_bytes=100), dv.DV_EWORKSPACE),
     (dict(ws=BAD), dv.DV_EALIGN), (dict(out=P), dv.DV_EINVAL),
     (dict(act=2), dv.DV_EINVAL), (dict(act=-1), dv.DV_EINVAL),
+    (dict(wdt=dv.DV_FP8), dv.DV_EUNSUPPORTED),
 ])
 def test_sparse_mlp_rejects(over, code):
     assert call_mlp(**over) == code
@@ -153,7 +154,10 @@ def _layer(**over):
     (dict(), dict(d=512), dict(), dv.DV_EINVAL),
     (dict(), dict(k_m=2000), dict(), dv.DV_EINVAL),
     (dict(), dict(B_M=None), dict(), dv.DV_EINVAL),
-    (dict(), dict(wdt=dv.DV_F32), dict(), dv.DV_EUNSUPPORTED),
+    (dict(), dict(pwdt=7), dict(), dv.DV_EINVAL),
+    (dict(wdt=dv.DV_FP8), dict(), dict(), dv.DV_EINVAL),                  # fp8 without scales
+    (dict(wdt=dv.DV_FP8, d=264, W1s=P, W2s=P, Wqs=P, Wos=P), dict(d=264), dict(), dv.DV_EALIGN),
+    (dict(wdt=dv.DV_FP8, W1s=P, W2s=BAD, Wqs=P, Wos=P), dict(), dict(), dv.DV_EALIGN),
     (dict(), dict(), dict(next_idx_m=None), dv.DV_EINVAL),
     (dict(), dict(), dict(max_count_a=9), dv.DV_EINVAL),
     (dict(K=BAD), dict(), dict(), dv.DV_EALIGN),

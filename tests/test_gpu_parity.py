@@ -307,9 +307,16 @@ def test_sparse_mha_edges(name):
 # A5 decode layer with the look-ahead predictor                               #
 # --------------------------------------------------------------------------- #
 
-def _layer_case(cfg, batch=None, with_next=True, seed_sets=None, act="relu"):
+def _layer_case(cfg, batch=None, with_next=True, seed_sets=None, act="relu", fp8=False):
     B = cfg.batch if batch is None else batch
     L = synth.make_layer(cfg, DEV, batch=B)
+    row_scales = None
+    if fp8:
+        # weight-only fp8: W1t, W2t, W^Q, W^O as E4M3 codes with one scale per row
+        q = {k: synth.quantize_rows_e4m3(getattr(L, k)) for k in ("W1t", "W2t", "Wq", "Wo")}
+        for k, (codes, _) in q.items():
+            setattr(L, k, codes)
+        row_scales = tuple(q[k][1] for k in ("W1t", "W2t", "Wq", "Wo"))
     P1 = synth.make_predictor(cfg, DEV, layer=1)
     y = synth.make_y(cfg, DEV, batch=B)
     Lh = {k: host(v) for k, v in vars(L).items() if isinstance(v, torch.Tensor)}
@@ -322,7 +329,8 @@ def _layer_case(cfg, batch=None, with_next=True, seed_sets=None, act="relu"):
     idx_a, cnt_a = put_set(S_A, cap_a)
     layer = dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, L.A_M, L.B_M, L.A_A, L.B_A,
                      k_m=cfg.k_m, k_a=cfg.k_a, scale=cfg.scale,
-                     act=dv.DV_ACT_GELU if act == "gelu" else dv.DV_ACT_RELU)
+                     act=dv.DV_ACT_GELU if act == "gelu" else dv.DV_ACT_RELU,
+                     row_scales=row_scales)
     nxt = dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, P1["A_M"], P1["B_M"], P1["A_A"], P1["B_A"],
                    k_m=cfg.k_m, k_a=cfg.k_a, scale=cfg.scale) if with_next else None
     n_idx_m = torch.full((cap_m,), -9, dtype=torch.int32, device=DEV)
@@ -337,6 +345,9 @@ def _layer_case(cfg, batch=None, with_next=True, seed_sets=None, act="relu"):
     torch.cuda.synchronize()
     layer_d = dict(W1t=Lh["W1t"], W2t=Lh["W2t"], Wq=Lh["Wq"], Wo=Lh["Wo"], K=Lh["K"], V=Lh["V"],
                    act=act)
+    if fp8:
+        for k, sc in zip(("W1t", "W2t", "Wq", "Wo"), row_scales):
+            layer_d[k] = O.Fp8Rows(Lh[k], host(sc))
     y_ref, _ = O.decode_layer(yh, layer_d, S_M, S_A, None, cfg.scale)
     res = dict(y_out=y_out.cpu().numpy(), y_ref=y_ref, y=y, layer=layer, ws=ws)
     if with_next:
@@ -376,6 +387,27 @@ def test_decode_layer_gelu(name):
     assert_close(r["y_out"], r["y_ref"], tol_of(cfg, TIGHT_ATTN), f"gelu layer {name}")
     for got, ref_s, k, bound in r["sets"]:
         check_sets_certified(got, ref_s, k, True, bound, f"gelu {name} next sets")
+
+
+FP8_CASES = {
+    "c1": CONFIGS["c1"], "bf16-dh256": RAGGED["bf16-dh256"],
+    "fp8-ragged": LayerConfig("fp8-ragged", 17, d=272, F=1000, h=6, dh=64, batch=3, n_ctx=37,
+                              k_m=97, k_a=2, r=24, union=True),
+    "c2": CONFIGS["c2"], "c3": CONFIGS["c3"],
+}
+
+
+@pytest.mark.parametrize("name", list(FP8_CASES) + ["c4"])
+def test_decode_layer_fp8(name):
+    """Weight-only fp8 layers (E4M3 rows, per-row scales): the oracle computes with the
+    exactly dequantized weights; c4 at batch 1 is the benchmarked shape."""
+    cfg = FP8_CASES.get(name, CONFIGS.get(name))
+    banner(f"decode_layer fp8 {name}")
+    r = _layer_case(cfg, batch=1 if name == "c4" else None, fp8=True)
+    tol = BOUND_F32 * 10 if cfg.wdtype == "f32" else TIGHT_ATTN
+    assert_close(r["y_out"], r["y_ref"], tol, f"fp8 layer {name}")
+    for got, ref_s, k, bound in r["sets"]:
+        check_sets_certified(got, ref_s, k, True, bound, f"fp8 {name} next sets")
 
 
 def test_decode_layer_last_layer_and_alias():
