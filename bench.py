@@ -233,8 +233,13 @@ def main():
     torch.cuda.synchronize()
     sp_ms, sp_n = dv.timing_read(8)
     dv.timing_enable(False)
-    sp_bytes = acc.phase_bytes(**shape, with_predictor=False)
-    sparse_phases = [dict(launch=i, avg_us=round(ms * 1e3 / max(n, 1), 2), bytes=sp_bytes[i],
+    # two launches when the attention shares the row sum's launch, three otherwise
+    n_sp = sum(1 for n in sp_n if n > 0)
+    sp_bytes = acc.phase_bytes(**shape, with_predictor=False, sparse_launches=n_sp)
+    sp_names = (["row dots (W1, W^Q rows)", "attention", "row sum W2 + W^O rows"] if n_sp == 3
+                else ["row dots (W1, W^Q rows)", "attention + row sum W2 then W^O rows"])
+    sparse_phases = [dict(launch=i, name=sp_names[i], avg_us=round(ms * 1e3 / max(n, 1), 2),
+                          bytes=sp_bytes[i],
                           GBps=round(sp_bytes[i] / (ms * 1e-3 / max(n, 1)) / 1e9, 1))
                      for i, (ms, n) in enumerate(zip(sp_ms, sp_n)) if i < len(sp_bytes)]
 

@@ -63,7 +63,7 @@ def step_flops(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: in
 
 def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
                 u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True,
-                p_bytes: int | None = None, row_scale_bytes: int = 0):
+                p_bytes: int | None = None, row_scale_bytes: int = 0, sparse_launches: int = 2):
     """Bytes each launch of the decode layer must move.
 
     With the predictor (the look-ahead step), three launches:
@@ -76,6 +76,8 @@ def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: i
       1 gathered row dots: W1 rows, W^Q rows, y;
       2 attention, and the row sum over W2 then W^O rows: K/V, W2 rows, W^O rows,
         y_in read, y_out written.
+    or, when the attention cannot share the row sum's launch (fp8 rows, larger
+    batches: sparse_launches=3), row dots, attention alone (K/V), then the row sum.
     Small intermediates handed between launches (row dots, q, head outputs, attention
     pieces, scores written: under 1 MB at batch 1) are not counted.
     """
@@ -85,7 +87,7 @@ def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: i
     kv = batch * u_a * 2 * n_ctx * dh * kv_bytes
     out = u_m * row + u_a * dh * row + 2 * batch * d * 4
     if not with_predictor:
-        return [p1, kv + out]
+        return [p1, kv, out] if sparse_launches == 3 else [p1, kv + out]
     p1 += 2 * r * d * pb
     p2 = kv + (r * F + r * h) * pb
     p3 = out + batch * (F + h) * 4

@@ -34,6 +34,10 @@ def test_c4_batch1_bytes():
                        u_a=c.k_a, with_predictor=False)
     # the sparse layer alone: two launches, y read twice
     assert len(sp) == 2 and sum(sp) == b.selected + 1 * c.d * 4
+    sp3 = A.phase_bytes(batch=1, d=c.d, F=c.F, h=c.h, dh=c.dh, n_ctx=c.n_ctx, r=c.r, u_m=c.k_m,
+                        u_a=c.k_a, with_predictor=False, sparse_launches=3)
+    # attention in a launch of its own: the same bytes, split three ways
+    assert len(sp3) == 3 and sum(sp3) == sum(sp) and sp3[0] == sp[0]
 
 
 def test_flops_intensity_batch1():

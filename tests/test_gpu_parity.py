@@ -410,6 +410,17 @@ def test_decode_layer_fp8(name):
         check_sets_certified(got, ref_s, k, True, bound, f"fp8 {name} next sets")
 
 
+@pytest.mark.parametrize("name", ["fp8-ragged", "c2", "c4"])
+def test_decode_layer_fp8_last_layer(name):
+    """fp8 layers without a next layer: at c4 batch 1 (the benchmarked sparse MLP + MHA)
+    the attention and the waiting fp8 row sum share one launch."""
+    cfg = FP8_CASES.get(name, CONFIGS.get(name))
+    banner(f"decode_layer fp8 last layer {name}")
+    r = _layer_case(cfg, batch=1 if name == "c4" else None, with_next=False, fp8=True)
+    tol = BOUND_F32 * 10 if cfg.wdtype == "f32" else TIGHT_ATTN
+    assert_close(r["y_out"], r["y_ref"], tol, f"fp8 last layer {name}")
+
+
 def test_decode_layer_last_layer_and_alias():
     cfg = RAGGED["bf16-ragged"]
     banner("decode_layer last layer, y_out aliasing y_in")
