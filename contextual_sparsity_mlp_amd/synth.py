@@ -169,6 +169,30 @@ def make_layer(cfg: LayerConfig, device="cpu", layer: int = 0, batch: int | None
     return LayerTensors(cfg, W1t, W2t, Wq, Wo, K, V, A_M, B_M, A_A, B_A)
 
 
+def make_kv_weights(cfg: LayerConfig, device="cpu", layer: int = 0):
+    """W^K and W^V of one layer, stored like W^Q as [h][d_h][d] (row c of head i is
+    column c of W_i^K), from the seed recipe."""
+    s = lambda name: seed_of(cfg.cfg_id, layer, name)  # noqa: E731
+    return (_normal((cfg.h, cfg.dh, cfg.d), cfg.w_std, s("Wk"), device, cfg.torch_wdtype),
+            _normal((cfg.h, cfg.dh, cfg.d), cfg.w_std, s("Wv"), device, cfg.torch_wdtype))
+
+
+def make_kv_cache(cfg: LayerConfig, cap: int, device="cpu", layer: int = 0,
+                  batch: int | None = None, fill: float = 1e4):
+    """A KV cache with room for ``cap`` rows per (token, head), [B][h][cap][d_h]:
+    rows 0..n_ctx-1 are the layer's seeded cache, the rest hold ``fill`` (a value no
+    computed row takes, so a test can see which rows a step wrote)."""
+    B = cfg.batch if batch is None else batch
+    s = lambda name: seed_of(cfg.cfg_id, layer, name)  # noqa: E731
+    out = []
+    for name in ("K", "V"):
+        t = torch.full((B, cfg.h, cap, cfg.dh), fill, dtype=cfg.torch_kvdtype, device=device)
+        t[:, :, :cfg.n_ctx] = _normal((B, cfg.h, cfg.n_ctx, cfg.dh), cfg.kv_std, s(name), device,
+                                      cfg.torch_kvdtype)
+        out.append(t)
+    return tuple(out)
+
+
 def make_predictor(cfg: LayerConfig, device="cpu", layer: int = 0):
     """Only the predictor factors (A_M, B_M, A_A, B_A) of a layer, same seeds as make_layer."""
     wdt = cfg.torch_wdtype

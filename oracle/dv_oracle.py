@@ -30,8 +30,9 @@ Readings where the pages are silent (each is listed in the design notes):
   standard normal CDF (the page gives no approximation); no biases (Eq. 1/2 have none); the logit scale is a parameter,
   1.0 by default (Eq. 2 has no 1/sqrt(d_h)); exp is evaluated after subtracting
   the row maximum, an exact identity in real arithmetic that keeps fp64 finite;
-  the cache holds exactly n rows K = X W^K, V = X W^V and the current token is
-  not appended; for a batch, S is the union of the per-token top-k sets and is
+  the cache holds n rows K = X W^K, V = X W^V; the plain step does not append the
+  current token, the full step (``decode_layer_append``) does, for every head (see
+  there); for a batch, S is the union of the per-token top-k sets and is
   used by every token; index sets are returned in ascending order; the top-k
   decision is taken on scores rounded to fp32, the precision the kernel decides in.
 
@@ -277,6 +278,74 @@ def decode_layer(y, layer: dict, S_M, S_A, next_layer: dict | None, scale: float
                 predict_and_select(yy, next_layer["A_A"], next_layer["B_A"],
                                    next_layer["k_a"], next_layer["union"]))
     return y_next, sets
+
+
+# --------------------------------------------------------------------------- #
+# The full decode step: the current token's keys and values join the cache    #
+# --------------------------------------------------------------------------- #
+
+
+def round_bf16(x) -> np.ndarray:
+    """float64 values rounded to the nearest bfloat16 (8 significant bits, ties to
+    even, bf16 subnormals below 2^-126 on the 2^-133 grid), as bf16 bit patterns
+    (uint16).  Rounds once, from the float64 value."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                        # |x| = m 2^e with 0.5 <= m < 1
+    e = np.maximum(e, -125)                   # bf16 normals start at 2^-126 = 0.5 * 2^-125
+    q = np.rint(np.ldexp(x, 8 - e))           # 8 significant bits; rint ties to even
+    v = np.ldexp(q, e - 8).astype(np.float32)   # exact: v has at most 8 significant bits
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def store_as(x, like) -> np.ndarray:
+    """float64 values rounded to the storage type of array ``like`` (bf16 bit
+    patterns for uint16, else float32 or float64)."""
+    dt = np.asarray(like).dtype
+    if dt == np.uint16:
+        return round_bf16(x)
+    return np.asarray(x, dtype=np.float64).astype(dt)
+
+
+def kv_for_token(y, Wk, Wv):
+    """k_i = y W_i^K and v_i = y W_i^V of the current token for every head i
+    (float64 [B][h][dh]); Wk, Wv are stored like Wq: [h][dh][d], row c of head i
+    holding column c of W_i^K (W_i^V).  Eq. (2) builds K = X W^K, V = X W^V from
+    the rows of X; these are the current token's rows."""
+    y = widen(y)
+    WK, WV = widen(Wk), widen(Wv)
+    h, dh, d = WK.shape
+    k = (WK.reshape(h * dh, d) @ y.T).T.reshape(-1, h, dh)
+    v = (WV.reshape(h * dh, d) @ y.T).T.reshape(-1, h, dh)
+    return k, v
+
+
+def decode_layer_append(y, layer: dict, S_M, S_A, next_layer: dict | None, n: int,
+                        scale: float = 1.0):
+    """One decode step that also extends the KV cache (the KV-cache blog page,
+    figure (b): at a decode step the current token's key and value join the
+    stored ones, attention runs over all of them, and they are then kept).
+
+    Readings (the pages say nothing of heads a step skips): X in Eq. (2) holds
+    every previous token for every head, so the current token's k and v are
+    computed and stored for all h heads, selected or not; they are stored at row
+    n of each head's cache, rounded to the cache's storage type, and the selected
+    heads attend over rows 0..n, the current token's own stored row among them.
+
+    ``layer`` holds the decode layer's arrays plus Wk, Wv; K, V are [B][h][cap][dh]
+    with cap > n, of which rows 0..n-1 are the cache (rows n and beyond are not
+    read).  Returns (y_next, sets, (k_row, v_row)): the layer output and next sets
+    as ``decode_layer`` gives them, and the stored rows [B][h][dh] in the cache's
+    storage type.
+    """
+    K, V = np.asarray(layer["K"]), np.asarray(layer["V"])
+    if not 0 <= n < K.shape[2]:
+        raise ValueError(f"row {n} is outside a cache of {K.shape[2]} rows")
+    k, v = kv_for_token(y, layer["Wk"], layer["Wv"])
+    k_row, v_row = store_as(k, K), store_as(v, V)
+    K1 = np.concatenate([K[:, :, :n], k_row[:, :, None, :]], axis=2)
+    V1 = np.concatenate([V[:, :, :n], v_row[:, :, None, :]], axis=2)
+    y_next, sets = decode_layer(y, dict(layer, K=K1, V=V1), S_M, S_A, next_layer, scale)
+    return y_next, sets, (k_row, v_row)
 
 
 def decode_stack(y0, layers: list, scale: float = 1.0):

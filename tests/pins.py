@@ -18,7 +18,9 @@ What pins what:
   * the mean-shift restatement of a head on the Deja Vu page, section 3.2:
     H_i(y) = m_i(y) W_i^V with m_i a similarity-weighted mean of the x_j;
   * brute force: all k-subsets for top-k on tiny N, scalar loops for the
-    products, np.lexsort for the ordering rule.
+    products, np.lexsort for the ordering rule;
+  * the KV-cache blog page, figure (b): a decode step over the cache plus the
+    appended current token equals causal attention over the whole sequence.
 """
 from __future__ import annotations
 
@@ -497,6 +499,115 @@ def check_stack_lookahead(O):
         assert list(a0) == list(b0) and list(a1) == list(b1), "stack sets"
 
 
+# --------------------------------------------------------------------------- #
+# the full decode step: the current token's k and v join the cache            #
+# --------------------------------------------------------------------------- #
+
+def check_round_bf16(O):
+    """Storage rounding of appended rows: nearest bf16, ties to even, rounded once
+    from float64.  Against torch's float32 -> bfloat16 cast where the value is a
+    float32 (one rounding either way), and hand-worked bit patterns."""
+    r = _rng(30)
+    x = r.standard_normal(20000) * np.exp2(r.integers(-30, 30, 20000).astype(np.float64))
+    x = np.concatenate([x, np.exp2(np.arange(-133, -120, dtype=np.float64)) * 1.37])
+    x32 = x.astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.round_bf16(x32.astype(np.float64))
+    assert got.dtype == np.uint16 and np.array_equal(got, ref), "bf16 rounding vs torch"
+    hand = [(1.0, 0x3F80), (1 + 2.0 ** -8, 0x3F80),         # tie, even neighbour below
+            (1 + 3 * 2.0 ** -8, 0x3F82),                      # tie, even neighbour above
+            (1 + 2.0 ** -8 + 2.0 ** -30, 0x3F81),             # just above the tie: one rounding
+            (-2.5, 0xC020), (-0.0, 0x8000), (0.0, 0x0000),
+            (2.0 ** -130, 0x0008),                            # bf16 subnormal
+            (255.5, 0x4380), (257.0, 0x4380), (259.0, 0x4382)]   # 8 significant bits
+    for v, bits in hand:
+        assert int(O.round_bf16(np.array([v]))[0]) == bits, f"round_bf16({v!r})"
+
+
+def _append_data(seed, B=2, d=12, h=4, dh=3, n=6, F=16):
+    r = _rng(seed)
+    X = r.standard_normal((B, n + 1, d))          # each token's sequence; row n is the current token
+    W = {k: r.standard_normal((h, dh, d)) * 0.4 for k in ("Wq", "Wk", "Wv", "Wo")}
+    W["W1t"], W["W2t"] = r.standard_normal((F, d)), r.standard_normal((F, d))
+    return X, W
+
+
+def check_append_equals_recompute(O):
+    """KV-cache blog page, figure (b): caching the keys and values and appending the
+    current token's gives what attention over the whole sequence gives.  Reference:
+    the last query of causal scaled_dot_product_attention over all n + 1 tokens,
+    projected by W^O of the selected heads; the appended rows are the last rows of
+    X W^K and X W^V for every head."""
+    for scale in (1.0, 0.7):
+        X, W = _append_data(31)
+        B, n1, d = X.shape
+        n = n1 - 1
+        h, dh, _ = W["Wq"].shape
+        Xt = torch.from_numpy(X)
+        proj = {k: torch.einsum("bnd,icd->bin c".replace(" ", ""), Xt, torch.from_numpy(W[k]))
+                for k in ("Wq", "Wk", "Wv")}                       # [B][h][n+1][dh]
+        cap = n + 3
+        K = np.full((B, h, cap, dh), 7.0)
+        V = np.full((B, h, cap, dh), -7.0)
+        K[:, :, :n] = proj["Wk"][:, :, :n].numpy()
+        V[:, :, :n] = proj["Wv"][:, :, :n].numpy()
+        K0, V0 = K.copy(), V.copy()
+        S_A = [0, 2, 3]
+        layer = dict(W1t=W["W1t"], W2t=W["W2t"], Wq=W["Wq"], Wo=W["Wo"], Wk=W["Wk"],
+                     Wv=W["Wv"], K=K, V=V)
+        y = X[:, n]
+        y_next, _, (k_row, v_row) = O.decode_layer_append(y, layer, [], S_A, None, n, scale)
+        assert np.array_equal(K, K0) and np.array_equal(V, V0), "inputs modified"
+        o = torch.nn.functional.scaled_dot_product_attention(
+            proj["Wq"], proj["Wk"], proj["Wv"], is_causal=True, scale=scale)[:, :, n]   # [B][h][dh]
+        ref = sum(o[:, i] @ torch.from_numpy(W["Wo"][i]) for i in S_A).numpy()
+        assert_close(y_next - y, ref, 1e-12, f"append = attention over the sequence, scale {scale}")
+        assert_close(k_row, proj["Wk"][:, :, n].numpy(), 1e-13, "appended keys, every head")
+        assert_close(v_row, proj["Wv"][:, :, n].numpy(), 1e-13, "appended values, every head")
+        try:
+            O.decode_layer_append(y, layer, [], S_A, None, cap, scale)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("a row outside the cache must be refused")
+
+
+def check_append_stored_row_attended(O):
+    """With a bf16 cache the stored (rounded) row is the one attended: the step's
+    output is Eq. (2) over the widened cache rows 0..n-1 plus the returned row,
+    computed here with scaled_dot_product_attention; and an empty cache (n = 0)
+    gives each selected head exactly its stored value row."""
+    X, W = _append_data(32, n=5)
+    B, n1, d = X.shape
+    n = n1 - 1
+    h, dh, _ = W["Wq"].shape
+    r = _rng(33)
+    Kb = torch.from_numpy(r.standard_normal((B, h, n + 2, dh))).to(torch.bfloat16)
+    Vb = torch.from_numpy(r.standard_normal((B, h, n + 2, dh))).to(torch.bfloat16)
+    K = Kb.view(torch.int16).numpy().view(np.uint16)
+    V = Vb.view(torch.int16).numpy().view(np.uint16)
+    layer = dict(W1t=W["W1t"], W2t=W["W2t"], Wq=W["Wq"], Wo=W["Wo"], Wk=W["Wk"], Wv=W["Wv"],
+                 K=K, V=V)
+    y = X[:, n]
+    S_A = [1, 3]
+    y_next, _, (k_row, v_row) = O.decode_layer_append(y, layer, [], S_A, None, n)
+    assert k_row.dtype == np.uint16 and v_row.dtype == np.uint16, "rows stored as bf16"
+    wid = lambda a: torch.from_numpy(a.astype(np.uint32) << 16).view(torch.float32).double()  # noqa: E731
+    Kc = torch.cat([Kb[:, :, :n].double(), wid(k_row).unsqueeze(2)], dim=2)
+    Vc = torch.cat([Vb[:, :, :n].double(), wid(v_row).unsqueeze(2)], dim=2)
+    q = torch.einsum("bd,icd->bic", torch.from_numpy(y), torch.from_numpy(W["Wq"]))
+    o = torch.nn.functional.scaled_dot_product_attention(q.unsqueeze(2), Kc, Vc, scale=1.0).squeeze(2)
+    ref = sum(o[:, i] @ torch.from_numpy(W["Wo"][i]) for i in S_A).numpy()
+    assert_close(y_next - y, ref, 1e-12, "bf16 cache: stored row attended")
+    v_exact = np.einsum("bd,icd->bic", y, W["Wv"])
+    assert np.max(np.abs(wid(v_row).numpy() - v_exact) / np.maximum(np.abs(v_exact), 1e-30)) \
+        <= 2.0 ** -8, "stored values within half a bf16 ulp (2^-8 relative)"
+    # empty cache: softmax over one key is 1, H_i = v_i
+    y0, _, (_, v0) = O.decode_layer_append(y, layer, [], S_A, None, 0)
+    ref0 = sum(wid(v0)[:, i].numpy() @ W["Wo"][i] for i in S_A)
+    assert_close(y0 - y, ref0, 1e-13, "n = 0: each head returns its own value")
+
+
 ALL_CHECKS = [
     check_golden_mlp, check_golden_mha, check_golden_predictor, check_golden_layer,
     check_scores_associative, check_scores_identity_factor, check_scores_bf16_widening,
@@ -507,4 +618,5 @@ ALL_CHECKS = [
     check_layer_gelu, check_e4m3_decode, check_fp8_rows_mlp_mha,
     check_mha_dense_library, check_mha_empty_and_additive, check_head_closed_forms,
     check_head_mean_shift, check_layer_composition, check_stack_lookahead,
+    check_round_bf16, check_append_equals_recompute, check_append_stored_row_attended,
 ]

@@ -5,6 +5,7 @@ import types
 
 import numpy as np
 import pytest
+import torch
 
 import pins
 from oracle import dv_oracle as O
@@ -190,6 +191,55 @@ def _widen_fp8_no_scale(a):
     return O.widen(a)
 
 
+def _append_ignores_current(y, layer, S_M, S_A, next_layer, n, scale=1.0):
+    k, v = O.kv_for_token(y, layer["Wk"], layer["Wv"])
+    K, V = np.asarray(layer["K"]), np.asarray(layer["V"])
+    lay = dict(layer, K=K[:, :, :n], V=V[:, :, :n])
+    y_next, sets = O.decode_layer(y, lay, S_M, S_A, next_layer, scale) if n > 0 else \
+        (O.widen(y) + O.sparse_mlp(y, layer["W1t"], layer["W2t"], S_M), None)
+    return y_next, sets, (O.store_as(k, K), O.store_as(v, V))
+
+
+def _append_overwrites_last(y, layer, S_M, S_A, next_layer, n, scale=1.0):
+    return O.decode_layer_append(y, layer, S_M, S_A, next_layer, max(n - 1, 0), scale)
+
+
+def _kv_swapped(y, Wk, Wv):
+    k, v = _real_kv(y, Wk, Wv)
+    return v, k
+
+
+def _kv_selected_only(y, layer, S_M, S_A, next_layer, n, scale=1.0):
+    y_next, sets, (k, v) = O.decode_layer_append(y, layer, S_M, S_A, next_layer, n, scale)
+    keep = np.zeros(k.shape[1], dtype=bool)
+    keep[O.as_set(S_A)] = True
+    k, v = k.copy(), v.copy()
+    k[:, ~keep] = 0
+    v[:, ~keep] = 0
+    return y_next, sets, (k, v)
+
+
+def _append_attends_unrounded(y, layer, S_M, S_A, next_layer, n, scale=1.0):
+    k, v = O.kv_for_token(y, layer["Wk"], layer["Wv"])
+    K, V = np.asarray(layer["K"]), np.asarray(layer["V"])
+    K1 = np.concatenate([O.widen(K[:, :, :n]), k[:, :, None]], axis=2)
+    V1 = np.concatenate([O.widen(V[:, :, :n]), v[:, :, None]], axis=2)
+    y_next, sets = O.decode_layer(y, dict(layer, K=K1, V=V1), S_M, S_A, next_layer, scale)
+    return y_next, sets, (O.store_as(k, K), O.store_as(v, V))
+
+
+def _bf16_truncate(x):
+    v = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_via_f32(x):
+    v = torch.from_numpy(np.asarray(x, dtype=np.float64).astype(np.float32)).to(torch.bfloat16)
+    return v.view(torch.int16).numpy().view(np.uint16)
+
+
+_real_kv = O.kv_for_token
+
 MUTANTS = {
     "mlp without ReLU": dict(sparse_mlp=_mlp_no_relu),
     "mlp W1/W2 swapped": dict(sparse_mlp=_mlp_swapped),
@@ -219,6 +269,13 @@ MUTANTS = {
     "layer predicts from output": dict(decode_layer=_layer_predict_from_output),
     "layer drops residual": dict(decode_layer=_layer_no_residual),
     "layer drops attention": dict(decode_layer=_layer_no_mha),
+    "append ignores the current token": dict(decode_layer_append=_append_ignores_current),
+    "append overwrites the last cached row": dict(decode_layer_append=_append_overwrites_last),
+    "append keys and values swapped": dict(kv_for_token=_kv_swapped),
+    "append stores selected heads only": dict(decode_layer_append=_kv_selected_only),
+    "append attends the unrounded row": dict(decode_layer_append=_append_attends_unrounded),
+    "bf16 store truncates": dict(round_bf16=_bf16_truncate),
+    "bf16 store rounds twice": dict(round_bf16=_bf16_via_f32),
 }
 
 
