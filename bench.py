@@ -89,6 +89,10 @@ def main():
                          "with per-row scales (predictor factors and KV stay bf16)")
     ap.add_argument("--act", choices=("relu", "gelu"), default="relu",
                     help="sigma of the MLP (OPT uses ReLU; GeLU is the page's other choice)")
+    ap.add_argument("--kv-append", action="store_true",
+                    help="the full decode step: every head's k and v of the current token are "
+                         "computed (W^K, W^V read in full), stored at row n_ctx of the cache "
+                         "and attended with it")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -127,10 +131,19 @@ def main():
     log(f"generating {R} replicas of the c4 layer (batch {B}) on the GPU")
     layers, ys = [], []
     for l in range(R):
-        Lt = synth.make_layer(cfg, dev, layer=l, batch=B)
+        Lt = synth.make_layer(cfg, dev, layer=l, batch=B, with_kv=not args.kv_append)
+        if args.kv_append:
+            # a cache with a free row n_ctx; every step of the loop appends there
+            Lt.K, Lt.V = synth.make_kv_cache(cfg, cfg.n_ctx + 1, dev, layer=l, batch=B)
+            Lt.extra["Wk"], Lt.extra["Wv"] = synth.make_kv_weights(cfg, dev, layer=l)
         if args.wdt == "fp8":
             # weight-only fp8 input preparation: E4M3 codes with one fp32 scale per row
-            for k in ("W1t", "W2t", "Wq", "Wo"):
+            for k in ("W1t", "W2t", "Wq", "Wo") + (("Wk", "Wv") if args.kv_append else ()):
+                if k in Lt.extra:
+                    codes, sc = synth.quantize_rows_e4m3(Lt.extra[k])
+                    Lt.extra[k] = codes
+                    Lt.extra[k + "_scale"] = sc
+                    continue
                 codes, sc = synth.quantize_rows_e4m3(getattr(Lt, k))
                 setattr(Lt, k, codes)
                 Lt.extra[k + "_scale"] = sc
@@ -142,10 +155,17 @@ def main():
             return None
         return tuple(L.extra[k + "_scale"] for k in ("W1t", "W2t", "Wq", "Wo"))
 
+    def kv_args(L):
+        if not args.kv_append:
+            return {}
+        return dict(Wk=L.extra["Wk"], Wv=L.extra["Wv"], n_ctx=cfg.n_ctx,
+                    kv_scales=((L.extra["Wk_scale"], L.extra["Wv_scale"]) if args.wdt == "fp8"
+                               else None))
+
     dvl = [dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, L.A_M, L.B_M, L.A_A, L.B_A,
                     k_m=k_m, k_a=k_a, scale=cfg.scale,
                     act=dv.DV_ACT_GELU if args.act == "gelu" else dv.DV_ACT_RELU,
-                    row_scales=row_scales(L)) for L in layers]
+                    row_scales=row_scales(L), **kv_args(L)) for L in layers]
 
     i32 = lambda n: torch.zeros(n, dtype=torch.int32, device=dev)  # noqa: E731
     sets = [dict(m=i32(cap_m), cm=i32(1), a=i32(cap_a), ca=i32(1)) for _ in range(2)]
@@ -196,7 +216,8 @@ def main():
     u_a = int(sets[0]["ca"].cpu()[0])
     shape = dict(batch=B, d=cfg.d, F=cfg.F, h=cfg.h, dh=cfg.dh, n_ctx=cfg.n_ctx, r=cfg.r,
                  u_m=u_m, u_a=u_a,
-                 **(dict(w_bytes=1, p_bytes=2, row_scale_bytes=4) if args.wdt == "fp8" else {}))
+                 **(dict(w_bytes=1, p_bytes=2, row_scale_bytes=4) if args.wdt == "fp8" else {}),
+                 kv_append=args.kv_append)
     full_bytes = acc.step_bytes(**shape)
     log(f"timing {args.steps} steps (|S_M|={u_m}, |S_A|={u_a})")
     ms_step, ev_step = timed(args.steps)
@@ -213,7 +234,8 @@ def main():
     dv.timing_enable(False)
     ph_bytes = acc.phase_bytes(**shape)
     phases = []
-    names = ["row dots (W1, W^Q, A rows)", "attention + predictor B rows",
+    kvn = "; W^K, W^V of every head" if args.kv_append else ""
+    names = [f"row dots (W1, W^Q, A rows{kvn})", "attention + predictor B rows",
              "row sum W2 + W^O rows, combine, top-k"]
     for i, (ms, n) in enumerate(zip(ph_ms, ph_n)):
         avg_us = ms * 1e3 / max(n, 1)
@@ -236,8 +258,9 @@ def main():
     # two launches when the attention shares the row sum's launch, three otherwise
     n_sp = sum(1 for n in sp_n if n > 0)
     sp_bytes = acc.phase_bytes(**shape, with_predictor=False, sparse_launches=n_sp)
-    sp_names = (["row dots (W1, W^Q rows)", "attention", "row sum W2 + W^O rows"] if n_sp == 3
-                else ["row dots (W1, W^Q rows)", "attention + row sum W2 then W^O rows"])
+    sp_names = ([f"row dots (W1, W^Q rows{kvn})", "attention", "row sum W2 + W^O rows"]
+                if n_sp == 3 else
+                [f"row dots (W1, W^Q rows{kvn})", "attention + row sum W2 then W^O rows"])
     sparse_phases = [dict(launch=i, name=sp_names[i], avg_us=round(ms * 1e3 / max(n, 1), 2),
                           bytes=sp_bytes[i],
                           GBps=round(sp_bytes[i] / (ms * 1e-3 / max(n, 1)) / 1e9, 1))
@@ -254,7 +277,7 @@ def main():
     cpu = None
     if args.cpu_layers > 0:
         cpu = cpu_baseline(args.cpu_layers, layers, ys, sets, cfg, B, u_m, u_a, full_bytes.total,
-                           args.act, args.wdt == "fp8")
+                           args.act, args.wdt == "fp8", args.kv_append)
 
     out = {
         "metric": METRIC,
@@ -273,9 +296,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"opt-175b-shaped decode layer, batch {B}, look-ahead predictor"
                                + (", GeLU MLP" if args.act == "gelu" else "")
-                               + (", fp8 weights" if args.wdt == "fp8" else ""),
+                               + (", fp8 weights" if args.wdt == "fp8" else "")
+                               + (", KV append" if args.kv_append else ""),
                    "wdt": args.wdt,
                    "act": args.act,
+                   "kv_append": args.kv_append,
                    "d": cfg.d, "F": cfg.F, "h": cfg.h, "dh": cfg.dh, "n_ctx": cfg.n_ctx,
                    "r": cfg.r, "batch": B, "k_m": k_m, "k_a": k_a, "U_M": u_m, "U_A": u_a,
                    "replicas": R},
@@ -301,7 +326,7 @@ def main():
 
 
 def cpu_baseline(n_layers, layers, ys, sets, cfg, B, u_m, u_a, step_bytes_total, act="relu",
-                 fp8=False):
+                 fp8=False, kv_append=False):
     """The CPU oracle (float64 NumPy, as it stands) on host copies of replica 0."""
     import numpy as np
     import torch
@@ -318,9 +343,14 @@ def cpu_baseline(n_layers, layers, ys, sets, cfg, B, u_m, u_a, step_bytes_total,
     L, L1 = layers[0], layers[1 % len(layers)]
     layer_h = dict(W1t=host(L.W1t), W2t=host(L.W2t), Wq=host(L.Wq), Wo=host(L.Wo), K=host(L.K),
                    V=host(L.V), act=act)
+    if kv_append:
+        layer_h["Wk"], layer_h["Wv"] = host(L.extra["Wk"]), host(L.extra["Wv"])
     if fp8:
         for k in ("W1t", "W2t", "Wq", "Wo"):
             layer_h[k] = O.Fp8Rows(layer_h[k], host(L.extra[k + "_scale"]))
+        if kv_append:
+            for k in ("Wk", "Wv"):
+                layer_h[k] = O.Fp8Rows(layer_h[k], host(L.extra[k + "_scale"]))
     nxt_h = dict(A_M=host(L1.A_M), B_M=host(L1.B_M), A_A=host(L1.A_A), B_A=host(L1.B_A),
                  k_m=cfg.k_m, k_a=cfg.k_a, union=True)
     # replica 0's own sets, as the oracle would predict them from y_0
@@ -330,13 +360,17 @@ def cpu_baseline(n_layers, layers, ys, sets, cfg, B, u_m, u_a, step_bytes_total,
     times = []
     for _ in range(n_layers):
         t0 = time.perf_counter()
-        O.decode_layer(yh, layer_h, S_M, S_A, nxt_h, cfg.scale)
+        if kv_append:
+            O.decode_layer_append(yh, layer_h, S_M, S_A, nxt_h, cfg.n_ctx, cfg.scale)
+        else:
+            O.decode_layer(yh, layer_h, S_M, S_A, nxt_h, cfg.scale)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     return {"value": round(step_bytes_total / t / 1e9, 3), "unit": "GB/s",
             "us_per_layer": round(t * 1e6, 1), "cores": blas_threads(), "kind": "oracle",
             "sample": f"{n_layers} full decode layers of the same workload (replica 0, batch {B}, "
-                      f"look-ahead predictor + top-k + sparse MLP + sparse MHA), float64 NumPy, "
+                      f"look-ahead predictor + top-k + sparse MLP + sparse MHA"
+                      f"{' + KV append' if kv_append else ''}), float64 NumPy, "
                       f"median of {n_layers}; same byte count as the GPU line"}
 
 

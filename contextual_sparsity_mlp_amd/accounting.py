@@ -27,10 +27,12 @@ class StepBytes:
     kv: int             # K and V rows of S_A for every token
     io: int             # y in, y out (and the MLP partial the combine reads)
     predictor: int      # A_M, B_M, A_A, B_A in full
+    append: int = 0     # the KV append: W^K, W^V rows of every head, the rows written
 
     @property
     def selected(self) -> int:
-        return self.mlp + self.attn_weights + self.kv + self.io
+        """Everything the layer step moves except the predictor."""
+        return self.mlp + self.attn_weights + self.kv + self.io + self.append
 
     @property
     def total(self) -> int:
@@ -39,18 +41,23 @@ class StepBytes:
 
 def step_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
                u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True,
-               p_bytes: int | None = None, row_scale_bytes: int = 0) -> StepBytes:
+               p_bytes: int | None = None, row_scale_bytes: int = 0,
+               kv_append: bool = False) -> StepBytes:
     """Algorithmic bytes of one step.  w_bytes per selected weight element (1 for
     weight-only fp8, whose rows also carry row_scale_bytes of scale each); p_bytes per
-    predictor element (default w_bytes)."""
+    predictor element (default w_bytes).  kv_append: the step also computes every
+    head's k and v of the current token (W^K and W^V read in full), writes them to
+    row n_ctx of the cache and attends over n_ctx + 1 rows."""
     row = d * w_bytes + row_scale_bytes
     mlp = u_m * 2 * row
     attn_w = u_a * 2 * dh * row
-    kv = batch * u_a * 2 * n_ctx * dh * kv_bytes
+    n_att = n_ctx + (1 if kv_append else 0)
+    kv = batch * u_a * 2 * n_att * dh * kv_bytes
     io = 2 * batch * d * 4
     pb = w_bytes if p_bytes is None else p_bytes
     pred = (2 * d * r + r * F + r * h) * pb if with_predictor else 0
-    return StepBytes(mlp, attn_w, kv, io, pred)
+    app = (2 * h * dh * row + 2 * batch * h * dh * kv_bytes) if kv_append else 0
+    return StepBytes(mlp, attn_w, kv, io, pred, app)
 
 
 def step_flops(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
@@ -63,7 +70,8 @@ def step_flops(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: in
 
 def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
                 u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True,
-                p_bytes: int | None = None, row_scale_bytes: int = 0, sparse_launches: int = 2):
+                p_bytes: int | None = None, row_scale_bytes: int = 0, sparse_launches: int = 2,
+                kv_append: bool = False):
     """Bytes each launch of the decode layer must move.
 
     With the predictor (the look-ahead step), three launches:
@@ -78,13 +86,18 @@ def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: i
         y_in read, y_out written.
     or, when the attention cannot share the row sum's launch (fp8 rows, larger
     batches: sparse_launches=3), row dots, attention alone (K/V), then the row sum.
+    With kv_append the row dots also read W^K and W^V in full and write the cache
+    rows, and the attention reads n_ctx + 1 rows.
     Small intermediates handed between launches (row dots, q, head outputs, attention
     pieces, scores written: under 1 MB at batch 1) are not counted.
     """
     row = d * w_bytes + row_scale_bytes
     pb = w_bytes if p_bytes is None else p_bytes
     p1 = u_m * row + u_a * dh * row + batch * d * 4
-    kv = batch * u_a * 2 * n_ctx * dh * kv_bytes
+    n_att = n_ctx + (1 if kv_append else 0)
+    kv = batch * u_a * 2 * n_att * dh * kv_bytes
+    if kv_append:
+        p1 += 2 * h * dh * row + 2 * batch * h * dh * kv_bytes
     out = u_m * row + u_a * dh * row + 2 * batch * d * 4
     if not with_predictor:
         return [p1, kv, out] if sparse_launches == 3 else [p1, kv + out]

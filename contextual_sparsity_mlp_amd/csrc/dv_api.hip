@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cassert>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -234,7 +235,8 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   p.a = w.take((size_t)batch * cap_m * 4);
   p.q = w.take((size_t)batch * cap_a * dh * 4);
   p.o = w.take((size_t)batch * cap_a * dh * 4);
-  p.part = w.take((size_t)batch * cap_a * attn_nsplit_max(n_ctx) * (dh + 2) * 4);
+  // pieces for n_ctx + 1 attended rows: room for the step with the KV append
+  p.part = w.take((size_t)batch * cap_a * attn_nsplit_max(n_ctx + 1) * (dh + 2) * 4);
   p.zm = w.take((size_t)batch * r * 4);
   p.za = w.take((size_t)batch * r * 4);
   p.sm = w.take((size_t)batch * F * 4);
@@ -258,9 +260,12 @@ RowList make_list(const int32_t* idx, const int32_t* count, int host_count, int 
   return L;
 }
 
+// store: the segment's dots go into a KV cache row instead of out (RowdotTask::seg_store).
 void add_rowdot(RowdotTask& T, const void* W, long long stride, dv_dtype wdt, RowList L, float* out,
-                int out_ld, const float* scale = nullptr) {
+                int out_ld, const float* scale = nullptr, void* store = nullptr) {
+  assert(T.nseg < kMaxRowdotSeg);
   T.seg_scale[T.nseg] = scale;
+  T.seg_store[T.nseg] = store;
   RowdotSeg& S = T.seg[T.nseg++];
   S.W = W; S.row_stride = stride; S.wdt = wcode(wdt);
   S.rows = L; S.out = out; S.out_ld = out_ld; S.cap = L.host_count * L.expand;
@@ -336,11 +341,12 @@ int axpy_lds(int bt, int vec = 8) {
                   (16 + kHistBins) * 4);
 }
 
+// n: cache rows attended; kv_cap: rows per (token, head) in K and V (>= n).
 void setup_attn(AttnTask& A, const float* q, int q_ld, const void* K, const void* V, dv_dtype kvdt,
-                int batch, int h, int n, int dh, RowList heads, float scale, float* part,
+                int batch, int h, int n, int kv_cap, int dh, RowList heads, float scale, float* part,
                 uint32_t* tickets, float* o, int o_ld, int other_blocks) {
   A.q = q; A.q_ld = q_ld; A.K = K; A.V = V; A.kvdt = (kvdt == DV_BF16) ? W_BF16 : W_F32;
-  A.batch = batch; A.h = h; A.n = n; A.dh = dh; A.heads = heads; A.scale = scale;
+  A.batch = batch; A.h = h; A.n = n; A.cap = kv_cap; A.dh = dh; A.heads = heads; A.scale = scale;
   const int cap = heads.host_count;
   // Splits of about 128 keys keep each block's chain of dependent loads short;
   // with few (token, head) pairs and nothing else in the launch, more splits
@@ -428,7 +434,7 @@ extern "C" {
 
 const char* dv_last_error(void) { return g_err.c_str(); }
 
-int dv_version(void) { return 102; }
+int dv_version(void) { return 103; }
 
 static size_t ws_bytes_for(int op, const dv_shape* s, dv_dtype wdt) {
   const int B = s->batch;
@@ -466,7 +472,7 @@ size_t dv_workspace_bytes(int op, const dv_shape* s) {
       }
       break;
     case DV_OP_DECODE_LAYER:
-      if (s->d <= 0 || s->F <= 0 || s->h <= 0 || s->dh <= 0 || s->n_ctx <= 0 || s->r <= 0 ||
+      if (s->d <= 0 || s->F <= 0 || s->h <= 0 || s->dh <= 0 || s->n_ctx < 0 || s->r <= 0 ||
           s->max_count_m < 0 || s->max_count_a < 0) {
         fail(DV_EINVAL, "%s: bad layer shape", fn); return 0;
       }
@@ -620,7 +626,7 @@ int dv_sparse_mha(const float* y, int batch, int d, int h, int dh, const void* W
   if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
 
   PhaseArgs a2 = zero_args();
-  setup_attn(a2.attn, q, cap * dh, K, V, kvdt, batch, h, n_ctx, dh,
+  setup_attn(a2.attn, q, cap * dh, K, V, kvdt, batch, h, n_ctx, n_ctx, dh,
              make_list(heads, count, max_count, 1, h), scale, part, t_attn, o, cap * dh, 0);
   if (max_count > 0) {
     if (int e = launch(T_ATTN, 1, a2, a2.attn.blocks, attn_lds(), stream, fn)) return e;
@@ -645,13 +651,27 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   if (batch <= 0) return fail(DV_EINVAL, "%s: batch = %d", fn, batch);
   const int d = L->d, F = L->F, h = L->h, dh = L->dh, n = L->n_ctx;
   if (F <= 0 || h <= 0) return fail(DV_EINVAL, "%s: F = %d, h = %d", fn, F, h);
-  if (int e = check_nctx(fn, n)) return e;
+  // The full step with the KV append (W^K and W^V given): the current token's k and
+  // v go to row n_ctx of every head's cache, and n_ctx + 1 rows are attended.
+  const bool append = L->Wk != nullptr || L->Wv != nullptr;
+  if (append) {
+    CHECK_PTR(L->Wk); CHECK_PTR(L->Wv); CHECK_ALIGN(L->Wk); CHECK_ALIGN(L->Wv);
+    if (n < 0) return fail(DV_EINVAL, "%s: n_ctx = %d", fn, n);
+  }
+  const int n_att = n + (append ? 1 : 0);
+  if (int e = check_nctx(fn, n_att)) return e;
+  if (L->kv_cap < 0) return fail(DV_EINVAL, "%s: kv_cap = %d", fn, L->kv_cap);
+  const int kv_cap = L->kv_cap ? L->kv_cap : n;
+  if (kv_cap < n_att)
+    return fail(DV_EINVAL, "%s: kv_cap = %d rows cannot hold %d%s", fn, kv_cap, n_att,
+                append ? " (the cached rows and the appended one)" : "");
   if (!(valid_dtype(L->wdt) || L->wdt == DV_FP8) || !valid_dtype(L->kvdt))
     return fail(DV_EINVAL, "%s: bad dtype", fn);
   if (!valid_act(L->act)) return fail(DV_EINVAL, "%s: bad activation %d", fn, L->act);
   if (L->wdt == DV_FP8) {
     CHECK_PTR(L->W1s); CHECK_PTR(L->W2s); CHECK_PTR(L->Wqs); CHECK_PTR(L->Wos);
     CHECK_ALIGN(L->W1s); CHECK_ALIGN(L->W2s); CHECK_ALIGN(L->Wqs); CHECK_ALIGN(L->Wos);
+    if (append) { CHECK_PTR(L->Wks); CHECK_PTR(L->Wvs); CHECK_ALIGN(L->Wks); CHECK_ALIGN(L->Wvs); }
     if (L->d % 16 != 0) return fail(DV_EALIGN, "%s: fp8 rows need d %% 16 == 0 (d = %d)", fn, L->d);
   }
   if (!(L->scale == L->scale)) return fail(DV_EINVAL, "%s: scale is NaN", fn);
@@ -711,9 +731,20 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     add_rowdot(a1.rowdot, nx->A_M, d, pwdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r);
     add_rowdot(a1.rowdot, nx->A_A, d, pwdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r);
   }
+  if (append) {   // every head's k and v, stored at row n of its cache
+    const RowList LK = make_list(nullptr, nullptr, h, dh, h);
+    const size_t row_n = (size_t)n * dh * esize(L->kvdt);
+    add_rowdot(a1.rowdot, L->Wk, d, wdt, LK, nullptr, 0, fp8 ? L->Wks : nullptr,
+               static_cast<char*>(L->K) + row_n);
+    add_rowdot(a1.rowdot, L->Wv, d, wdt, LK, nullptr, 0, fp8 ? L->Wvs : nullptr,
+               static_cast<char*>(L->V) + row_n);
+    a1.rowdot.store_ld_b = (long long)h * kv_cap * dh;
+    a1.rowdot.store_ld_item = (long long)kv_cap * dh;
+    a1.rowdot.store_dt = L->kvdt == DV_BF16 ? W_BF16 : W_F32;
+  }
   finish_rowdot(a1.rowdot, y_in, batch, d, up(P.zero), P.zero_words);
-  if (int e = launch(T_ROWDOT | (fp8 ? T_FP8 : 0), bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot),
-                     stream, fn))
+  if (int e = launch(T_ROWDOT | (fp8 ? T_FP8 : 0) | (append ? T_KV : 0), bt, a1, a1.rowdot.blocks,
+                     rowdot_lds(a1.rowdot), stream, fn))
     return e;
 
   // After the row dots, the rest of the layer: attention over the cache for S_A; one
@@ -736,7 +767,8 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   // the single launch against 22 + 25 us for the attention and a row-sum launch)
   if (!nx && max_count_a > 0 && !fp8) {
     PhaseArgs f = zero_args();
-    setup_attn(f.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n, dh, LH, L->scale,
+    setup_attn(f.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n_att, kv_cap, dh, LH,
+               L->scale,
                fp(P.part), nullptr, nullptr, 0, 1);
     f.attn.done_ctr = up(P.done);
     f.b_attn = 0;
@@ -758,7 +790,8 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   // the next layer's top-k, whose last classify block of each row resolves it.
   PhaseArgs a2 = zero_args();
   if (max_count_a > 0)
-    setup_attn(a2.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n, dh, LH, L->scale,
+    setup_attn(a2.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n_att, kv_cap, dh, LH,
+               L->scale,
                fp(P.part), t_attn, fp(P.o), cap_a * dh, nx ? 1 : 0);
   a2.b_attn = 0;
   a2.b_axpy = a2.attn.blocks;

@@ -21,6 +21,8 @@ namespace dv {
 constexpr int kThreads = 256;            // threads per block, every kernel
 constexpr int kWaves = kThreads / 64;    // wave64
 constexpr int kMaxSeg = 4;               // segments per rowdot / axpy task
+constexpr int kMaxRowdotSeg = 6;         // row-dot segments of a launch that also stores
+                                         //   the current token's k and v (T_KV)
 constexpr int kMaxChunks = 32;           // row chunks per axpy segment (partials bound)
 constexpr int kAxSliceLanes = 32;        // lanes across the columns of one axpy slice
 constexpr int kAxGroups = 8;             // row groups (half-waves) per axpy block
@@ -60,8 +62,14 @@ struct RowdotSeg {
 };
 
 struct RowdotTask {
-  RowdotSeg seg[kMaxSeg];
-  const float* seg_scale[kMaxSeg];   // W_FP8 segments: scale of row (item*expand + e)
+  RowdotSeg seg[kMaxRowdotSeg];      // launches without T_KV use the first kMaxSeg
+  const float* seg_scale[kMaxRowdotSeg];   // W_FP8 segments: scale of row (item*expand + e)
+  // T_KV segments: instead of out, the dot of row (item*expand + e) with token b is
+  // stored in the cache's type at seg_store + b*store_ld_b + item*store_ld_item + e
+  void* seg_store[kMaxRowdotSeg];
+  long long store_ld_b;
+  long long store_ld_item;
+  int store_dt;            // W_BF16 or W_F32
   int nseg;
   const float* y;          // [batch][d]
   int batch, d;
@@ -122,10 +130,11 @@ struct AxpyTask {
 struct AttnTask {
   const float* q;          // q[b * q_ld + s*dh + c]
   int q_ld;
-  const void* K;           // [batch][h][n][dh]
+  const void* K;           // [batch][h][cap][dh]; rows 0..n-1 are attended
   const void* V;
   int kvdt;
   int batch, h, n, dh;
+  int cap;                 // rows per (token, head) in K and V
   RowList heads;           // expand = 1, items = h
   float scale;
   int nsplit, per;         // key splits per (token, slot), keys per split
@@ -179,10 +188,12 @@ struct ZeroTask {
 
 // T_WAIT: the row sums of the launch may wait for in-launch producers before their
 // second source (see AxpySeg::wait_ctr) and combine attention pieces while staging.
+// T_KV: the row dots of the launch include the current token's k and v, stored into
+// the cache (RowdotTask::seg_store).
 // T_FP8: the row dots and row sums of the launch may hold fp8 rows; the launches
 // without it carry no fp8 code, which keeps their bf16 loops as tight as before.
 enum : int { T_ROWDOT = 1, T_ATTN = 2, T_AXPY = 4, T_HIST = 8, T_CLASSIFY = 16, T_WAIT = 32,
-             T_ZERO = 64, T_FP8 = 128 };
+             T_ZERO = 64, T_FP8 = 128, T_KV = 256 };
 
 struct PhaseArgs {
   RowdotTask rowdot;

@@ -222,18 +222,45 @@ __device__ __forceinline__ void find_digit(const uint32_t (&hv)[PT], uint32_t re
 // rowdot                                                                       //
 // --------------------------------------------------------------------------- //
 
+template <int NSEG>
 __device__ __forceinline__ RowdotSeg rd_seg(const RowdotTask& T, int s) {
-  switch (s) {
-    case 0: return T.seg[0];
-    case 1: return T.seg[1];
-    case 2: return T.seg[2];
-    default: return T.seg[3];
+  if constexpr (NSEG > kMaxSeg) {
+    switch (s) {
+      case 0: return T.seg[0];
+      case 1: return T.seg[1];
+      case 2: return T.seg[2];
+      case 3: return T.seg[3];
+      case 4: return T.seg[4];
+      default: return T.seg[5];
+    }
+  } else {
+    switch (s) {
+      case 0: return T.seg[0];
+      case 1: return T.seg[1];
+      case 2: return T.seg[2];
+      default: return T.seg[3];
+    }
   }
 }
-// fp8 row scales of segment s (kept outside RowdotSeg, whose by-value selection the
-// compiler keeps in registers only while the struct stays this size)
-__device__ __forceinline__ const float* rd_scale(const RowdotTask& T, int s) {
-  return s == 0 ? T.seg_scale[0] : s == 1 ? T.seg_scale[1] : s == 2 ? T.seg_scale[2] : T.seg_scale[3];
+// Entry s (wave-uniform) of a per-segment pointer array, by selects: fp8 row scales
+// and cache stores are kept outside RowdotSeg, whose by-value selection the compiler
+// keeps in registers only while the struct stays this size.
+// (written as one conditional chain: a loop of selects is folded back into a dynamic
+// index of the kernel argument, which the compiler then copies to scratch)
+template <int NSEG, class P>
+__device__ __forceinline__ P rd_pick(const P (&a)[kMaxRowdotSeg], int s) {
+  if constexpr (NSEG > kMaxSeg)
+    return s == 0 ? a[0] : s == 1 ? a[1] : s == 2 ? a[2] : s == 3 ? a[3] : s == 4 ? a[4] : a[5];
+  else
+    return s == 0 ? a[0] : s == 1 ? a[1] : s == 2 ? a[2] : a[3];
+}
+
+// float -> bfloat16 bits, rounded to nearest with ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
 }
 
 // acc[b] += row . y_b for the lane's share of one bf16 row of d elements.
@@ -338,15 +365,16 @@ __device__ __forceinline__ void rowdot_f32(const float4* __restrict__ rp, const 
   }
 }
 
-template <int BT, bool FP8>
+template <int BT, bool FP8, bool KV>
 __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float* lds) {
+  constexpr int NSEG = KV ? kMaxRowdotSeg : kMaxSeg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Counters and histograms used by later launches of the same call start at zero.
   for (int i = blk * kThreads + tid; i < T.zero_words; i += T.blocks * kThreads) T.zero_ptr[i] = 0u;
 
   int total_cap = 0;
 #pragma unroll
-  for (int s = 0; s < kMaxSeg; ++s) total_cap += (s < T.nseg) ? T.seg[s].cap : 0;
+  for (int s = 0; s < NSEG; ++s) total_cap += (s < T.nseg) ? T.seg[s].cap : 0;
   const int total_waves = T.blocks * kWaves;
   const int gw = blk * kWaves + wave;
   const int d = T.d;
@@ -364,11 +392,11 @@ __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float*
     for (int g = gw; g < total_cap; g += total_waves) {
       int s = 0, r = g;
 #pragma unroll
-      for (int i = 0; i < kMaxSeg - 1; ++i) {
+      for (int i = 0; i < NSEG - 1; ++i) {
         const int c = T.seg[i].cap;
         if (s == i && r >= c) { r -= c; s = i + 1; }
       }
-      const RowdotSeg S = rd_seg(T, s);
+      const RowdotSeg S = rd_seg<NSEG>(T, s);
       const int ex = S.rows.expand;
       const int slot = (ex == 1) ? r : r / ex;
       const int e = (ex == 1) ? 0 : r - slot * ex;
@@ -389,7 +417,7 @@ __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float*
             const uint4* rp = reinterpret_cast<const uint4*>(
                 static_cast<const uint8_t*>(S.W) + row * S.row_stride);
             rowdot_fp8<BT, 12>(rp, lds, d, nb, lane, acc);
-            rscale = rd_scale(T, s)[row];
+            rscale = rd_pick<NSEG>(T.seg_scale, s)[row];
           }
         } else {
           const float4* rp = reinterpret_cast<const float4*>(
@@ -400,9 +428,22 @@ __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float*
 #pragma unroll
       for (int b = 0; b < BT; ++b) acc[b] = FP8 ? wave_sum(acc[b]) * rscale : wave_sum(acc[b]);
       if (lane == 0) {
+        void* st = nullptr;
+        if constexpr (KV) st = rd_pick<NSEG>(T.seg_store, s);
+        if (st) {   // the current token's k or v: stored into its cache row
+          const long long o = (long long)item * T.store_ld_item + e;
 #pragma unroll
-        for (int b = 0; b < BT; ++b)
-          if (b < nb) S.out[(size_t)(b0 + b) * S.out_ld + r] = acc[b];
+          for (int b = 0; b < BT; ++b) {
+            if (b >= nb) continue;
+            const long long ob = o + (long long)(b0 + b) * T.store_ld_b;
+            if (T.store_dt == W_BF16) static_cast<uint16_t*>(st)[ob] = f32_to_bf16_rne(acc[b]);
+            else static_cast<float*>(st)[ob] = acc[b];
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < BT; ++b)
+            if (b < nb) S.out[(size_t)(b0 + b) * S.out_ld + r] = acc[b];
+        }
       }
     }
   }
@@ -872,7 +913,7 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
   float* gl = lds + 64;              // [NG] group sum
   float* go = lds + 128;             // [NG][dh] group p.V; NG * dh = 256 * VEC <= 2048
 
-  const size_t row0 = ((size_t)b * T.h + head) * (size_t)T.n + k0;   // first key row
+  const size_t row0 = ((size_t)b * T.h + head) * (size_t)T.cap + k0;   // first key row
   float qv[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v)
@@ -1290,7 +1331,7 @@ __device__ __forceinline__ void phase_body(const PhaseArgs& a, float* lds) {
   }
   if constexpr ((FLAGS & T_ROWDOT) != 0) {
     if (blk >= a.b_rowdot && blk < a.b_rowdot + a.rowdot.blocks) {
-      rowdot_task<BT, (FLAGS & T_FP8) != 0>(a.rowdot, blk - a.b_rowdot, lds);
+      rowdot_task<BT, (FLAGS & T_FP8) != 0, (FLAGS & T_KV) != 0>(a.rowdot, blk - a.b_rowdot, lds);
       return;
     }
   }
@@ -1343,9 +1384,23 @@ __global__ __launch_bounds__(kThreads) void rowdot_kernel(PhaseArgs a) {
   phase_body<FLAGS, BT>(a, lds);
 }
 
+// The row dots with the KV stores, one token per block: held to 3 waves per SIMD like
+// the plain row dots (the store path would otherwise take it past 168 registers, to 2;
+// the cap costs two spilled values outside the load loop).  Larger token tiles run
+// at 2 waves either way and use rowdot_kernel.
+template <int FLAGS, int BT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void rowdot_kv_kernel(PhaseArgs a) {
+  extern __shared__ float lds[];
+  phase_body<FLAGS, BT>(a, lds);
+}
+
 template <int FLAGS, int BT>
 static int launch_t(const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
-  if constexpr ((FLAGS & ~T_FP8) == T_ROWDOT)
+  if constexpr ((FLAGS & ~T_FP8) == (T_ROWDOT | T_KV) && BT == 1)
+    hipLaunchKernelGGL((rowdot_kv_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
+                       static_cast<hipStream_t>(stream), a);
+  else if constexpr ((FLAGS & ~(T_FP8 | T_KV)) == T_ROWDOT)
     hipLaunchKernelGGL((rowdot_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
                        static_cast<hipStream_t>(stream), a);
   else if constexpr (BT == 1)
@@ -1374,6 +1429,9 @@ int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes,
     case T_ATTN | T_AXPY | T_WAIT: return launch_bt<T_ATTN | T_AXPY | T_WAIT>(bt, a, grid, lds_bytes, stream);
     case T_AXPY | T_CLASSIFY: return launch_bt<T_AXPY | T_CLASSIFY>(bt, a, grid, lds_bytes, stream);
     case T_ROWDOT | T_FP8: return launch_bt<T_ROWDOT | T_FP8>(bt, a, grid, lds_bytes, stream);
+    case T_ROWDOT | T_KV: return launch_bt<T_ROWDOT | T_KV>(bt, a, grid, lds_bytes, stream);
+    case T_ROWDOT | T_KV | T_FP8:
+      return launch_bt<T_ROWDOT | T_KV | T_FP8>(bt, a, grid, lds_bytes, stream);
     case T_AXPY | T_FP8: return launch_bt<T_AXPY | T_FP8>(bt, a, grid, lds_bytes, stream);
     case T_AXPY | T_CLASSIFY | T_FP8:
       return launch_bt<T_AXPY | T_CLASSIFY | T_FP8>(bt, a, grid, lds_bytes, stream);
@@ -1391,7 +1449,10 @@ template <int FLAGS, int BT>
 static int occupancy_t(int lds_bytes) {
   int n = 0;
   hipError_t e;
-  if constexpr ((FLAGS & ~T_FP8) == T_ROWDOT)
+  if constexpr ((FLAGS & ~T_FP8) == (T_ROWDOT | T_KV) && BT == 1)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rowdot_kv_kernel<FLAGS, BT>, kThreads,
+                                                     lds_bytes);
+  else if constexpr ((FLAGS & ~(T_FP8 | T_KV)) == T_ROWDOT)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rowdot_kernel<FLAGS, BT>, kThreads, lds_bytes);
   else if constexpr (BT == 1)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, phase_kernel<FLAGS, BT>, kThreads, lds_bytes);

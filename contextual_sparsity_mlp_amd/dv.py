@@ -46,7 +46,9 @@ class LayerStruct(ctypes.Structure):
                [(n, ctypes.c_void_p) for n in ("W1t", "W2t", "Wq", "Wo", "K", "V",
                                                 "A_M", "B_M", "A_A", "B_A")] + \
                [("act", ctypes.c_int), ("pwdt", ctypes.c_int)] + \
-               [(n, ctypes.c_void_p) for n in ("W1s", "W2s", "Wqs", "Wos")]
+               [(n, ctypes.c_void_p) for n in ("W1s", "W2s", "Wqs", "Wos")] + \
+               [(n, ctypes.c_void_p) for n in ("Wk", "Wv", "Wks", "Wvs")] + \
+               [("kv_cap", ctypes.c_int)]
 
 
 _lib = None
@@ -186,19 +188,32 @@ class Layer:
     """A dv_layer built from a layer's tensors; keeps them alive while in use."""
 
     def __init__(self, W1t, W2t, Wq, Wo, K, V, A_M=None, B_M=None, A_A=None, B_A=None, *,
-                 k_m=0, k_a=0, scale=1.0, act=DV_ACT_RELU, row_scales=None):
-        """row_scales = (W1s, W2s, Wqs, Wos) for fp8 weights (uint8 E4M3 codes)."""
-        self.tensors = (W1t, W2t, Wq, Wo, K, V, A_M, B_M, A_A, B_A, row_scales)
+                 k_m=0, k_a=0, scale=1.0, act=DV_ACT_RELU, row_scales=None, Wk=None, Wv=None,
+                 kv_scales=None, n_ctx=None):
+        """row_scales = (W1s, W2s, Wqs, Wos) for fp8 weights (uint8 E4M3 codes).
+
+        K, V are [batch][h][kv_cap][dh]; n_ctx (default kv_cap) rows are the cache.
+        Wk, Wv (with kv_scales = (Wks, Wvs) for fp8) make each decode step append the
+        current token's k and v at row n_ctx; advance with ``set_n_ctx``."""
+        self.tensors = (W1t, W2t, Wq, Wo, K, V, A_M, B_M, A_A, B_A, row_scales, Wk, Wv, kv_scales)
         r = A_M.shape[0] if A_M is not None else 0
         rs = row_scales if row_scales is not None else (None, None, None, None)
+        ks = kv_scales if kv_scales is not None else (None, None)
         self.s = LayerStruct(d=W1t.shape[1], F=W1t.shape[0], h=Wq.shape[0], dh=Wq.shape[1],
-                             n_ctx=K.shape[2], r=r, k_m=int(k_m), k_a=int(k_a),
+                             n_ctx=K.shape[2] if n_ctx is None else int(n_ctx), r=r,
+                             k_m=int(k_m), k_a=int(k_a),
                              wdt=_dtype(W1t), kvdt=_dtype(K), scale=float(scale),
                              W1t=_ptr(W1t), W2t=_ptr(W2t), Wq=_ptr(Wq), Wo=_ptr(Wo), K=_ptr(K),
                              V=_ptr(V), A_M=_ptr(A_M), B_M=_ptr(B_M), A_A=_ptr(A_A), B_A=_ptr(B_A),
                              act=int(act),
                              pwdt=_dtype(A_M) if A_M is not None else DV_BF16,
-                             W1s=_ptr(rs[0]), W2s=_ptr(rs[1]), Wqs=_ptr(rs[2]), Wos=_ptr(rs[3]))
+                             W1s=_ptr(rs[0]), W2s=_ptr(rs[1]), Wqs=_ptr(rs[2]), Wos=_ptr(rs[3]),
+                             Wk=_ptr(Wk), Wv=_ptr(Wv), Wks=_ptr(ks[0]), Wvs=_ptr(ks[1]),
+                             kv_cap=K.shape[2])
+
+    def set_n_ctx(self, n: int):
+        """Rows of the cache the next step reads (the append goes to row n)."""
+        self.s.n_ctx = int(n)
 
 
 def decode_layer(layer: Layer, next_layer, y_in, y_out, idx_m, count_m, max_count_m, idx_a, count_a,

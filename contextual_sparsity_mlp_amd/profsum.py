@@ -43,7 +43,7 @@ def stats(src: str, trace: str, out: str, command: str):
     rows = list(csv.DictReader(open(src)))
     # fp8 weight rows: the row dots and the output row sum carry the fp8 flag (128),
     # and without a next layer the attention runs alone before the row sum
-    fp8 = any(re.search(r"(?:phase|rowdot)_kernel<129, ", r["Name"]) for r in rows)
+    fp8 = any(re.search(r"(?:phase|rowdot|rowdot_kv)_kernel<129, ", r["Name"]) for r in rows)
     weights = "fp8 (E4M3) weight rows" if fp8 else "bf16 weights"
     lines = [f"# rocprofv3 kernel summary: OPT-175B-shaped decode layer, batch 1, {weights}", "",
              f"Command: `{command}`", "",
@@ -60,7 +60,7 @@ def stats(src: str, trace: str, out: str, command: str):
     groups = {}
     seq = []
     for r in sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"])):
-        m = re.search(r"(?:phase|rowdot)_kernel<(\d+), (\d+)>", r["Kernel_Name"])
+        m = re.search(r"(?:phase|rowdot|rowdot_kv)_kernel<(\d+), (\d+)>", r["Kernel_Name"])
         if not m:
             continue
         blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
@@ -134,7 +134,7 @@ def _per_slot(rows):
     copy = [v for n, g, v in rows if "copyBuffer" in n]
     slots = {}
     for slot, flags in SLOT_FLAGS.items():
-        vals = [(g, v) for n, g, v in rows if re.search(rf"(?:phase|rowdot)_kernel<{flags}, 1>", n)]
+        vals = [(g, v) for n, g, v in rows if re.search(rf"(?:phase|rowdot|rowdot_kv)_kernel<{flags}, 1>", n)]
         if not vals:
             continue
         # the decode launches are the most frequent grid size of that kernel

@@ -99,7 +99,8 @@ typedef struct {
   int F;            /* MLP neurons (4d in OPT) */
   int h;            /* attention heads */
   int dh;           /* head width */
-  int n_ctx;        /* cached tokens per sequence */
+  int n_ctx;        /* cached tokens per sequence (DECODE_LAYER: may be 0, for a step
+                     * with the KV append on an empty cache) */
   int r;            /* predictor rank */
   int N;            /* items scored (PREDICT, SELECT_TOPK) */
   int max_count_m;  /* capacity of the neuron index list */
@@ -157,7 +158,8 @@ typedef struct {
   dv_dtype wdt, kvdt;
   float scale;             /* attention logit scale (1.0 = Eq. (2) as written) */
   const void *W1t, *W2t, *Wq, *Wo;
-  const void *K, *V;       /* [batch][h][n_ctx][dh] */
+  void *K, *V;             /* [batch][h][kv_cap][dh]; rows 0..n_ctx-1 are the cache (written
+                            * only by the KV append, at row n_ctx) */
   const void *A_M, *B_M;   /* neuron predictor: [r][d], [r][F] */
   const void *A_A, *B_A;   /* head predictor:   [r][d], [r][h] */
   int act;                 /* sigma of this layer's MLP: dv_act (DV_ACT_RELU = 0) */
@@ -165,6 +167,20 @@ typedef struct {
   /* wdt == DV_FP8: one fp32 scale per row of W1t [F], W2t [F], Wq [h*dh], Wo [h*dh]
    * (16-byte aligned; NULL otherwise) */
   const float *W1s, *W2s, *Wqs, *Wos;
+  /* The full decode step with the KV append (KV-cache blog page, figure (b): the
+   * current token's key and value join the cache and are attended with it).  When Wk
+   * and Wv are both non-NULL, k_i = y W_i^K and v_i = y W_i^V of EVERY head i (a
+   * reading: the pages say nothing of skipped heads, and Eq. (2)'s X holds every
+   * token for every head) are stored, rounded to kvdt (bf16: nearest, ties to even),
+   * at row n_ctx of each (token, head) cache; the heads of S_A then attend over rows
+   * 0..n_ctx, the stored current row among them.  Wk, Wv: [h][dh][d] in wdt like Wq
+   * (fp8: scales Wks, Wvs [h*dh], 16-byte aligned).  Both NULL: no append, rows
+   * 0..n_ctx-1 attended (n_ctx may then not be 0).  The caller advances n_ctx between
+   * steps.  Calls that append to the same cache rows must not overlap. */
+  const void *Wk, *Wv;
+  const float *Wks, *Wvs;
+  int kv_cap;              /* rows per (token, head) of K and V; 0 means n_ctx.  With the
+                            * append kv_cap > n_ctx (DV_EINVAL otherwise) */
 } dv_layer;
 
 /* A5 - one decode layer with the look-ahead predictor (Deja Vu page, section 1 and

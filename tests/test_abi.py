@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(dv.EXPORTS), f"header {names} vs binding {dv.EXPORTS}"
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.dv_version() == 102
+    assert lib.dv_version() == 103
 
 
 def test_library_has_gfx950_code():
@@ -164,6 +164,16 @@ def _layer(**over):
     (dict(), dict(), dict(ws_bytes=64), dv.DV_EWORKSPACE),
     (dict(n_ctx=0), dict(), dict(), dv.DV_EINVAL),
     (dict(act=5), dict(), dict(), dv.DV_EINVAL),
+    # the KV append: both W^K and W^V, a cache row to append to, aligned pointers
+    (dict(Wk=P), dict(), dict(), dv.DV_EINVAL),
+    (dict(Wk=P, Wv=P), dict(), dict(), dv.DV_EINVAL),                     # kv_cap 0 = n_ctx: no room
+    (dict(Wk=P, Wv=P, kv_cap=32), dict(), dict(), dv.DV_EINVAL),
+    (dict(Wk=P, Wv=P, kv_cap=33, n_ctx=-1), dict(), dict(), dv.DV_EINVAL),
+    (dict(Wk=P, Wv=BAD, kv_cap=33), dict(), dict(), dv.DV_EALIGN),
+    (dict(wdt=dv.DV_FP8, W1s=P, W2s=P, Wqs=P, Wos=P, Wk=P, Wv=P, kv_cap=33), dict(), dict(),
+     dv.DV_EINVAL),                                                         # fp8 W^K without scales
+    (dict(kv_cap=16), dict(), dict(), dv.DV_EINVAL),                      # cache smaller than n_ctx
+    (dict(kv_cap=-1), dict(), dict(), dv.DV_EINVAL),
 ])
 def test_decode_layer_rejects(lo, no, args, code):
     a = dict(batch=1, y_in=P, y_out=P, idx_m=P, count_m=P, max_count_m=154, idx_a=P, count_a=P,
