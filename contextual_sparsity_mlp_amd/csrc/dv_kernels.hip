@@ -887,19 +887,19 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
 // saw no key) and the splits of a (token, head) merge the same way.
 template <int WT>
 __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds) {
-  constexpr int VEC = (WT == W_BF16) ? 8 : 4;
-  constexpr int U = 2;
+  constexpr int VEC = (WT == W_BF16) ? 8 : 4;   // elements per 16-byte load
+  constexpr int U = 4;                           // key rows in flight per key group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = T.heads.host_count;
   const int split = blk % T.nsplit;
   const int rest = blk / T.nsplit;
   const int slot = rest % cap;
   const int b = rest / cap;
-  if (slot >= list_slots(T.heads)) return;
-  const int head = T.heads.idx ? T.heads.idx[slot] : slot;
-  if ((unsigned)head >= (unsigned)T.h) return;   // contributes nothing; W^O skips it too
-
   const int dh = T.dh;
+  // the list count, the head index (slot < capacity: readable) and q are independent
+  // loads, issued together
+  const int nslots = list_slots(T.heads);
+  const int head = T.heads.idx ? T.heads.idx[slot] : slot;
   const int LPK = dh / VEC;          // lanes per key row
   const int KPW = 64 / LPK;          // keys per wave-load
   const int NG = kWaves * KPW;       // key groups in the block
@@ -913,35 +913,52 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
   float* gl = lds + 64;              // [NG] group sum
   float* go = lds + 128;             // [NG][dh] group p.V; NG * dh = 256 * VEC <= 2048
 
-  const size_t row0 = ((size_t)b * T.h + head) * (size_t)T.cap + k0;   // first key row
   float qv[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v)
     qv[v] = T.scale * T.q[(size_t)b * T.q_ld + (size_t)slot * dh + dg * VEC + v];
+  if (slot >= nslots) return;
+  if ((unsigned)head >= (unsigned)T.h) return;   // contributes nothing; W^O skips it too
+  const size_t row0 = ((size_t)b * T.h + head) * (size_t)T.cap + k0;   // first key row
+  constexpr int ESZ = (WT == W_BF16) ? 2 : 4;
+  const char* Kb = static_cast<const char*>(T.K);
+  const char* Vb = static_cast<const char*>(T.V);
 
   float m = -INFINITY, l = 0.f;
   float o[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) o[v] = 0.f;
   for (int base = 0; base < len; base += NG * U) {
-    float kv[U][VEC], vv[U][VEC];
+    // raw 16-byte loads of U key and value rows, widened only where they are used
+    uint4 kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = base + u * NG + grp;
       if (j < len) {
-        load_cols<VEC, WT>(T.K, (long long)(row0 + j) * dh + dg * VEC, kv[u]);
-        load_cols<VEC, WT>(T.V, (long long)(row0 + j) * dh + dg * VEC, vv[u]);
+        const size_t off = ((row0 + j) * (size_t)dh + (size_t)dg * VEC) * ESZ;
+        kr[u] = ld_stream(reinterpret_cast<const uint4*>(Kb + off));
+        vr[u] = ld_stream(reinterpret_cast<const uint4*>(Vb + off));
       } else {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) { kv[u][v] = 0.f; vv[u][v] = 0.f; }
+        kr[u] = make_uint4(0u, 0u, 0u, 0u);
+        vr[u] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
+    auto widen16 = [](uint4 x, float (&f)[VEC]) {
+      if constexpr (WT == W_BF16) {
+        unpack8(x, f);
+      } else {
+        f[0] = __uint_as_float(x.x); f[1] = __uint_as_float(x.y);
+        f[2] = __uint_as_float(x.z); f[3] = __uint_as_float(x.w);
+      }
+    };
     float t[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      float kf[VEC];
+      widen16(kr[u], kf);
       float p = 0.f;
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) p = fmaf(qv[v], kv[u][v], p);
+      for (int v = 0; v < VEC; ++v) p = fmaf(qv[v], kf[v], p);
       t[u] = p;
     }
 #pragma unroll
@@ -961,8 +978,10 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
         if (base + u * NG + grp < len) {
           const float p = expf(t[u] - mc);
           l += p;
+          float vf[VEC];
+          widen16(vr[u], vf);
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) o[v] = fmaf(p, vv[u][v], o[v]);
+          for (int v = 0; v < VEC; ++v) o[v] = fmaf(p, vf[v], o[v]);
         }
       }
       m = mc;
