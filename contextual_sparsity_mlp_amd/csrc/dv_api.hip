@@ -750,18 +750,19 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   // After the row dots, the rest of the layer: attention over the cache for S_A; one
   // row sum y_out = y_in + sum_{S_M} ReLU(a) W2 rows + sum_{S_A} o W^O rows; and for
   // the next layer its predictor scores (with top-digit histograms) and top-k.
-  auto add_out = [&](AxpyTask& T, int target, const float* coef2, int nsplit) {
-    add_axpy2(T, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, act_code(L->act), L->Wo, LQ, coef2,
+  auto add_out = [&](AxpyTask& T, int target) {
+    add_axpy2(T, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, act_code(L->act), L->Wo, LQ, fp(P.o),
               cap_a * dh, A_NONE,
               d, fp(P.p_wo), t_wo, y_out, d, y_in, nullptr, d, 0, target,
               fp8 ? L->W2s : nullptr, fp8 ? L->Wos : nullptr);
-    T.seg[T.nseg - 1].coef2_nsplit = nsplit;
   };
 
   // Without a next layer, one launch when its blocks fit one resident round: every
   // row-sum block streams its W2 rows, then waits for the attention blocks (which come
-  // first in block order) and combines their split pieces into the head outputs as it
-  // stages the coefficients of its W^O rows.  The attention hides under the W2 stream.
+  // first in block order; the last key split of each head combines the splits into
+  // o) and stages o as the coefficients of its W^O rows.  The attention, its combine
+  // included, hides under the W2 stream.  (Combining the splits in each row-sum block
+  // instead, as it stages its W^O coefficients, measured 48.3 us against 46.1.)
   // (fp8 rows halve the column slices, so each row-sum block would stream as many rows
   // as at bf16 and the launch becomes bound by each block's chain: measured 60 us for
   // the single launch against 22 + 25 us for the attention and a row-sum launch)
@@ -769,11 +770,11 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     PhaseArgs f = zero_args();
     setup_attn(f.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n_att, kv_cap, dh, LH,
                L->scale,
-               fp(P.part), nullptr, nullptr, 0, 1);
+               fp(P.part), t_attn, fp(P.o), cap_a * dh, 1);
     f.attn.done_ctr = up(P.done);
     f.b_attn = 0;
     f.b_axpy = f.attn.blocks;
-    add_out(f.axpy, std::max(1, resident_blocks() - f.attn.blocks), fp(P.part), f.attn.nsplit);
+    add_out(f.axpy, std::max(1, resident_blocks() - f.attn.blocks));
     AxpySeg& S = f.axpy.seg[0];
     S.wait_ctr = up(P.done);
     S.wait_target = (uint32_t)f.attn.blocks;
@@ -812,7 +813,7 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
       return e;
   }
   PhaseArgs a3 = zero_args();
-  add_out(a3.axpy, default_axpy_blocks(), fp(P.o), 0);
+  add_out(a3.axpy, default_axpy_blocks());
   a3.axpy.batch = batch;
   int flags3 = T_AXPY | (fp8 ? T_FP8 : 0);
   if (nx) {

@@ -94,9 +94,6 @@ struct AxpySeg {
   const float* coef2;
   int coef2_ld;
   int act2;
-  int coef2_nsplit;        // > 0: coef2 holds attention pieces [batch][rows2.host_count]
-                           //   [coef2_nsplit][rows2.expand + 2] that are combined per
-                           //   row (rows2.expand = dh); 0: plain coefficients
   int ncols;               // output columns
   int vec;                 // elements per thread per row (8 bf16 / 4 f32 / 1 scalar)
   int nslices, nchunks, nbt;
@@ -141,8 +138,8 @@ struct AttnTask {
   float* part;             // [batch][cap][nsplit][dh + 2]: m, l, o[dh] of each split
                            //   (stored coherently)
   uint32_t* tickets;       // [batch][cap], zero on entry: the last split combines the
-                           //   pieces into o; nullptr: the consumer combines them
-  float* o;                // o[b * o_ld + s*dh + c] (with tickets), stored coherently
+                           //   pieces into o
+  float* o;                // o[b * o_ld + s*dh + c], stored coherently
   int o_ld;
   int blocks;              // batch * cap * nsplit
   uint32_t* done_ctr;      // optional: +1 per finished block, after its stores

@@ -43,7 +43,6 @@ static_assert(sizeof(PhaseArgs) <= 4096, "PhaseArgs exceeds the kernel-argument 
 // A row sum combining attention pieces keeps (weight, l) pairs of up to 9 head slots x
 // kMaxSplit splits per token where its row groups are later reduced (the LDS of a row
 // sum reserves kAxGroups * kAxSliceLanes * 8 floats per token there).
-static_assert(9 * kMaxSplit * 2 <= kAxGroups * kAxSliceLanes * 8, "attention-piece staging");
 
 // --------------------------------------------------------------------------- //
 // helpers                                                                      //
@@ -636,53 +635,15 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
 
     // one source's share of rows: coefficients staged in LDS a tile at a time, then the
     // row slices streamed by the row groups
-    auto rows_of = [&](auto merge, const RowList& L, const void* W, const float* cf, int cld,
-                       int rl, const float* sc, bool coherent, int nsplit, int nr) {
-      constexpr bool kMerge = decltype(merge)::value;
+    auto rows_of = [&](const RowList& L, const void* W, const float* cf, int cld, int rl,
+                       const float* sc, bool coherent, int nr) {
       const int per = (nr + S.nchunks - 1) / S.nchunks;
       const int r0 = min(chunk * per, nr);
       const int r1 = min(r0 + per, nr);
       const int ex = L.expand;
-      // with attention pieces a tile spans at most 9 head slots (ex = dh >= 32)
-      const int tile = kMerge ? min(kAxpyTile, 8 * ex) : kAxpyTile;
-      for (int t0 = r0; t0 < r1; t0 += tile) {
-        const int tn = min(tile, r1 - t0);
+      for (int t0 = r0; t0 < r1; t0 += kAxpyTile) {
+        const int tn = min(kAxpyTile, r1 - t0);
         __syncthreads();
-        int s_lo = 0, ns_t = 0;
-        if constexpr (kMerge) {
-          // Combine the key splits of the tile's head slots (Eq. (2)'s softmax over all
-          // keys): every split's (max, sum) loaded in one parallel pass, then per
-          // (token, slot) the weights exp(m_sp - max) and the denominator sum w l, in
-          // split order; wl[] holds (weight, l) pairs, the denominator replaces split
-          // 0's l.
-          s_lo = t0 / ex;
-          ns_t = (t0 + tn - 1) / ex - s_lo + 1;
-          float2* wl = reinterpret_cast<float2*>(red);     // [BT][ns_t][nsplit]
-          const int w2 = ex + 2;
-          for (int q = tid; q < BT * ns_t * nsplit; q += kThreads) {
-            const int sp = q % nsplit, j = (q / nsplit) % ns_t, b = q / (nsplit * ns_t);
-            float2 v = make_float2(-INFINITY, 0.f);
-            if (b < nb) {
-              const float* P = cf + (((size_t)(b0 + b) * L.host_count + s_lo + j) * nsplit + sp) * w2;
-              v = make_float2(ld_dev(P), ld_dev(P + 1));
-            }
-            wl[q] = v;
-          }
-          __syncthreads();
-          for (int q = tid; q < BT * ns_t; q += kThreads) {
-            float2* W = wl + (size_t)q * nsplit;
-            float MM = -INFINITY;
-            for (int sp = 0; sp < nsplit; ++sp) MM = fmaxf(MM, W[sp].x);
-            float LL = 0.f;
-            for (int sp = 0; sp < nsplit; ++sp) {
-              const float wgt = (W[sp].x == -INFINITY) ? 0.f : expf(W[sp].x - MM);
-              LL = fmaf(wgt, W[sp].y, LL);
-              W[sp].x = wgt;
-            }
-            W[0].y = LL;
-          }
-          __syncthreads();
-        }
         for (int i = tid; i < tn; i += kThreads) {
           const int rr = t0 + i;
           const int slot = (ex == 1) ? rr : rr / ex;
@@ -694,27 +655,8 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
           for (int b = 0; b < BT; ++b) {
             float c = 0.f;
             if (ok && b < nb) {
-              if constexpr (kMerge) {
-                // head output (slot, e): sum over splits of weight * p.V, over the
-                // denominator; the p.V pieces fetched in batches of independent loads
-                const float2* W = reinterpret_cast<const float2*>(red) +
-                                  ((size_t)b * ns_t + (slot - s_lo)) * nsplit;
-                const float* P = cf + ((size_t)(b0 + b) * L.host_count + slot) * nsplit * (ex + 2) + 2 + e;
-                constexpr int UB = 16;
-                float OO = 0.f;
-                for (int s0 = 0; s0 < nsplit; s0 += UB) {
-                  float ov[UB];
-  #pragma unroll
-                  for (int u = 0; u < UB; ++u) ov[u] = ld_dev(&P[(size_t)min(s0 + u, nsplit - 1) * (ex + 2)]);
-  #pragma unroll
-                  for (int u = 0; u < UB; ++u)
-                    if (s0 + u < nsplit) OO = fmaf(W[s0 + u].x, ov[u], OO);
-                }
-                c = OO / W[0].y;
-              } else {
-                const float* cp = &cf[(size_t)(b0 + b) * cld + rr];
-                c = coherent ? ld_dev(cp) : *cp;
-              }
+              const float* cp = &cf[(size_t)(b0 + b) * cld + rr];
+              c = coherent ? ld_dev(cp) : *cp;
               c = activate(c, rl);
               if constexpr (WT == W_FP8) c *= sc[item * ex + e];
             }
@@ -756,15 +698,11 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
         }
       }
     };
-    rows_of(std::false_type{}, S.rows, S.W, S.coef, S.coef_ld, S.act, sc1, false, 0, n1);
+    rows_of(S.rows, S.W, S.coef, S.coef_ld, S.act, sc1, false, n1);
     if (n2 > 0) {
+      // coefficients of the second source written in this launch: read coherently
       if (S.wait_ctr) wait_count(S.wait_ctr, S.wait_target);
-      if (S.coef2_nsplit > 0)
-        rows_of(std::true_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, sc2, true,
-                S.coef2_nsplit, n2);
-      else
-        rows_of(std::false_type{}, S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, sc2,
-                S.wait_ctr != nullptr, 0, n2);
+      rows_of(S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, sc2, S.wait_ctr != nullptr, n2);
     }
   }
 
@@ -1002,18 +940,16 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
       O = fmaf(w, go[g * dh + tid], O);
     }
   }
-  // Without tickets, this split's softmax piece (max, sum, p.V) is the result: the
-  // consumer of the head outputs combines the splits.  With tickets, the last split
-  // of each (token, head) to finish combines them here and stores o.
+  // Each split stores its softmax piece (max, sum, p.V); the last split of each
+  // (token, head) to finish combines them and stores o.
   const int w2 = dh + 2;
-  if (T.tickets != nullptr && T.nsplit == 1) {
+  if (T.nsplit == 1) {
     if (tid < dh) st_dev(&T.o[(size_t)b * T.o_ld + (size_t)slot * dh + tid], O / L);
     return;
   }
   float* P = T.part + (((size_t)b * cap + slot) * T.nsplit + split) * w2;
   if (tid < dh) st_dev(&P[2 + tid], O);
   if (tid == 0) { st_dev(&P[0], M); st_dev(&P[1], L); }
-  if (T.tickets == nullptr) return;
   int* flag = reinterpret_cast<int*>(lds + 128 + 2048);
   if (!arrive_last(&T.tickets[(size_t)b * cap + slot], (uint32_t)T.nsplit, flag)) return;
   // combine the splits: (max, sum) of every split staged in LDS with one parallel load,
