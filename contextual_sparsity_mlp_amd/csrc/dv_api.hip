@@ -282,8 +282,22 @@ void finish_rowdot(RowdotTask& T, const float* y, int batch, int d, uint32_t* ze
   const int per_cu = std::max(1, std::min(4, (160 * 1024) / std::max(1, T.bt_lds * d * 4)));
   T.blocks = std::min(want, device_cus() * per_cu);
   T.zero_ptr = zero; T.zero_words = nzero;
+  // A batch of tokens over bf16 rows runs on the matrix cores, which read each row
+  // once for up to 32 tokens (the wave-per-row path streams it once per token).
+  bool mfma = batch >= kMfmaMinBatch && d % kMfmaCols == 0;
+  for (int s = 0; s < T.nseg; ++s) mfma = mfma && T.seg[s].wdt == W_BF16 && !T.seg_store[s];
+  T.mfma_nt = 0;
+  if (mfma) {
+    T.mfma_nt = batch <= kMfmaRows ? 1 : 2;
+    int tiles = 0;
+    for (int s = 0; s < T.nseg; ++s) tiles += cdiv(T.seg[s].cap, kMfmaRows);
+    T.blocks = std::max(1, std::min(cdiv(tiles, kMfmaRT), device_cus() * kMfmaBlocksPerCu));
+  }
 }
-int rowdot_lds(const RowdotTask& T) { return T.bt_lds * T.d * 4; }
+int rowdot_lds(const RowdotTask& T) {
+  if (T.mfma_nt > 0) return kWaves * kMfmaRT * T.mfma_nt * 4 * 64 * 4;
+  return T.bt_lds * T.d * 4;
+}
 
 // Axpy segment over one row source, or two sources summed into the same columns
 // (second source: W2 != nullptr; same stride and dtype, rows after the first's).

@@ -38,6 +38,11 @@ constexpr int kCandTile = kThreads * kCandPerThread;
 constexpr int kResolveWords = 1536;      // bitmask words a resolving block keeps in LDS (N <= 49152)
 constexpr int kMaxSegs = 256;            // classify segments per row (N <= 524288)
 constexpr int kWordsPerThread = 4;       // bitmask words per thread when compacting
+constexpr int kMfmaRows = 16;            // matrix-core row dots: rows per tile and tokens per token tile
+constexpr int kMfmaRT = 2;               //   row tiles per block unit
+constexpr int kMfmaCols = 128;           //   columns per step (4 MFMA k-steps of 32); d % 128 == 0
+constexpr int kMfmaMinBatch = 2;         //   smallest batch that takes them
+constexpr int kMfmaBlocksPerCu = 4;      //   resident blocks per CU the grid is sized for
 
 enum : int { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };   // W_FP8: E4M3 codes, one scale per row
 enum : int { A_NONE = 0, A_RELU = 1, A_GELU = 2 };   // row-sum coefficient activations
@@ -74,6 +79,8 @@ struct RowdotTask {
   const float* y;          // [batch][d]
   int batch, d;
   int bt_lds;              // tokens of y staged in LDS at once (<= BT template)
+  int mfma_nt;             // > 0: the matrix-core row dots with mfma_nt token tiles of 16
+                           //   (bf16 rows only, no cache stores); 0: one wave per row
   int blocks;
   uint32_t* zero_ptr;      // counters used by later launches of the same call
   int zero_words;

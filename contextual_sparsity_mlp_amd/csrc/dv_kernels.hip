@@ -449,6 +449,171 @@ __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float*
 }
 
 // --------------------------------------------------------------------------- //
+// rowdot on the matrix cores (a batch of tokens, bf16 rows)                    //
+// --------------------------------------------------------------------------- //
+//
+// With B tokens the row dots are the product (B x d) . (d x rows) of Eq. (1)'s
+// y W1_S (and W^Q, predictor factor A): every selected row must be read once for
+// the whole batch, not once per token.  A block owns a unit of kMfmaRT tiles of
+// 16 rows; its four waves split the row length d in four and each runs
+// v_mfma_f32_16x16x32_bf16 over 128-column steps: the A operand is 16 rows x 32
+// columns of W (lane l holds 8 columns of row l % 16, loaded straight from HBM),
+// the B operand 32 columns x 16 tokens of y.  y stays fp32 in memory; each lane
+// splits its 8 values into hi = bf16(y) and mid = bf16(y - hi) and both products
+// go into the fp32 accumulator, so y is represented to about 2^-17 of its
+// magnitude: the predictor's scores keep an error far inside the fp32 summation
+// bound the top-k comparison relies on.  The four waves' partial tiles are summed
+// in LDS in wave order (deterministic) and stored like the wave-per-row path's
+// results.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// 8 fp32 values -> bf16 hi (nearest even) and mid = bf16(v - hi); v - hi is exact.
+__device__ __forceinline__ void split8(const float4& a, const float4& b, bf16x8& hi, bf16x8& mid) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 p = {v[2 * i], v[2 * i + 1]};
+    const bf16x2 h = __builtin_convertvector(p, bf16x2);
+    const f32x2 hf = __builtin_convertvector(h, f32x2);
+    const bf16x2 m = __builtin_convertvector(p - hf, bf16x2);
+    hi[2 * i] = h[0]; hi[2 * i + 1] = h[1];
+    mid[2 * i] = m[0]; mid[2 * i + 1] = m[1];
+  }
+}
+
+// Segment and first logical row of row tile t (tiles of 16 rows, segments in order);
+// s = -1 past the last tile.
+__device__ __forceinline__ void mfma_tile(const RowdotTask& T, int t, int& s, int& r0) {
+  s = -1; r0 = 0;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSeg; ++i) {
+    const int nt = (i < T.nseg) ? (T.seg[i].cap + kMfmaRows - 1) / kMfmaRows : 0;
+    if (s < 0 && t < base + nt) { s = i; r0 = (t - base) * kMfmaRows; }
+    base += nt;
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void rowdot_mfma_task(const RowdotTask& T, float* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = blockIdx.x * kThreads + tid; i < T.zero_words; i += gridDim.x * kThreads)
+    T.zero_ptr[i] = 0u;
+
+  int total_tiles = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSeg; ++i)
+    total_tiles += (i < T.nseg) ? (T.seg[i].cap + kMfmaRows - 1) / kMfmaRows : 0;
+  const int units = (total_tiles + kMfmaRT - 1) / kMfmaRT;
+  const int d = T.d;
+  const int nss = d / kMfmaCols;                 // 128-column steps (d % 128 == 0)
+  const int ss0 = wave * nss / kWaves, ss1 = (wave + 1) * nss / kWaves;
+  const int m = lane & 15, g = lane >> 4;        // operand row / token, 8-column group
+  constexpr int NACC = kMfmaRT * NT * 4;         // accumulator values per lane
+  float* red = lds;                              // [kWaves][NACC][64]
+
+  for (int tb0 = 0; tb0 < T.batch; tb0 += kMfmaRows * NT) {
+    for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+      // this lane's row of each tile (nullptr: outside the list, loads zeros)
+      const uint16_t* rp[kMfmaRT];
+#pragma unroll
+      for (int rt = 0; rt < kMfmaRT; ++rt) {
+        int s, r0;
+        mfma_tile(T, unit * kMfmaRT + rt, s, r0);
+        rp[rt] = nullptr;
+        if (s >= 0) {
+          const RowdotSeg S = rd_seg<kMaxSeg>(T, s);
+          const int r = r0 + m;
+          const int ex = S.rows.expand;
+          const int slot = (ex == 1) ? r : r / ex;
+          const int e = (ex == 1) ? 0 : r - slot * ex;
+          if (r < S.cap && slot < list_slots(S.rows)) {
+            const int item = S.rows.idx ? S.rows.idx[slot] : slot;
+            if ((unsigned)item < (unsigned)S.rows.items)
+              rp[rt] = static_cast<const uint16_t*>(S.W) + ((long long)item * ex + e) * S.row_stride +
+                       g * 8;
+          }
+        }
+      }
+      const float* yp[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = tb0 + nt * kMfmaRows + m;
+        yp[nt] = (n < T.batch) ? T.y + (size_t)n * d + g * 8 : nullptr;
+      }
+      f32x4 acc[kMfmaRT][NT];
+#pragma unroll
+      for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      for (int ss = ss0; ss < ss1; ++ss) {
+        const int c0 = ss * kMfmaCols;
+        uint4 w[kMfmaRT][4];
+#pragma unroll
+        for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            w[rt][j] = rp[rt] ? ld_stream(reinterpret_cast<const uint4*>(rp[rt] + c0 + 32 * j))
+                              : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float4 yv[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float4* q = reinterpret_cast<const float4*>(yp[nt] + c0 + 32 * j);
+            yv[2 * j] = yp[nt] ? q[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+            yv[2 * j + 1] = yp[nt] ? q[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bf16x8 hi, mid;
+            split8(yv[2 * j], yv[2 * j + 1], hi, mid);
+#pragma unroll
+            for (int rt = 0; rt < kMfmaRT; ++rt) {
+              const bf16x8 a = __builtin_bit_cast(bf16x8, w[rt][j]);
+              acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc[rt][nt], 0, 0, 0);
+              acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, mid, acc[rt][nt], 0, 0, 0);
+            }
+          }
+        }
+      }
+
+      // the four waves' partial tiles, summed in wave order
+      __syncthreads();
+#pragma unroll
+      for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            red[(wave * NACC + (rt * NT + nt) * 4 + i) * 64 + lane] = acc[rt][nt][i];
+      __syncthreads();
+      for (int x = tid; x < NACC * 64; x += kThreads) {
+        float v = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) v += red[wv * NACC * 64 + x];
+        // x = ((rt * NT + nt) * 4 + i) * 64 + ln: lane ln of the output tile holds
+        // row 4 * (ln / 16) + i for token ln % 16
+        const int ln = x & 63, i = (x >> 6) & 3, rtnt = x >> 8;
+        const int rt = rtnt / NT, nt = rtnt - rt * NT;
+        const int n = tb0 + nt * kMfmaRows + (ln & 15);
+        int s, r0;
+        mfma_tile(T, unit * kMfmaRT + rt, s, r0);
+        if (s < 0 || n >= T.batch) continue;
+        const RowdotSeg S = rd_seg<kMaxSeg>(T, s);
+        const int r = r0 + 4 * (ln >> 4) + i;
+        const int ex = S.rows.expand;
+        const int slot = (ex == 1) ? r : r / ex;
+        if (r < S.cap && slot < list_slots(S.rows)) S.out[(size_t)n * S.out_ld + r] = v;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------- //
 // axpy                                                                         //
 // --------------------------------------------------------------------------- //
 
@@ -1350,6 +1515,13 @@ void rowdot_kv_kernel(PhaseArgs a) {
   phase_body<FLAGS, BT>(a, lds);
 }
 
+// Matrix-core row dots (batch >= kMfmaMinBatch, bf16 rows): NT token tiles of 16.
+template <int NT>
+__global__ __launch_bounds__(kThreads) void rowdot_mfma_kernel(PhaseArgs a) {
+  extern __shared__ float lds[];
+  rowdot_mfma_task<NT>(a.rowdot, lds);
+}
+
 template <int FLAGS, int BT>
 static int launch_t(const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
   if constexpr ((FLAGS & ~T_FP8) == (T_ROWDOT | T_KV) && BT == 1)
@@ -1378,7 +1550,17 @@ static int launch_bt(int bt, const PhaseArgs& a, int grid, int lds_bytes, void* 
 
 int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
   switch (flags) {
-    case T_ROWDOT: return launch_bt<T_ROWDOT>(bt, a, grid, lds_bytes, stream);
+    case T_ROWDOT:
+      if (a.rowdot.mfma_nt > 0) {
+        if (a.rowdot.mfma_nt == 1)
+          hipLaunchKernelGGL((rowdot_mfma_kernel<1>), dim3(grid), dim3(kThreads), lds_bytes,
+                             static_cast<hipStream_t>(stream), a);
+        else
+          hipLaunchKernelGGL((rowdot_mfma_kernel<2>), dim3(grid), dim3(kThreads), lds_bytes,
+                             static_cast<hipStream_t>(stream), a);
+        return (int)hipGetLastError();
+      }
+      return launch_bt<T_ROWDOT>(bt, a, grid, lds_bytes, stream);
     case T_AXPY: return launch_bt<T_AXPY>(bt, a, grid, lds_bytes, stream);
     case T_ATTN | T_AXPY: return launch_bt<T_ATTN | T_AXPY>(bt, a, grid, lds_bytes, stream);
     case T_ATTN | T_AXPY | T_WAIT: return launch_bt<T_ATTN | T_AXPY | T_WAIT>(bt, a, grid, lds_bytes, stream);

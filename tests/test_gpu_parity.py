@@ -46,6 +46,12 @@ RAGGED = {
     "mixed-kv": LayerConfig("mixed-kv", 15, d=256, F=1024, h=4, dh=64, batch=5, n_ctx=130,
                             k_m=100, k_a=2, r=32, kvdtype="f32", union=True),
     "n1": LayerConfig("n1", 16, d=64, F=256, h=2, dh=32, batch=1, n_ctx=1, k_m=16, k_a=1, r=8),
+    # batches on the matrix-core row dots: a second, partial token tile (17) and a
+    # third token group (35)
+    "b17": LayerConfig("b17", 17, d=384, F=700, h=5, dh=32, batch=17, n_ctx=40, k_m=77, k_a=2,
+                       r=20, union=True),
+    "b35": LayerConfig("b35", 18, d=256, F=520, h=3, dh=64, batch=35, n_ctx=9, k_m=30, k_a=1,
+                       r=12, union=True),
 }
 SMALL = list(RAGGED)
 FULL = ["c2", "c3"]
