@@ -83,6 +83,9 @@ thread_local int t_slot = 0;
 
 int launch(int flags, int bt, const PhaseArgs& a, int grid, int lds, void* stream, const char* fn) {
   if (grid <= 0) return DV_OK;
+  if (flags & T_AXPY)
+    for (int s = 0; s < a.axpy.nseg; ++s)
+      if (a.axpy.seg[s].mfma_nt) flags |= T_MFMA;
   TimingState& T = timing();
   hipEvent_t ea = nullptr, eb = nullptr;
   const int slot = t_slot++;
@@ -113,20 +116,27 @@ struct Ws {
 
 int pick_bt(int batch) { return batch <= 1 ? 1 : (batch == 2 ? 2 : 4); }
 
-// Axpy segment geometry that does not depend on the device.
-struct AxGeo { int vec, nslices, nbt, chunks_max; };
+// Axpy segment geometry that does not depend on the device.  A batch of at least
+// kAxMfmaMinBatch tokens over bf16 rows whose row length is a multiple of 128 runs on
+// the matrix cores (128-column slices, 16 tokens per block tile); otherwise the wave
+// path (pick_bt tokens per block, each row read once per block tile).
+struct AxGeo { int vec, nslices, nbt, chunks_max, mfma_nt, bt; };
 AxGeo ax_geo(int batch, int ncols, long long row_stride, dv_dtype wdt, int cap_rows) {
   AxGeo g;
   const int full = (wdt == DV_FP8) ? 16 : ((wdt == DV_BF16) ? 8 : 4);
   g.vec = (ncols % full == 0 && row_stride % full == 0) ? full : 1;
-  g.nslices = cdiv(ncols, kAxSliceLanes * g.vec);
-  const int bt = pick_bt(batch);
-  g.nbt = cdiv(batch, bt);
+  g.mfma_nt = 0;
+  if (batch >= kAxMfmaMinBatch && wdt == DV_BF16 && ncols % kMfmaCols == 0 && row_stride % 8 == 0)
+    g.mfma_nt = 1;
+  g.nslices = g.mfma_nt ? ncols / kMfmaCols : cdiv(ncols, kAxSliceLanes * g.vec);
+  g.bt = g.mfma_nt ? kMfmaRows * g.mfma_nt : pick_bt(batch);
+  g.nbt = cdiv(batch, g.bt);
   g.chunks_max = std::max(1, std::min(kMaxChunks, cap_rows));
   return g;
 }
 size_t ax_partial_floats(int batch, int ncols, const AxGeo& g) {
-  return (size_t)g.nbt * g.chunks_max * pick_bt(batch) * ncols;
+  (void)batch;
+  return (size_t)g.nbt * g.chunks_max * g.bt * ncols;
 }
 size_t ax_tickets(const AxGeo& g) { return (size_t)g.nbt * g.nslices; }
 
@@ -283,8 +293,9 @@ void finish_rowdot(RowdotTask& T, const float* y, int batch, int d, uint32_t* ze
   T.blocks = std::min(want, device_cus() * per_cu);
   T.zero_ptr = zero; T.zero_words = nzero;
   // A batch of tokens over bf16 rows runs on the matrix cores, which read each row
-  // once for up to 32 tokens (the wave-per-row path streams it once per token).
-  bool mfma = batch >= kMfmaMinBatch && d % kMfmaCols == 0;
+  // once for up to 32 tokens, when the wave-per-row path would stream it more than
+  // once (it stages bt_lds tokens of y in LDS at a time).
+  bool mfma = batch >= kMfmaMinBatch && batch > T.bt_lds && d % kMfmaCols == 0;
   for (int s = 0; s < T.nseg; ++s) mfma = mfma && T.seg[s].wdt == W_BF16 && !T.seg_store[s];
   T.mfma_nt = 0;
   if (mfma) {
@@ -316,13 +327,14 @@ void add_axpy2(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype
   S.W = W; S.row_stride = stride; S.wdt = wcode(wdt);
   S.rows = L; S.coef = coef; S.coef_ld = coef_ld; S.act = act; S.ncols = ncols;
   S.W2 = W2; S.rows2 = L2; S.coef2 = coef2; S.coef2_ld = coef2_ld; S.act2 = act2;
-  S.vec = g.vec; S.nslices = g.nslices; S.nbt = g.nbt;
+  S.vec = g.vec; S.nslices = g.nslices; S.nbt = g.nbt; S.mfma_nt = g.mfma_nt;
   // About target_blocks blocks for the segment (512-byte row slices need many loads
   // in flight to stream well); at most kMaxChunks chunk partials per slice (a short,
-  // fixed-order final sum) and at least one row per row group.
+  // fixed-order final sum) and at least one row per row group (a matrix-core block
+  // takes 32 rows per wave at a time).
   const int per_chunk = g.nslices * g.nbt;
   int chunks = std::max(1, target_blocks / per_chunk);
-  chunks = std::min(chunks, std::max(1, cap_rows / kAxGroups));
+  chunks = std::min(chunks, std::max(1, cap_rows / (g.mfma_nt ? kWaves * 32 : kAxGroups)));
   S.nchunks = std::max(1, std::min(chunks, g.chunks_max));
   S.block0 = T.blocks;
   S.partial = partial; S.tickets = tickets; S.hist = nullptr;
@@ -351,8 +363,11 @@ int default_axpy_blocks() { return 6 * device_cus(); }
 // column sums (kAxSliceLanes * vec columns per slice; vec 16 for fp8 rows), or the
 // histogram of a row sum that builds one.
 int axpy_lds(int bt, int vec = 8) {
-  return std::max((kAxpyTileRows * (1 + bt) + kAxGroups * bt * kAxSliceLanes * vec) * 4,
-                  (16 + kHistBins) * 4);
+  // matrix-core blocks (launches with a batch): row ids, a padded coefficient tile
+  // and the wave sums for 16 tokens
+  const int mfma = bt > 1 ? (128 + 16 * (128 + 4) + 16 * (kMfmaCols + 1)) * 4 : 0;
+  return std::max(std::max((kAxpyTileRows * (1 + bt) + kAxGroups * bt * kAxSliceLanes * vec) * 4,
+                           (16 + kHistBins) * 4), mfma);
 }
 
 // n: cache rows attended; kv_cap: rows per (token, head) in K and V (>= n).
@@ -780,7 +795,9 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   // (fp8 rows halve the column slices, so each row-sum block would stream as many rows
   // as at bf16 and the launch becomes bound by each block's chain: measured 60 us for
   // the single launch against 22 + 25 us for the attention and a row-sum launch)
-  if (!nx && max_count_a > 0 && !fp8) {
+  // (Row sums on the matrix cores do not wait inside a launch: batches of tokens
+  // over bf16 rows take the two launches below.)
+  if (!nx && max_count_a > 0 && !fp8 && ax_geo(batch, d, d, wdt, 1).mfma_nt == 0) {
     PhaseArgs f = zero_args();
     setup_attn(f.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n_att, kv_cap, dh, LH,
                L->scale,

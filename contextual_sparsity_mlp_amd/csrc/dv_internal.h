@@ -41,8 +41,9 @@ constexpr int kWordsPerThread = 4;       // bitmask words per thread when compac
 constexpr int kMfmaRows = 16;            // matrix-core row dots: rows per tile and tokens per token tile
 constexpr int kMfmaRT = 2;               //   row tiles per block unit
 constexpr int kMfmaCols = 128;           //   columns per step (4 MFMA k-steps of 32); d % 128 == 0
-constexpr int kMfmaMinBatch = 2;         //   smallest batch that takes them
-constexpr int kMfmaBlocksPerCu = 4;      //   resident blocks per CU the grid is sized for
+constexpr int kMfmaMinBatch = 2;         //   smallest batch that takes them (row dots)
+constexpr int kAxMfmaMinBatch = 3;       //   row sums (measured: batch 4 row sum 187 -> 130 us)
+constexpr int kMfmaBlocksPerCu = 3;      //   resident blocks per CU the grid is sized for (137 VGPRs)
 
 enum : int { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };   // W_FP8: E4M3 codes, one scale per row
 enum : int { A_NONE = 0, A_RELU = 1, A_GELU = 2 };   // row-sum coefficient activations
@@ -103,6 +104,8 @@ struct AxpySeg {
   int act2;
   int ncols;               // output columns
   int vec;                 // elements per thread per row (8 bf16 / 4 f32 / 1 scalar)
+  int mfma_nt;             // 1: matrix-core blocks with 16 tokens per block tile (bf16 rows,
+                           //   128-column slices); 0: the wave path
   int nslices, nchunks, nbt;
   int block0;              // first block of this segment inside the task
   float* partial;          // [nbt][nchunks][BT][ncols]
@@ -196,8 +199,10 @@ struct ZeroTask {
 // the cache (RowdotTask::seg_store).
 // T_FP8: the row dots and row sums of the launch may hold fp8 rows; the launches
 // without it carry no fp8 code, which keeps their bf16 loops as tight as before.
+// T_MFMA: some row sum of the launch runs on the matrix cores (AxpySeg::mfma_nt); set by
+// the host launcher, so the wave-path launches keep their register budget.
 enum : int { T_ROWDOT = 1, T_ATTN = 2, T_AXPY = 4, T_HIST = 8, T_CLASSIFY = 16, T_WAIT = 32,
-             T_ZERO = 64, T_FP8 = 128, T_KV = 256 };
+             T_ZERO = 64, T_FP8 = 128, T_KV = 256, T_MFMA = 512 };
 
 struct PhaseArgs {
   RowdotTask rowdot;

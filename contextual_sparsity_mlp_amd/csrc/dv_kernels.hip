@@ -24,6 +24,10 @@
 //  top-k    hist / classify (with the row's resolve in its last block), see
 //           dv_internal.h.
 //
+// With a batch of tokens the row dots (from 2 tokens) and the row sums (from 3) run
+// on the matrix cores instead (v_mfma_f32_16x16x32_bf16 over 16-row x 16-token
+// tiles), so that each selected row is read once for the batch.
+//
 // Blocks of one launch hand values to each other only through device-coherent
 // (agent-scope) atomic stores and loads plus a wait for store completion before
 // the ticket: no cache writeback or invalidate is needed for that.  Values that
@@ -455,8 +459,8 @@ __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float*
 // With B tokens the row dots are the product (B x d) . (d x rows) of Eq. (1)'s
 // y W1_S (and W^Q, predictor factor A): every selected row must be read once for
 // the whole batch, not once per token.  A block owns a unit of kMfmaRT tiles of
-// 16 rows; its four waves split the row length d in four and each runs
-// v_mfma_f32_16x16x32_bf16 over 128-column steps: the A operand is 16 rows x 32
+// 16 rows; its four waves take the 128-column steps of the row length in turn and
+// run v_mfma_f32_16x16x32_bf16 over each: the A operand is 16 rows x 32
 // columns of W (lane l holds 8 columns of row l % 16, loaded straight from HBM),
 // the B operand 32 columns x 16 tokens of y.  y stays fp32 in memory; each lane
 // splits its 8 values into hi = bf16(y) and mid = bf16(y - hi) and both products
@@ -509,39 +513,45 @@ __device__ __forceinline__ void rowdot_mfma_task(const RowdotTask& T, float* lds
   const int units = (total_tiles + kMfmaRT - 1) / kMfmaRT;
   const int d = T.d;
   const int nss = d / kMfmaCols;                 // 128-column steps (d % 128 == 0)
-  const int ss0 = wave * nss / kWaves, ss1 = (wave + 1) * nss / kWaves;
   const int m = lane & 15, g = lane >> 4;        // operand row / token, 8-column group
   constexpr int NACC = kMfmaRT * NT * 4;         // accumulator values per lane
   float* red = lds;                              // [kWaves][NACC][64]
 
   for (int tb0 = 0; tb0 < T.batch; tb0 += kMfmaRows * NT) {
     for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
-      // this lane's row of each tile (nullptr: outside the list, loads zeros)
+      // This lane's row of each tile.  Lanes outside the list read a valid stand-in
+      // row (the segment's first) instead: their products only reach output rows that
+      // are not stored (or stored as 0 for an index outside [0, items)), and every
+      // load stays unconditional, so the wait for a step's y leaves the next step's
+      // rows in flight.  A unit with no listed row is skipped as a whole.
       const uint16_t* rp[kMfmaRT];
+      bool any = false;
 #pragma unroll
       for (int rt = 0; rt < kMfmaRT; ++rt) {
         int s, r0;
         mfma_tile(T, unit * kMfmaRT + rt, s, r0);
-        rp[rt] = nullptr;
+        const RowdotSeg S = rd_seg<kMaxSeg>(T, s < 0 ? 0 : s);
+        rp[rt] = static_cast<const uint16_t*>(S.W) + g * 8;
         if (s >= 0) {
-          const RowdotSeg S = rd_seg<kMaxSeg>(T, s);
-          const int r = r0 + m;
           const int ex = S.rows.expand;
+          const int nslots = list_slots(S.rows);
+          any = any || (r0 < S.cap && ((ex == 1) ? r0 : r0 / ex) < nslots);
+          const int r = r0 + m;
           const int slot = (ex == 1) ? r : r / ex;
           const int e = (ex == 1) ? 0 : r - slot * ex;
-          if (r < S.cap && slot < list_slots(S.rows)) {
+          if (r < S.cap && slot < nslots) {
             const int item = S.rows.idx ? S.rows.idx[slot] : slot;
             if ((unsigned)item < (unsigned)S.rows.items)
-              rp[rt] = static_cast<const uint16_t*>(S.W) + ((long long)item * ex + e) * S.row_stride +
-                       g * 8;
+              rp[rt] += ((long long)item * ex + e) * S.row_stride;
           }
         }
       }
+      if (!any) continue;   // block-uniform
       const float* yp[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int n = tb0 + nt * kMfmaRows + m;
-        yp[nt] = (n < T.batch) ? T.y + (size_t)n * d + g * 8 : nullptr;
+        const int n = min(tb0 + nt * kMfmaRows + m, T.batch - 1);   // stand-in: last token
+        yp[nt] = T.y + (size_t)n * d + g * 8;
       }
       f32x4 acc[kMfmaRT][NT];
 #pragma unroll
@@ -549,28 +559,40 @@ __device__ __forceinline__ void rowdot_mfma_task(const RowdotTask& T, float* lds
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      for (int ss = ss0; ss < ss1; ++ss) {
-        const int c0 = ss * kMfmaCols;
-        uint4 w[kMfmaRT][4];
+      // The waves take the steps in turn, so a block's four waves read 512 contiguous
+      // columns (1 KiB) of each of its rows at about the same time.  The rows of the
+      // wave's next step are requested before the current step is computed, after
+      // that step's y; the last step requests its own rows again (a cache hit).
+      const int last = wave + ((nss - 1 - wave) / kWaves) * kWaves;
+      uint4 w[kMfmaRT][4];
+      auto load_w = [&](int ss, uint4 (&dst)[kMfmaRT][4]) {
+        const int c0 = min(ss, last) * kMfmaCols;
 #pragma unroll
         for (int rt = 0; rt < kMfmaRT; ++rt)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            w[rt][j] = rp[rt] ? ld_stream(reinterpret_cast<const uint4*>(rp[rt] + c0 + 32 * j))
-                              : make_uint4(0u, 0u, 0u, 0u);
+            dst[rt][j] = ld_stream(reinterpret_cast<const uint4*>(rp[rt] + c0 + 32 * j));
+      };
+      if (wave < nss) load_w(wave, w);
+      for (int ss = wave; ss < nss; ss += kWaves) {
+        const int c0 = ss * kMfmaCols;
+        float4 yv[NT][8];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          float4 yv[8];
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float4* q = reinterpret_cast<const float4*>(yp[nt] + c0 + 32 * j);
-            yv[2 * j] = yp[nt] ? q[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-            yv[2 * j + 1] = yp[nt] ? q[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+            yv[nt][2 * j] = q[0];
+            yv[nt][2 * j + 1] = q[1];
           }
+        uint4 wn[kMfmaRT][4];
+        load_w(ss + kWaves, wn);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             bf16x8 hi, mid;
-            split8(yv[2 * j], yv[2 * j + 1], hi, mid);
+            split8(yv[nt][2 * j], yv[nt][2 * j + 1], hi, mid);
 #pragma unroll
             for (int rt = 0; rt < kMfmaRT; ++rt) {
               const bf16x8 a = __builtin_bit_cast(bf16x8, w[rt][j]);
@@ -579,6 +601,10 @@ __device__ __forceinline__ void rowdot_mfma_task(const RowdotTask& T, float* lds
             }
           }
         }
+#pragma unroll
+        for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[rt][j] = wn[rt][j];
       }
 
       // the four waves' partial tiles, summed in wave order
@@ -607,7 +633,10 @@ __device__ __forceinline__ void rowdot_mfma_task(const RowdotTask& T, float* lds
         const int r = r0 + 4 * (ln >> 4) + i;
         const int ex = S.rows.expand;
         const int slot = (ex == 1) ? r : r / ex;
-        if (r < S.cap && slot < list_slots(S.rows)) S.out[(size_t)n * S.out_ld + r] = v;
+        if (r < S.cap && slot < list_slots(S.rows)) {
+          const int item = S.rows.idx ? S.rows.idx[slot] : slot;
+          S.out[(size_t)n * S.out_ld + r] = ((unsigned)item < (unsigned)S.rows.items) ? v : 0.f;
+        }
       }
     }
   }
@@ -957,7 +986,205 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
   }
 }
 
-template <int BT, bool WAIT, bool FP8>
+// --------------------------------------------------------------------------- //
+// axpy on the matrix cores (a batch of tokens, bf16 rows)                      //
+// --------------------------------------------------------------------------- //
+//
+// out[b][col] = sum_s c[b][s] R[row(s)][col] contracts over the row index, while a
+// row is contiguous along col.  The MFMA operand wants the contracted index along
+// a lane's eight values, so each lane loads an 8 x 8 block (16 bytes from each of
+// 8 consecutive rows of the list, at the same 8 columns) and regroups it in
+// registers into eight column vectors of 8 rows.  Vector j of lane l is the A
+// operand row l % 16 of MFMA j: MFMA j (v_mfma_f32_16x16x32_bf16) covers the 16
+// columns col0 + 8 m + j (m < 16) against 32 rows and 16 tokens.  Eight MFMAs
+// cover a 128-column slice.  Coefficients (fp32) are split into bf16 hi + mid like
+// the row dots' y.  A block owns a (128-column slice x row chunk x token tile):
+// its four waves take 32-row groups in turn and are summed in LDS in wave order;
+// chunk partials go to the last block of the slice (tickets), which sums them in
+// chunk order and applies the epilogue: deterministic, like the wave path.
+constexpr int kAxmTile = 128;            // rows whose ids / coefficients sit in LDS
+constexpr int kAxmCoefLd = kAxmTile + 4; // padded row of the coefficient tile
+constexpr int kAxmRedLd = kMfmaCols + 1; // padded row of the wave sums
+
+// Low / high bf16 halves of two words packed into one word (row a low, row b high).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+template <int NT>
+__device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int batch, float* lds) {
+  constexpr int TB = kMfmaRows * NT;       // tokens per block tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int slice = lb % S.nslices;
+  const int rest = lb / S.nslices;
+  const int chunk = rest % S.nchunks;
+  const int bti = rest / S.nchunks;
+  const int b0 = bti * TB;
+  const int nb = min(TB, batch - b0);
+  const int col0 = slice * kMfmaCols;
+
+  int* lrow = reinterpret_cast<int*>(lds);               // [kAxmTile] row or -1
+  float* lcoef = lds + kAxmTile;                         // [TB][kAxmCoefLd]
+  float* red = lcoef + TB * kAxmCoefLd;                  // [TB][kAxmRedLd]
+
+  f32x4 acc[NT][8];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The rows of both sources form one list (first source first); chunk c takes a
+  // contiguous share; lrow marks second-source rows with bit 30.
+  const int nrows_a = list_slots(S.rows) * S.rows.expand;
+  const int nrows = nrows_a + (S.W2 ? list_slots(S.rows2) * S.rows2.expand : 0);
+  const int per = (nrows + S.nchunks - 1) / S.nchunks;
+  const int r0 = min(chunk * per, nrows);
+  const int r1 = min(r0 + per, nrows);
+
+  for (int t0 = r0; t0 < r1; t0 += kAxmTile) {
+    const int tn = min(kAxmTile, r1 - t0);
+    __syncthreads();
+    for (int i = tid; i < kAxmTile; i += kThreads) {
+      int rowv = -1;
+      bool ok = false, second = false;
+      int rr = 0;
+      if (i < tn) {
+        second = t0 + i >= nrows_a;
+        rr = second ? t0 + i - nrows_a : t0 + i;
+        const RowList& L = second ? S.rows2 : S.rows;
+        const int ex = L.expand;
+        const int slot = (ex == 1) ? rr : rr / ex;
+        const int e = (ex == 1) ? 0 : rr - slot * ex;
+        const int item = L.idx ? L.idx[slot] : slot;
+        ok = (unsigned)item < (unsigned)L.items;
+        if (ok) rowv = (item * ex + e) | (second ? (1 << 30) : 0);
+      }
+      lrow[i] = rowv;
+      const float* cf = second ? S.coef2 : S.coef;
+      const int cld = second ? S.coef2_ld : S.coef_ld;
+      const int rl = second ? S.act2 : S.act;
+#pragma unroll 4
+      for (int b = 0; b < TB; ++b) {
+        float c = 0.f;
+        if (ok && b < nb) c = activate(cf[(size_t)(b0 + b) * cld + rr], rl);
+        lcoef[b * kAxmCoefLd + i] = c;
+      }
+    }
+    __syncthreads();
+    for (int q = wave * 32; q < tn; q += kWaves * 32) {
+      // 16 bytes of each of the rows q + 8 g + i, i < 8, at columns col0 + 8 m
+      uint4 w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = lrow[q + 8 * g + i];
+        w[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (row >= 0) {
+          const void* W = (row & (1 << 30)) ? S.W2 : S.W;
+          w[i] = ld_stream(reinterpret_cast<const uint4*>(
+              static_cast<const uint16_t*>(W) + (long long)(row & ((1 << 30) - 1)) * S.row_stride +
+              col0 + 8 * m));
+        }
+      }
+      bf16x8 chi[NT], cmid[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float4* cp = reinterpret_cast<const float4*>(lcoef + (nt * kMfmaRows + m) * kAxmCoefLd +
+                                                           q + 8 * g);
+        split8(cp[0], cp[1], chi[nt], cmid[nt]);
+      }
+      // column vectors: element i of vector j = row 8 g + i, column col0 + 8 m + j
+      const uint32_t* wu = reinterpret_cast<const uint32_t*>(w);   // w[i] word x at wu[4 i + x]
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t a[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t lo = wu[4 * (2 * p) + (j >> 1)], hi = wu[4 * (2 * p + 1) + (j >> 1)];
+          a[p] = (j & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
+        }
+        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(a[0], a[1], a[2], a[3]));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, chi[nt], acc[nt][j], 0, 0, 0);
+          acc[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, cmid[nt], acc[nt][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Sum the waves in wave order.  Lane l of MFMA j holds, for token l % 16, the
+  // columns col0 + 8 (4 (l / 16) + i) + j, i < 4.
+  for (int wv = 0; wv < kWaves; ++wv) {
+    __syncthreads();
+    if (wave == wv) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float* rp = &red[(nt * kMfmaRows + m) * kAxmRedLd + 8 * (4 * g + i) + j];
+            *rp = (wv == 0) ? acc[nt][j][i] : *rp + acc[nt][j][i];
+          }
+    }
+  }
+  __syncthreads();
+
+  // each thread finalises column tid % 128 of tokens 2 it + tid / 128
+  constexpr int PER = TB * kMfmaCols / kThreads;
+  const int cc = tid & (kMfmaCols - 1), th = tid >> 7;
+  const size_t ncols = (size_t)S.ncols;
+  const int col = col0 + cc;
+  float part[PER];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) part[it] = red[(2 * it + th) * kAxmRedLd + cc];
+
+  if (S.nchunks > 1) {
+    float* P = S.partial + ((size_t)(bti * S.nchunks + chunk) * TB) * ncols;
+#pragma unroll
+    for (int it = 0; it < PER; ++it)
+      if (2 * it + th < nb) st_dev(&P[(2 * it + th) * ncols + col], part[it]);
+    int* flag = reinterpret_cast<int*>(lds);
+    if (!arrive_last(&S.tickets[bti * S.nslices + slice], (uint32_t)S.nchunks, flag)) return;
+    const float* P0 = S.partial + (size_t)bti * S.nchunks * TB * ncols;
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int b = 2 * it + th;
+      if (b < nb) {
+        float v[kMaxChunks];
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c)
+          v[c] = (c < S.nchunks) ? ld_dev(&P0[((size_t)c * TB + b) * ncols + col]) : 0.f;
+        float t = 0.f;
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) t += v[c];
+        part[it] = t;
+      }
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int b = 2 * it + th;
+    if (b < nb) {
+      const size_t bo = (size_t)(b0 + b);
+      float sum = part[it];
+      if (S.add1) sum = S.add1[bo * S.add_ld + col] + sum;
+      if (S.add0) sum = S.add0[bo * S.add_ld + col] + sum;
+      float* o = S.out + bo * S.out_ld + col;
+      if (S.accumulate) sum = *o + sum;
+      *o = sum;
+      part[it] = sum;
+    }
+  }
+  if (S.hist) {
+    uint32_t* lh = reinterpret_cast<uint32_t*>(lds) + 16;
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      if (b < nb) hist_flush_one(part[b >> 1], (b & 1) == th, lh, S.hist + (size_t)(b0 + b) * kHistBins);
+  }
+}
+
+template <int BT, bool WAIT, bool FP8, bool MFMA>
 __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds) {
   int s = 0;
 #pragma unroll
@@ -965,6 +1192,9 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
     if (i < T.nseg && blk >= T.seg[i].block0) s = i;
   const AxpySeg S = ax_seg(T, s);
   const int lb = blk - S.block0;
+  if constexpr (MFMA && BT > 1 && !WAIT && !FP8) {
+    if (S.mfma_nt) { axpy_mfma_block<1>(S, lb, T.batch, lds); return; }
+  }
   if (S.wdt == W_BF16) {
     if (S.vec == 8) axpy_block<BT, 8, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
     else axpy_block<BT, 1, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
@@ -1471,7 +1701,8 @@ __device__ __forceinline__ void phase_body(const PhaseArgs& a, float* lds) {
   }
   if constexpr ((FLAGS & T_AXPY) != 0) {
     if (blk >= a.b_axpy && blk < a.b_axpy + a.axpy.blocks) {
-      axpy_task<BT, (FLAGS & T_WAIT) != 0, (FLAGS & T_FP8) != 0>(a.axpy, blk - a.b_axpy, lds);
+      axpy_task<BT, (FLAGS & T_WAIT) != 0, (FLAGS & T_FP8) != 0, (FLAGS & T_MFMA) != 0>(
+          a.axpy, blk - a.b_axpy, lds);
       return;
     }
   }
@@ -1572,6 +1803,15 @@ int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes,
     case T_AXPY | T_FP8: return launch_bt<T_AXPY | T_FP8>(bt, a, grid, lds_bytes, stream);
     case T_AXPY | T_CLASSIFY | T_FP8:
       return launch_bt<T_AXPY | T_CLASSIFY | T_FP8>(bt, a, grid, lds_bytes, stream);
+    // matrix-core row sums: batches of at least kAxMfmaMinBatch tokens (bt 4)
+    case T_AXPY | T_MFMA:
+      return bt == 4 ? launch_t<T_AXPY | T_MFMA, 4>(a, grid, lds_bytes, stream) : (int)hipErrorInvalidValue;
+    case T_ATTN | T_AXPY | T_MFMA:
+      return bt == 4 ? launch_t<T_ATTN | T_AXPY | T_MFMA, 4>(a, grid, lds_bytes, stream)
+                     : (int)hipErrorInvalidValue;
+    case T_AXPY | T_CLASSIFY | T_MFMA:
+      return bt == 4 ? launch_t<T_AXPY | T_CLASSIFY | T_MFMA, 4>(a, grid, lds_bytes, stream)
+                     : (int)hipErrorInvalidValue;
     case T_ATTN: return launch_t<T_ATTN, 1>(a, grid, lds_bytes, stream);
     case T_ZERO: return launch_t<T_ZERO, 1>(a, grid, lds_bytes, stream);
     case T_HIST: return launch_t<T_HIST, 1>(a, grid, lds_bytes, stream);

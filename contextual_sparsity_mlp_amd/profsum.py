@@ -45,7 +45,9 @@ def stats(src: str, trace: str, out: str, command: str):
     # and without a next layer the attention runs alone before the row sum
     fp8 = any(re.search(r"(?:phase|rowdot|rowdot_kv)_kernel<129, ", r["Name"]) for r in rows)
     weights = "fp8 (E4M3) weight rows" if fp8 else "bf16 weights"
-    lines = [f"# rocprofv3 kernel summary: OPT-175B-shaped decode layer, batch 1, {weights}", "",
+    mb = re.search(r"--batch (\d+)", command)
+    batch = int(mb.group(1)) if mb else 1
+    lines = [f"# rocprofv3 kernel summary: OPT-175B-shaped decode layer, batch {batch}, {weights}", "",
              f"Command: `{command}`", "",
              "## Per kernel (rocprofv3 --stats)", "",
              "| kernel | calls | avg us | min us | max us | % time |",
@@ -60,18 +62,24 @@ def stats(src: str, trace: str, out: str, command: str):
     groups = {}
     seq = []
     for r in sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"])):
-        m = re.search(r"(?:phase|rowdot|rowdot_kv)_kernel<(\d+), (\d+)>", r["Kernel_Name"])
-        if not m:
+        m = re.search(r"(?:phase|rowdot|rowdot_kv)_kernel(?:_bt)?<(\d+), (\d+)>", r["Kernel_Name"])
+        mm = re.search(r"rowdot_mfma_kernel<(\d+)>", r["Kernel_Name"])
+        if not m and not mm:
             continue
         blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        groups.setdefault((m.group(1), m.group(2), blocks), []).append(dur)
-        seq.append((m.group(1), dur))
+        # matrix-core row dots are listed as flags "mfma", batch tile = token tiles of 16
+        fl, bt = (m.group(1), m.group(2)) if m else ("mfma", mm.group(1))
+        groups.setdefault((fl, bt, blocks), []).append(dur)
+        seq.append((fl, dur))
     # launches of the look-ahead step: a row-dot launch directly followed by the
-    # attention + row-sum launch and the row-sum + top-k launch
+    # attention + row-sum launch and the row-sum + top-k launch (with a batch of at
+    # least 3 tokens: matrix-core row dots and row sums, flag 512)
     slot_flags = dict(SLOT_FLAGS)
     if fp8:
         slot_flags = {0: "129", 1: "6", 2: "148"}
+    elif batch >= 3:
+        slot_flags = {0: "mfma", 1: "518", 2: "532"}
     order = [slot_flags[k] for k in sorted(slot_flags)]
     slot_durs = {k: [] for k in slot_flags}
     for i in range(len(seq) - len(order) + 1):
@@ -80,8 +88,9 @@ def stats(src: str, trace: str, out: str, command: str):
                 slot_durs[j].append(seq[i + j][1])
     lines += ["", "## Decode launches by configuration (from the kernel trace)", "",
               "flags: 1 row dots, 2 attention, 4 row sums, 8 histogram, 16 top-k classify, "
-              "32 row sums that wait for in-launch attention, 64 zero fill, 128 fp8 rows "
-              "(sums of these for a mixed launch)", "",
+              "32 row sums that wait for in-launch attention, 64 zero fill, 128 fp8 rows, "
+              "256 KV stores, 512 matrix-core row sums (sums of these for a mixed launch); "
+              "mfma: the matrix-core row dots", "",
               "| phase_kernel<flags, batch tile> | blocks | launches | avg us | median us | min us |",
               "|---|---|---|---|---|---|"]
     for (fl, bt, blocks), v in sorted(groups.items(), key=lambda kv: -len(kv[1])):
@@ -89,7 +98,8 @@ def stats(src: str, trace: str, out: str, command: str):
                      f"{statistics.median(v):.2f} | {min(v):.2f} |")
     # launches of the sparse MLP + MHA step: row dots, then the single launch of
     # attention and the waiting row sum
-    sp_order = ["129", "2", "132"] if fp8 else ["1", "38"]
+    sp_order = (["129", "2", "132"] if fp8 else ["mfma", "2", "516"] if batch >= 3
+                else ["1", "38"])
     sp_durs = {k: [] for k in range(len(sp_order))}
     for i in range(len(seq) - len(sp_order) + 1):
         if all(seq[i + j][0] == sp_order[j] for j in range(len(sp_order))):
@@ -103,18 +113,18 @@ def stats(src: str, trace: str, out: str, command: str):
                   "|---|---|---|---|---|---|"]
         for k in sorted(slot_durs):
             v = slot_durs[k]
-            lines.append(f"| {k}: {names[k]} | <{slot_flags[k]}, 1> | {len(v)} | "
+            lines.append(f"| {k}: {names[k]} | <{slot_flags[k]}> | {len(v)} | "
                          f"{statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} |")
     if sp_durs[0]:
         names = ({0: "row dots (W1, W^Q rows)", 1: "attention, split pieces combined per head",
-                  2: "row sum W2 + W^O rows"} if fp8 else
+                  2: "row sum W2 + W^O rows"} if len(sp_order) == 3 else
                  {0: "row dots (W1, W^Q rows)", 1: "attention + row sum W2 then W^O rows"})
         lines += ["", "## Sparse MLP + MHA step, per launch (from the kernel trace)", "",
                   "| launch | phase_kernel<flags> | launches | avg us | median us | min us |",
                   "|---|---|---|---|---|---|"]
         for k in sorted(sp_durs):
             v = sp_durs[k]
-            lines.append(f"| {k}: {names[k]} | <{sp_order[k]}, 1> | {len(v)} | "
+            lines.append(f"| {k}: {names[k]} | <{sp_order[k]}> | {len(v)} | "
                          f"{statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} |")
     open(out, "w").write("\n".join(lines) + "\n")
 
