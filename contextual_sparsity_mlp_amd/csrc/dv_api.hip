@@ -81,11 +81,13 @@ constexpr size_t kTimingPairs = 8192;
 // Per-call launch counter (the k-th launch of the current entry point).
 thread_local int t_slot = 0;
 
+int axpy_mfma_lds();
 int launch(int flags, int bt, const PhaseArgs& a, int grid, int lds, void* stream, const char* fn) {
   if (grid <= 0) return DV_OK;
   if (flags & T_AXPY)
     for (int s = 0; s < a.axpy.nseg; ++s)
       if (a.axpy.seg[s].mfma_nt) flags |= T_MFMA;
+  if (flags & T_MFMA) lds = std::max(lds, axpy_mfma_lds());
   TimingState& T = timing();
   hipEvent_t ea = nullptr, eb = nullptr;
   const int slot = t_slot++;
@@ -363,12 +365,13 @@ int default_axpy_blocks() { return 6 * device_cus(); }
 // column sums (kAxSliceLanes * vec columns per slice; vec 16 for fp8 rows), or the
 // histogram of a row sum that builds one.
 int axpy_lds(int bt, int vec = 8) {
-  // matrix-core blocks (launches with a batch): row ids, a padded coefficient tile
-  // and the wave sums for 16 tokens
-  const int mfma = bt > 1 ? (128 + 16 * (128 + 4) + 16 * (kMfmaCols + 1)) * 4 : 0;
-  return std::max(std::max((kAxpyTileRows * (1 + bt) + kAxGroups * bt * kAxSliceLanes * vec) * 4,
-                           (16 + kHistBins) * 4), mfma);
+  return std::max((kAxpyTileRows * (1 + bt) + kAxGroups * bt * kAxSliceLanes * vec) * 4,
+                  (16 + kHistBins) * 4);
 }
+// LDS of a matrix-core row-sum block: row ids and a padded coefficient tile of
+// kAxmTile rows for 16 tokens, and the wave sums (a launch with T_MFMA takes the larger
+// of this and its other tasks' needs).
+int axpy_mfma_lds() { return (kAxmTile + 16 * (kAxmTile + 4) + 16 * (kMfmaCols + 1)) * 4; }
 
 // n: cache rows attended; kv_cap: rows per (token, head) in K and V (>= n).
 void setup_attn(AttnTask& A, const float* q, int q_ld, const void* K, const void* V, dv_dtype kvdt,

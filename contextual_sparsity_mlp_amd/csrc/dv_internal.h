@@ -42,6 +42,7 @@ constexpr int kMfmaRows = 16;            // matrix-core row dots: rows per tile 
 constexpr int kMfmaRT = 2;               //   row tiles per block unit
 constexpr int kMfmaCols = 128;           //   columns per step (4 MFMA k-steps of 32); d % 128 == 0
 constexpr int kMfmaMinBatch = 2;         //   smallest batch that takes them (row dots)
+constexpr int kAxmTile = 256;           //   row sums: rows whose ids / coefficients sit in LDS (2 groups a wave)
 constexpr int kAxMfmaMinBatch = 3;       //   row sums (measured: batch 4 row sum 187 -> 130 us)
 constexpr int kMfmaBlocksPerCu = 3;      //   resident blocks per CU the grid is sized for (137 VGPRs)
 

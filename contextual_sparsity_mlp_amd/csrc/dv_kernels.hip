@@ -1002,7 +1002,6 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
 // its four waves take 32-row groups in turn and are summed in LDS in wave order;
 // chunk partials go to the last block of the slice (tickets), which sums them in
 // chunk order and applies the epilogue: deterministic, like the wave path.
-constexpr int kAxmTile = 128;            // rows whose ids / coefficients sit in LDS
 constexpr int kAxmCoefLd = kAxmTile + 4; // padded row of the coefficient tile
 constexpr int kAxmRedLd = kMfmaCols + 1; // padded row of the wave sums
 
@@ -1013,7 +1012,8 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a 
 template <int NT>
 __device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int batch, float* lds) {
   constexpr int TB = kMfmaRows * NT;       // tokens per block tile
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int m = lane & 15, g = lane >> 4;
   const int slice = lb % S.nslices;
   const int rest = lb / S.nslices;
@@ -1071,20 +1071,24 @@ __device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int ba
       }
     }
     __syncthreads();
-    for (int q = wave * 32; q < tn; q += kWaves * 32) {
-      // 16 bytes of each of the rows q + 8 g + i, i < 8, at columns col0 + 8 m
-      uint4 w[8];
+    // 16 bytes of each of the rows q + 8 g + i, i < 8, at columns col0 + 8 m.  Rows
+    // outside the list load a stand-in (row 0 of the first source) and are zeroed,
+    // so every load is unconditional and the next group's rows stay in flight while
+    // this group is computed.
+    auto load_rows = [&](int q, uint4 (&dst)[8], uint32_t& valid) {
+      valid = 0u;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = lrow[q + 8 * g + i];
-        w[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (row >= 0) {
-          const void* W = (row & (1 << 30)) ? S.W2 : S.W;
-          w[i] = ld_stream(reinterpret_cast<const uint4*>(
-              static_cast<const uint16_t*>(W) + (long long)(row & ((1 << 30) - 1)) * S.row_stride +
-              col0 + 8 * m));
-        }
+        const int rr = row < 0 ? 0 : row;
+        const void* W = (rr & (1 << 30)) ? S.W2 : S.W;
+        dst[i] = ld_stream(reinterpret_cast<const uint4*>(
+            static_cast<const uint16_t*>(W) + (long long)(rr & ((1 << 30) - 1)) * S.row_stride +
+            col0 + 8 * m));
+        valid |= (row >= 0 ? 1u : 0u) << i;
       }
+    };
+    auto group = [&](int q, const uint4 (&w)[8], uint32_t valid) {
       bf16x8 chi[NT], cmid[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -1093,7 +1097,13 @@ __device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int ba
         split8(cp[0], cp[1], chi[nt], cmid[nt]);
       }
       // column vectors: element i of vector j = row 8 g + i, column col0 + 8 m + j
-      const uint32_t* wu = reinterpret_cast<const uint32_t*>(w);   // w[i] word x at wu[4 i + x]
+      uint32_t wu[32];   // w[i] word x at wu[4 i + x], zero for rows outside the list
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = (valid >> i) & 1u;
+        wu[4 * i + 0] = ok ? w[i].x : 0u; wu[4 * i + 1] = ok ? w[i].y : 0u;
+        wu[4 * i + 2] = ok ? w[i].z : 0u; wu[4 * i + 3] = ok ? w[i].w : 0u;
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint32_t a[4];
@@ -1108,6 +1118,32 @@ __device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int ba
           acc[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, chi[nt], acc[nt][j], 0, 0, 0);
           acc[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, cmid[nt], acc[nt][j], 0, 0, 0);
         }
+      }
+    };
+    // this wave's 32-row groups of the tile, two register sets in turn (no copy waits
+    // for the next group's rows); past the last group the "next" rows repeat it
+    int q = wave * 32;
+    if (q < tn) {
+      uint4 wa[8], wb[8];
+      uint32_t va, vb;
+      load_rows(q, wa, va);
+      // (the scheduling barriers keep each group's loads ahead of the previous
+      // group's arithmetic, so the wait for one set does not cover the other)
+      for (;;) {
+        int qn = q + kWaves * 32;
+        __builtin_amdgcn_sched_barrier(0);
+        load_rows(qn < tn ? qn : q, wb, vb);
+        __builtin_amdgcn_sched_barrier(0);
+        group(q, wa, va);
+        if (qn >= tn) break;
+        q = qn;
+        qn = q + kWaves * 32;
+        __builtin_amdgcn_sched_barrier(0);
+        load_rows(qn < tn ? qn : q, wa, va);
+        __builtin_amdgcn_sched_barrier(0);
+        group(q, wb, vb);
+        if (qn >= tn) break;
+        q = qn;
       }
     }
   }
