@@ -212,7 +212,8 @@ def test_sparse_mlp_gelu(name):
     assert_close(got_a, ref_a, tol_of(cfg, TIGHT_MLP), f"gelu mlp accumulate {name}")
 
 
-@pytest.mark.parametrize("name", ["c1", "bf16-ragged", "f32-ragged"])
+# mixed-kv (batch 5, d 256) and b17 take the matrix-core row dots and row sums
+@pytest.mark.parametrize("name", ["c1", "bf16-ragged", "f32-ragged", "mixed-kv", "b17"])
 def test_sparse_mlp_edges(name):
     cfg = cfg_of(name)
     banner(f"sparse_mlp edges {name}")
@@ -238,12 +239,14 @@ def test_sparse_mlp_edges(name):
     assert_close(got, ref, tol, "mlp last neuron")
 
 
-def test_sparse_mlp_device_count_clamped_and_bad_indices():
-    cfg = RAGGED["bf16-ragged"]
-    banner("sparse_mlp clamp / bad indices")
+@pytest.mark.parametrize("name", ["bf16-ragged", "mixed-kv", "b17"])
+def test_sparse_mlp_device_count_clamped_and_bad_indices(name):
+    cfg = RAGGED[name]
+    banner(f"sparse_mlp clamp / bad indices {name}")
     L = synth.make_layer(cfg, DEV, with_kv=False)
     y = synth.make_y(cfg, DEV)
-    S = np.array([3, 10, 500, 999])
+    F = cfg.F
+    S = np.array([3, 10, F // 2, F - 1])
     # the device count says 9 but the capacity is 4: only the 4 slots are read
     idx = i32(S)
     cnt = i32([9])
@@ -253,7 +256,7 @@ def test_sparse_mlp_device_count_clamped_and_bad_indices():
     ref = O.sparse_mlp(host(y), host(L.W1t), host(L.W2t), S)
     assert_close(out.cpu().numpy(), ref, TIGHT_MLP, "clamped count")
     # out-of-range entries contribute nothing
-    idx = i32([3, -1, 10, cfg.F, 500, 1 << 30, 999])
+    idx = i32([3, -1, 10, F, F // 2, 1 << 30, F - 1])
     cnt = i32([7])
     ws = dv.workspace(dv.OP_SPARSE_MLP, batch=cfg.batch, d=cfg.d, max_count_m=7)
     dv.sparse_mlp(y, L.W1t, L.W2t, idx, cnt, 7, out, 0, ws)
@@ -292,7 +295,7 @@ def test_sparse_mha_parity(name):
     assert_close(got, ref, tol_of(cfg, TIGHT_ATTN), f"mha {name}")
 
 
-@pytest.mark.parametrize("name", ["c1", "bf16-ragged", "f32-ragged", "long-ctx"])
+@pytest.mark.parametrize("name", ["c1", "bf16-ragged", "f32-ragged", "long-ctx", "mixed-kv", "b17"])
 def test_sparse_mha_edges(name):
     cfg = cfg_of(name)
     banner(f"sparse_mha edges {name}")
