@@ -232,11 +232,16 @@ def main():
     torch.cuda.synchronize()
     ph_ms, ph_n = dv.timing_read(8)
     dv.timing_enable(False)
-    ph_bytes = acc.phase_bytes(**shape)
+    # three launches, or five when the attention runs alone before the predictor's
+    # matrix-core row sums and their score histograms (a batch of tokens)
+    n_la = sum(1 for n in ph_n if n > 0)
+    ph_bytes = acc.phase_bytes(**shape, lookahead_launches=n_la)
     phases = []
     kvn = "; W^K, W^V of every head" if args.kv_append else ""
-    names = [f"row dots (W1, W^Q, A rows{kvn})", "attention + predictor B rows",
-             "row sum W2 + W^O rows, combine, top-k"]
+    names = ([f"row dots (W1, W^Q, A rows{kvn})", "attention", "predictor B rows",
+              "score histograms", "row sum W2 + W^O rows, combine, top-k"] if n_la == 5 else
+             [f"row dots (W1, W^Q, A rows{kvn})", "attention + predictor B rows",
+              "row sum W2 + W^O rows, combine, top-k"])
     for i, (ms, n) in enumerate(zip(ph_ms, ph_n)):
         avg_us = ms * 1e3 / max(n, 1)
         b = ph_bytes[i] if i < len(ph_bytes) else 0

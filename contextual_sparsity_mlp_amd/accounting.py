@@ -71,7 +71,7 @@ def step_flops(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: in
 def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: int, u_m: int,
                 u_a: int, w_bytes: int = 2, kv_bytes: int = 2, with_predictor: bool = True,
                 p_bytes: int | None = None, row_scale_bytes: int = 0, sparse_launches: int = 2,
-                kv_append: bool = False):
+                kv_append: bool = False, lookahead_launches: int = 3):
     """Bytes each launch of the decode layer must move.
 
     With the predictor (the look-ahead step), three launches:
@@ -80,6 +80,9 @@ def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: i
         predictor B factors;
       3 one row sum over W2 and W^O rows, combined with y_in into y_out, beside the
         next layer's top-k: W2 rows, W^O rows, y_in read, y_out written, scores read.
+    or five (lookahead_launches=5: the predictor's row sums on the matrix cores, for a
+    batch): the attention alone, the predictor B factors, then the score histograms
+    (the scores read) before the row sum and top-k.
     Without it (the sparse MLP + MHA alone at small batch), two launches:
       1 gathered row dots: W1 rows, W^Q rows, y;
       2 attention, and the row sum over W2 then W^O rows: K/V, W2 rows, W^O rows,
@@ -104,4 +107,6 @@ def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: i
     p1 += 2 * r * d * pb
     p2 = kv + (r * F + r * h) * pb
     p3 = out + batch * (F + h) * 4
+    if lookahead_launches == 5:
+        return [p1, kv, (r * F + r * h) * pb, batch * (F + h) * 4, p3]
     return [p1, p2, p3]

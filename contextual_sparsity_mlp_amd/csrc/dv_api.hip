@@ -822,9 +822,20 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
 
   // Otherwise two launches: the attention (its last split of each head combines the
   // pieces into o) beside the next layer's predictor scores; then the row sum beside
-  // the next layer's top-k, whose last classify block of each row resolves it.
+  // the next layer's top-k, whose last classify block of each row resolves it.  When
+  // the predictor's row sums run on the matrix cores (a batch of tokens), the attention
+  // gets a launch of its own first: sharing a kernel with them would hold its
+  // latency-bound blocks to their register budget (measured at batch 16: 437 us for the
+  // shared launch against 283 us for the attention alone).
+  const bool attn_alone = nx && max_count_a > 0 && ax_geo(batch, Fn, Fn, pwdt, r).mfma_nt > 0;
+  if (attn_alone) {
+    PhaseArgs at = zero_args();
+    setup_attn(at.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n_att, kv_cap, dh, LH,
+               L->scale, fp(P.part), t_attn, fp(P.o), cap_a * dh, 0);
+    if (int e = launch(T_ATTN, 1, at, at.attn.blocks, attn_lds(), stream, fn)) return e;
+  }
   PhaseArgs a2 = zero_args();
-  if (max_count_a > 0)
+  if (max_count_a > 0 && !attn_alone)
     setup_attn(a2.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n_att, kv_cap, dh, LH,
                L->scale,
                fp(P.part), t_attn, fp(P.o), cap_a * dh, nx ? 1 : 0);
@@ -834,12 +845,15 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     // B_M's row sum fills the resident round beside the attention (measured 31.0 us for
     // the launch against 31.5 with six blocks per CU and 33.9 with four)
     const int bm_blocks = std::max(default_axpy_blocks(), resident_blocks() - a2.attn.blocks - 48);
+    // The blocks that finish the scores also build their top-digit histograms, except on
+    // the matrix-core path: there a block finishes 16 tokens' scores, one LDS histogram
+    // pass each, so the histograms get a launch of their own below.
     add_axpy(a2.axpy, batch, nx->B_M, Fn, pwdt, make_list(nullptr, nullptr, r, 1, r), fp(P.zm), r,
              0, Fn, fp(P.p_bm), t_bm, fp(P.sm), Fn, nullptr, nullptr, 0, 0, bm_blocks);
-    a2.axpy.seg[a2.axpy.nseg - 1].hist = up(P.hist_m);
+    a2.axpy.seg[a2.axpy.nseg - 1].hist = attn_alone ? nullptr : up(P.hist_m);
     add_axpy(a2.axpy, batch, nx->B_A, hn, pwdt, make_list(nullptr, nullptr, r, 1, r), fp(P.za), r,
              0, hn, fp(P.p_ba), t_ba, fp(P.sa), hn, nullptr, nullptr, 0, 0, default_axpy_blocks());
-    a2.axpy.seg[a2.axpy.nseg - 1].hist = up(P.hist_a);
+    a2.axpy.seg[a2.axpy.nseg - 1].hist = attn_alone ? nullptr : up(P.hist_a);
   }
   a2.axpy.batch = batch;
   const int flags2 = (a2.attn.blocks ? T_ATTN : 0) | (a2.axpy.nseg ? T_AXPY : 0);
@@ -864,6 +878,11 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     flags3 |= T_CLASSIFY;
     a3.b_topk = 0;
     a3.b_axpy = tk.blocks;
+  }
+  if (nx && attn_alone) {   // the score histograms, a launch of their own (see above)
+    PhaseArgs hs = zero_args();
+    hs.topk = a3.topk;
+    if (int e = launch(T_HIST, 1, hs, hs.topk.blocks, hist_lds(), stream, fn)) return e;
   }
   const int lds3 = std::max(axpy_lds(bt, fp8 ? 16 : 8), nx ? classify_lds() : 0);
   if (int e = launch(flags3, bt, a3, a3.topk.blocks + a3.axpy.blocks, lds3, stream, fn)) return e;

@@ -74,12 +74,14 @@ def stats(src: str, trace: str, out: str, command: str):
         seq.append((fl, dur))
     # launches of the look-ahead step: a row-dot launch directly followed by the
     # attention + row-sum launch and the row-sum + top-k launch (with a batch of at
-    # least 3 tokens: matrix-core row dots and row sums, flag 512)
+    # least 3 tokens: matrix-core row dots and row sums, flag 512, the attention in a
+    # launch of its own before the predictor's row sums, and the score histograms in
+    # one of their own after them)
     slot_flags = dict(SLOT_FLAGS)
     if fp8:
         slot_flags = {0: "129", 1: "6", 2: "148"}
     elif batch >= 3:
-        slot_flags = {0: "mfma", 1: "518", 2: "532"}
+        slot_flags = {0: "mfma", 1: "2", 2: "516", 3: "8", 4: "532"}
     order = [slot_flags[k] for k in sorted(slot_flags)]
     slot_durs = {k: [] for k in slot_flags}
     for i in range(len(seq) - len(order) + 1):
@@ -102,12 +104,19 @@ def stats(src: str, trace: str, out: str, command: str):
                 else ["1", "38"])
     sp_durs = {k: [] for k in range(len(sp_order))}
     for i in range(len(seq) - len(sp_order) + 1):
+        # (not the first launches of a look-ahead step, whose order starts alike)
+        nxt = seq[i + len(sp_order)][0] if i + len(sp_order) < len(seq) else None
+        if len(order) > len(sp_order) and nxt == order[len(sp_order)]:
+            continue
         if all(seq[i + j][0] == sp_order[j] for j in range(len(sp_order))):
             for j in range(len(sp_order)):
                 sp_durs[j].append(seq[i + j][1])
     if slot_durs[0]:
-        names = {0: "row dots (W1, W^Q, A rows)", 1: "attention + predictor B rows",
-                 2: "row sum W2 + W^O rows, combine, top-k"}
+        names = ({0: "row dots (W1, W^Q, A rows)", 1: "attention", 2: "predictor B rows",
+                  3: "score histograms", 4: "row sum W2 + W^O rows, combine, top-k"}
+                 if len(order) == 5 else
+                 {0: "row dots (W1, W^Q, A rows)", 1: "attention + predictor B rows",
+                  2: "row sum W2 + W^O rows, combine, top-k"})
         lines += ["", "## Look-ahead decode step, per launch (from the kernel trace)", "",
                   "| launch | phase_kernel<flags> | launches | avg us | median us | min us |",
                   "|---|---|---|---|---|---|"]
