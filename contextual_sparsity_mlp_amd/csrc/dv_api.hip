@@ -156,15 +156,41 @@ TopkWs plan_topk_parts(Ws& w, int batch, int N) {
   return t;
 }
 
-struct PredictWs { size_t z, tickets, partial, total; int nt; };
+// Matrix-core row dots with y in LDS (RowdotTask::mfma_nt 3) split each 128-row unit's
+// row length into parts when there are few units: each part stores a partial tile
+// (2048 floats) and the last part to finish (per-unit ticket) sums them in part order.
+// Parts are chosen so that units x parts stays near kRdItems, so the partials need at
+// most (kRdItems + units) tiles.  Sized from a bound on the rows.
+constexpr int kRdItems = 1024;
+constexpr int kRdUnitRows = kWaves * kMfmaRT * kMfmaRows;   // 128
+constexpr int kRdTile = kWaves * kMfmaRT * 4 * 64;          // partial tile floats
+struct RdWs { size_t partial = 0, tickets = 0; int ticket_words = 0; };
+bool rd_lds_path(int batch, int d) {
+  return batch >= kMfmaMinBatch && batch <= kMfmaRows && d % kMfmaCols == 0;
+}
+int rd_parts(int units, int d) {
+  const int max_parts = std::max(1, d / kMfmaCols / 4);      // at least 4 steps a part
+  return std::max(1, std::min(cdiv(kRdItems, std::max(units, 1)), max_parts));
+}
+RdWs plan_rd(Ws& w, int batch, int d, int rows_bound, bool bf16_rows) {
+  RdWs p;
+  if (!bf16_rows || !rd_lds_path(batch, d)) return p;
+  const int units = cdiv(std::max(rows_bound, 1) + kMaxSeg * kMfmaRows, kRdUnitRows);
+  p.partial = w.take((size_t)(kRdItems + units) * kRdTile * 4);
+  p.ticket_words = units;
+  p.tickets = w.take((size_t)p.ticket_words * 4);
+  return p;
+}
+
+struct PredictWs { size_t z, tickets, partial, total; int nt; RdWs rd; };
 PredictWs plan_predict(int batch, int d, int r, int N, dv_dtype wdt) {
-  (void)d;
   PredictWs p; Ws w;
   const AxGeo g = ax_geo(batch, N, N, wdt, r);
   p.nt = (int)ax_tickets(g);
   p.z = w.take((size_t)batch * r * 4);
   p.tickets = w.take((size_t)p.nt * 4);
   p.partial = w.take(ax_partial_floats(batch, N, g) * 4);
+  p.rd = plan_rd(w, batch, d, r, wdt == DV_BF16);
   p.total = w.off;
   return p;
 }
@@ -184,7 +210,7 @@ SelectWs plan_select(int batch, int N) {
   return p;
 }
 
-struct MlpWs { size_t a, tickets, partial, total; int nt; };
+struct MlpWs { size_t a, tickets, partial, total; int nt; RdWs rd; };
 MlpWs plan_mlp(int batch, int d, int cap, dv_dtype wdt) {
   MlpWs p; Ws w;
   const AxGeo g = ax_geo(batch, d, d, wdt, std::max(cap, 1));
@@ -192,11 +218,12 @@ MlpWs plan_mlp(int batch, int d, int cap, dv_dtype wdt) {
   p.a = w.take((size_t)batch * std::max(cap, 1) * 4);
   p.tickets = w.take((size_t)p.nt * 4);
   p.partial = w.take(ax_partial_floats(batch, d, g) * 4);
+  p.rd = plan_rd(w, batch, d, cap, wdt == DV_BF16);
   p.total = w.off;
   return p;
 }
 
-struct MhaWs { size_t q, o, part, tickets, partial, total; int nt_attn, nt_ax; };
+struct MhaWs { size_t q, o, part, tickets, partial, total; int nt_attn, nt_ax; RdWs rd; };
 MhaWs plan_mha(int batch, int d, int dh, int n_ctx, int cap, dv_dtype wdt) {
   MhaWs p; Ws w;
   cap = std::max(cap, 1);
@@ -208,6 +235,7 @@ MhaWs plan_mha(int batch, int d, int dh, int n_ctx, int cap, dv_dtype wdt) {
   p.part = w.take((size_t)batch * cap * attn_nsplit_max(n_ctx) * (dh + 2) * 4);
   p.tickets = w.take((size_t)(p.nt_attn + p.nt_ax) * 4);
   p.partial = w.take(ax_partial_floats(batch, d, g) * 4);
+  p.rd = plan_rd(w, batch, d, cap * dh, wdt == DV_BF16);
   p.total = w.off;
   return p;
 }
@@ -219,6 +247,7 @@ struct LayerWs {
   size_t p_bm, p_ba, p_wo, total;
   int t_attn, t_bm, t_ba, t_wo, t_total, zero_words;
   TopkWs tm, ta;
+  RdWs rd;
 };
 LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int cap_m, int cap_a,
                    dv_dtype wdt, dv_dtype pwdt) {
@@ -258,6 +287,8 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   p.p_wo = w.take(ax_partial_floats(batch, d, g_wo) * 4);
   p.tm = plan_topk_parts(w, batch, F);
   p.ta = plan_topk_parts(w, batch, h);
+  // row dots: W1 rows of S_M, W^Q rows of S_A and the two predictor factors
+  p.rd = plan_rd(w, batch, d, cap_m + cap_a * dh + 2 * r, wdt == DV_BF16 && pwdt == DV_BF16);
   p.total = w.off;
   return p;
 }
@@ -284,7 +315,8 @@ void add_rowdot(RowdotTask& T, const void* W, long long stride, dv_dtype wdt, Ro
 }
 
 // Rowdot blocks: enough waves for every row, at most a few resident blocks per CU.
-void finish_rowdot(RowdotTask& T, const float* y, int batch, int d, uint32_t* zero, int nzero) {
+void finish_rowdot(RowdotTask& T, const float* y, int batch, int d, uint32_t* zero, int nzero,
+                   char* ws, const RdWs& rd) {
   T.y = y; T.batch = batch; T.d = d;
   T.bt_lds = std::max(1, std::min(pick_bt(batch), kLdsBudget / (d * 4)));
   int cap = 0;
@@ -305,9 +337,25 @@ void finish_rowdot(RowdotTask& T, const float* y, int batch, int d, uint32_t* ze
     int tiles = 0;
     for (int s = 0; s < T.nseg; ++s) tiles += cdiv(T.seg[s].cap, kMfmaRows);
     T.blocks = std::max(1, std::min(cdiv(tiles, kMfmaRT), device_cus() * kMfmaBlocksPerCu));
+    T.mfma_parts = 1;
+    if (rd.ticket_words > 0 && rd_lds_path(batch, d)) {
+      // y staged in LDS: 128-row units, row lengths split into parts when units are few
+      const int units = cdiv(tiles, kWaves * kMfmaRT);
+      assert(units <= rd.ticket_words);
+      T.mfma_nt = 3;
+      T.mfma_parts = rd_parts(units, d);
+      T.mfma_partial = reinterpret_cast<float*>(ws + rd.partial);
+      T.mfma_tickets = reinterpret_cast<uint32_t*>(ws + rd.tickets);
+      T.mfma_ticket_words = units;
+      T.blocks = std::max(1, std::min(units * T.mfma_parts, device_cus() * kMfmaLdsBlocksPerCu));
+    }
   }
 }
+// The row-dot launch; row dots split into parts first clear their unit tickets (a
+// small launch outside the per-launch timing slots).
+int launch_rowdot(int flags, int bt, const PhaseArgs& a1, void* stream, const char* fn);
 int rowdot_lds(const RowdotTask& T) {
+  if (T.mfma_nt == 3) return 2 * 4 * 2 * 64 * 16 + 16;   // two steps of y fragments + flag
   if (T.mfma_nt > 0) return kWaves * kMfmaRT * T.mfma_nt * 4 * 64 * 4;
   return T.bt_lds * T.d * 4;
 }
@@ -421,6 +469,20 @@ PhaseArgs zero_args() {
   PhaseArgs a;
   memset(&a, 0, sizeof a);
   return a;
+}
+
+int launch_rowdot(int flags, int bt, const PhaseArgs& a1, void* stream, const char* fn) {
+  const RowdotTask& T = a1.rowdot;
+  if (T.mfma_nt == 3 && T.mfma_parts > 1) {
+    PhaseArgs z = zero_args();
+    z.zero.ptr = T.mfma_tickets;
+    z.zero.words = T.mfma_ticket_words;
+    z.zero.blocks = std::max(1, std::min(cdiv(T.mfma_ticket_words, kThreads * 4), 64));
+    const int err = launch_phase(T_ZERO, 1, z, z.zero.blocks, 0, stream);
+    if (err != 0)
+      return fail(DV_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString((hipError_t)err));
+  }
+  return launch(flags, bt, a1, T.blocks, rowdot_lds(T), stream, fn);
 }
 
 // ------------------------------------------------------------------------- //
@@ -539,8 +601,8 @@ int dv_predict(const float* y, int batch, int d, const void* A, const void* Bm, 
 
   PhaseArgs a1 = zero_args();
   add_rowdot(a1.rowdot, A, d, wdt, make_list(nullptr, nullptr, r, 1, r), z, r);
-  finish_rowdot(a1.rowdot, y, batch, d, tickets, P.nt);
-  if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
+  finish_rowdot(a1.rowdot, y, batch, d, tickets, P.nt, w, P.rd);
+  if (int e = launch_rowdot(T_ROWDOT, bt, a1, stream, fn)) return e;
 
   PhaseArgs a2 = zero_args();
   add_axpy(a2.axpy, batch, Bm, N, wdt, make_list(nullptr, nullptr, r, 1, r), z, r, 0, N,
@@ -609,8 +671,8 @@ int dv_sparse_mlp(const float* y, int batch, int d, const void* W1t, const void*
 
   PhaseArgs a1 = zero_args();
   add_rowdot(a1.rowdot, W1t, d, wdt, L, hbuf, cap);
-  finish_rowdot(a1.rowdot, y, batch, d, tickets, P.nt);
-  if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
+  finish_rowdot(a1.rowdot, y, batch, d, tickets, P.nt, w, P.rd);
+  if (int e = launch_rowdot(T_ROWDOT, bt, a1, stream, fn)) return e;
 
   PhaseArgs a2 = zero_args();
   add_axpy(a2.axpy, batch, W2t, d, wdt, L, hbuf, cap, act_code(act), d, reinterpret_cast<float*>(w + P.partial),
@@ -654,8 +716,8 @@ int dv_sparse_mha(const float* y, int batch, int d, int h, int dh, const void* W
 
   PhaseArgs a1 = zero_args();
   add_rowdot(a1.rowdot, Wq, d, wdt, L, q, cap * dh);
-  finish_rowdot(a1.rowdot, y, batch, d, t_attn, P.nt_attn + P.nt_ax);
-  if (int e = launch(T_ROWDOT, bt, a1, a1.rowdot.blocks, rowdot_lds(a1.rowdot), stream, fn)) return e;
+  finish_rowdot(a1.rowdot, y, batch, d, t_attn, P.nt_attn + P.nt_ax, w, P.rd);
+  if (int e = launch_rowdot(T_ROWDOT, bt, a1, stream, fn)) return e;
 
   PhaseArgs a2 = zero_args();
   setup_attn(a2.attn, q, cap * dh, K, V, kvdt, batch, h, n_ctx, n_ctx, dh,
@@ -774,9 +836,8 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
     a1.rowdot.store_ld_item = (long long)kv_cap * dh;
     a1.rowdot.store_dt = L->kvdt == DV_BF16 ? W_BF16 : W_F32;
   }
-  finish_rowdot(a1.rowdot, y_in, batch, d, up(P.zero), P.zero_words);
-  if (int e = launch(T_ROWDOT | (fp8 ? T_FP8 : 0) | (append ? T_KV : 0), bt, a1, a1.rowdot.blocks,
-                     rowdot_lds(a1.rowdot), stream, fn))
+  finish_rowdot(a1.rowdot, y_in, batch, d, up(P.zero), P.zero_words, w, P.rd);
+  if (int e = launch_rowdot(T_ROWDOT | (fp8 ? T_FP8 : 0) | (append ? T_KV : 0), bt, a1, stream, fn))
     return e;
 
   // After the row dots, the rest of the layer: attention over the cache for S_A; one

@@ -642,6 +642,202 @@ __device__ __forceinline__ void rowdot_mfma_task(const RowdotTask& T, float* lds
   }
 }
 
+// Matrix-core row dots with y in LDS (batch <= 16).  Loading each step's 16 tokens of
+// y from L2 in every wave, as above, costs as much load throughput as the rows
+// themselves (measured: 5.2 TB/s for the row stream alone, 3.2 TB/s with the y
+// loads).  Here a block owns 128 rows (4 waves x 2 tiles of 16) and a part of the
+// row length; its waves walk the part one 128-column step at a time together, and
+// each step's y (16 tokens, split into bf16 hi / mid in MFMA B-fragment order, 8 KB)
+// is staged in LDS once for the 128 rows, double-buffered.  Each wave requests the
+// next step's rows and y before computing the current step (two register sets in
+// turn, the last step peeled), so the rows stay in flight across the barrier.  With
+// several parts per unit, each part stores its partial tile and the last part to
+// finish (ticket) sums them in part order.
+constexpr int kRdwRows = kWaves * kMfmaRT * kMfmaRows;   // 128 rows per unit
+constexpr int kRdwFrag = 4 * 2 * 64;                     // 16-byte B fragments per step
+constexpr int kRdwTile = kWaves * kMfmaRT * 4 * 64;      // partial tile floats per part
+
+__device__ __forceinline__ void rdw_task(const RowdotTask& T, float* lds) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  for (int i = blockIdx.x * kThreads + tid; i < T.zero_words; i += gridDim.x * kThreads)
+    T.zero_ptr[i] = 0u;
+
+  int total_tiles = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSeg; ++i)
+    total_tiles += (i < T.nseg) ? (T.seg[i].cap + kMfmaRows - 1) / kMfmaRows : 0;
+  const int units = (total_tiles + kWaves * kMfmaRT - 1) / (kWaves * kMfmaRT);
+  const int d = T.d;
+  const int nss = d / kMfmaCols;
+  const int P = T.mfma_parts;
+  const int items = units * P;
+  uint4* ybuf = reinterpret_cast<uint4*>(lds);            // [2][kRdwFrag]
+  int* flag = reinterpret_cast<int*>(ybuf + 2 * kRdwFrag);
+  // the y fragment slot of this thread: j = tid / 64 (< 4), fragment lane tid % 64
+  const int yj = tid >> 6, yfl = tid & 63;
+
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int part = item % P;
+    const int unit = item / P;
+    const int s0 = part * nss / P, s1 = (part + 1) * nss / P;   // steps of this part
+
+    const uint16_t* rp[kMfmaRT];
+    bool any = false;
+#pragma unroll
+    for (int rt = 0; rt < kMfmaRT; ++rt) {
+      int s, r0;
+      mfma_tile(T, (unit * kWaves + wave) * kMfmaRT + rt, s, r0);
+      const RowdotSeg S = rd_seg<kMaxSeg>(T, s < 0 ? 0 : s);
+      rp[rt] = static_cast<const uint16_t*>(S.W) + g * 8;
+      if (s >= 0) {
+        const int ex = S.rows.expand;
+        const int nslots = list_slots(S.rows);
+        any = any || (r0 < S.cap && ((ex == 1) ? r0 : r0 / ex) < nslots);
+        const int r = r0 + m;
+        const int slot = (ex == 1) ? r : r / ex;
+        const int e = (ex == 1) ? 0 : r - slot * ex;
+        if (r < S.cap && slot < nslots) {
+          const int it = S.rows.idx ? S.rows.idx[slot] : slot;
+          if ((unsigned)it < (unsigned)S.rows.items) rp[rt] += ((long long)it * ex + e) * S.row_stride;
+        }
+      }
+    }
+    // A unit with no listed row is skipped by all its parts alike (its ticket is then
+    // never needed); waves whose own tiles hold none still stage y and pass the
+    // barriers (their stand-in rows reach no stored output).
+    if (!__syncthreads_or(any ? 1 : 0)) continue;   // block-uniform
+
+    auto load_w = [&](int ss, uint4 (&w)[kMfmaRT][4]) {
+#pragma unroll
+      for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[rt][j] = ld_stream(reinterpret_cast<const uint4*>(rp[rt] + ss * kMfmaCols + 32 * j));
+    };
+    // slot (j, fragment lane fl): token min(fl % 16, batch - 1), columns
+    // step * 128 + 32 j + 8 (fl / 16) .. + 8 (the columns of absent tokens are never
+    // stored)
+    auto load_y = [&](int ss, float4 (&yv)[2]) {
+      const int n = min(yfl & 15, T.batch - 1);
+      const float4* q = reinterpret_cast<const float4*>(
+          T.y + (size_t)n * d + ss * kMfmaCols + 32 * yj + (yfl >> 4) * 8);
+      yv[0] = q[0];
+      yv[1] = q[1];
+    };
+    auto stage_y = [&](const float4 (&yv)[2], int buf) {
+      bf16x8 hi, mid;
+      split8(yv[0], yv[1], hi, mid);
+      ybuf[buf * kRdwFrag + (yj * 2 + 0) * 64 + yfl] = __builtin_bit_cast(uint4, hi);
+      ybuf[buf * kRdwFrag + (yj * 2 + 1) * 64 + yfl] = __builtin_bit_cast(uint4, mid);
+    };
+    f32x4 acc[kMfmaRT] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    auto compute = [&](const uint4 (&w)[kMfmaRT][4], int buf) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 hi = __builtin_bit_cast(bf16x8, ybuf[buf * kRdwFrag + (j * 2 + 0) * 64 + lane]);
+        const bf16x8 mid = __builtin_bit_cast(bf16x8, ybuf[buf * kRdwFrag + (j * 2 + 1) * 64 + lane]);
+#pragma unroll
+        for (int rt = 0; rt < kMfmaRT; ++rt) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, w[rt][j]);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc[rt], 0, 0, 0);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, mid, acc[rt], 0, 0, 0);
+        }
+      }
+    };
+    // one step with the next one's y and rows requested first (issue order y, rows:
+    // the load counter is in order, so waiting for y does not wait for the rows)
+    auto step = [&](int ss, const uint4 (&cur)[kMfmaRT][4], uint4 (&nxt)[kMfmaRT][4]) {
+      float4 yv[2];
+      load_y(ss + 1, yv);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(ss + 1, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(cur, (ss - s0) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_y(yv, (ss + 1 - s0) & 1);
+      __syncthreads();
+    };
+
+    uint4 wa[kMfmaRT][4], wb[kMfmaRT][4];
+    {
+      float4 yv[2];
+      load_y(s0, yv);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(s0, wa);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();                          // the previous item's last reads of ybuf
+      stage_y(yv, 0);
+      __syncthreads();
+    }
+    int ss = s0;
+    for (; ss + 2 < s1; ss += 2) {
+      step(ss, wa, wb);
+      step(ss + 1, wb, wa);
+    }
+    if (ss + 1 < s1) {                          // two steps left: the last one peeled
+      step(ss, wa, wb);
+      compute(wb, (ss + 1 - s0) & 1);
+    } else {                                    // one step left
+      compute(wa, (ss - s0) & 1);
+    }
+
+    // the wave's outputs: lane ln of tile rt holds rows 4 (ln / 16) + i, token ln % 16
+    float v[kMfmaRT][4];
+#pragma unroll
+    for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[rt][i] = acc[rt][i];
+    if (P > 1) {
+      float* base = T.mfma_partial + (size_t)unit * P * kRdwTile;
+      const int off = (wave * kMfmaRT * 4) * 64 + lane;
+#pragma unroll
+      for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          st_dev(&base[(size_t)part * kRdwTile + off + (rt * 4 + i) * 64], v[rt][i]);
+      if (!arrive_last(&T.mfma_tickets[unit], (uint32_t)P, flag)) continue;   // block-uniform
+#pragma unroll
+      for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[rt][i] = 0.f;
+      for (int p = 0; p < P; ++p) {             // part order; 8 loads in flight per part
+        float t[kMfmaRT][4];
+#pragma unroll
+        for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t[rt][i] = ld_dev(&base[(size_t)p * kRdwTile + off + (rt * 4 + i) * 64]);
+#pragma unroll
+        for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[rt][i] += t[rt][i];
+      }
+    }
+    if (!any) continue;
+    const int n = m;
+    if (n >= T.batch) continue;
+#pragma unroll
+    for (int rt = 0; rt < kMfmaRT; ++rt) {
+      int s, r0;
+      mfma_tile(T, (unit * kWaves + wave) * kMfmaRT + rt, s, r0);
+      if (s < 0) continue;
+      const RowdotSeg S = rd_seg<kMaxSeg>(T, s);
+      const int ex = S.rows.expand;
+      const int nslots = list_slots(S.rows);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * g + i;
+        const int slot = (ex == 1) ? r : r / ex;
+        if (r < S.cap && slot < nslots) {
+          const int it = S.rows.idx ? S.rows.idx[slot] : slot;
+          S.out[(size_t)n * S.out_ld + r] = ((unsigned)it < (unsigned)S.rows.items) ? v[rt][i] : 0.f;
+        }
+      }
+    }
+  }
+}
+
 // --------------------------------------------------------------------------- //
 // axpy                                                                         //
 // --------------------------------------------------------------------------- //
@@ -1789,6 +1985,12 @@ __global__ __launch_bounds__(kThreads) void rowdot_mfma_kernel(PhaseArgs a) {
   rowdot_mfma_task<NT>(a.rowdot, lds);
 }
 
+// Matrix-core row dots with y staged in LDS (batch <= 16).
+__global__ __launch_bounds__(kThreads) void rowdot_mfma_lds_kernel(PhaseArgs a) {
+  extern __shared__ float lds[];
+  rdw_task(a.rowdot, lds);
+}
+
 template <int FLAGS, int BT>
 static int launch_t(const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
   if constexpr ((FLAGS & ~T_FP8) == (T_ROWDOT | T_KV) && BT == 1)
@@ -1818,6 +2020,11 @@ static int launch_bt(int bt, const PhaseArgs& a, int grid, int lds_bytes, void* 
 int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
   switch (flags) {
     case T_ROWDOT:
+      if (a.rowdot.mfma_nt == 3) {
+        hipLaunchKernelGGL(rowdot_mfma_lds_kernel, dim3(grid), dim3(kThreads), lds_bytes,
+                           static_cast<hipStream_t>(stream), a);
+        return (int)hipGetLastError();
+      }
       if (a.rowdot.mfma_nt > 0) {
         if (a.rowdot.mfma_nt == 1)
           hipLaunchKernelGGL((rowdot_mfma_kernel<1>), dim3(grid), dim3(kThreads), lds_bytes,
