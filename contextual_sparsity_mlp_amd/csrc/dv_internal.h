@@ -45,7 +45,7 @@ constexpr int kMfmaMinBatch = 2;         //   smallest batch that takes them (ro
 constexpr int kAxmTile = 256;           //   row sums: rows whose ids / coefficients sit in LDS (2 groups a wave)
 constexpr int kAxMfmaMinBatch = 3;       //   row sums (measured: batch 4 row sum 187 -> 130 us)
 constexpr int kMfmaBlocksPerCu = 3;      //   resident blocks per CU the grid is sized for (137 VGPRs)
-constexpr int kMfmaLdsBlocksPerCu = 4;   //   the same for the row dots with y in LDS
+constexpr int kMfmaLdsBlocksPerCu = 3;   //   the same for the row dots with y in LDS (133 registers)
 
 enum : int { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };   // W_FP8: E4M3 codes, one scale per row
 enum : int { A_NONE = 0, A_RELU = 1, A_GELU = 2 };   // row-sum coefficient activations

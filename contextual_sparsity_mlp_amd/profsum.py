@@ -63,13 +63,13 @@ def stats(src: str, trace: str, out: str, command: str):
     seq = []
     for r in sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"])):
         m = re.search(r"(?:phase|rowdot|rowdot_kv)_kernel(?:_bt)?<(\d+), (\d+)>", r["Kernel_Name"])
-        mm = re.search(r"rowdot_mfma_kernel<(\d+)>", r["Kernel_Name"])
+        mm = re.search(r"rowdot_mfma(_lds)?_kernel(?:<(\d+)>)?", r["Kernel_Name"])
         if not m and not mm:
             continue
         blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         # matrix-core row dots are listed as flags "mfma", batch tile = token tiles of 16
-        fl, bt = (m.group(1), m.group(2)) if m else ("mfma", mm.group(1))
+        fl, bt = (m.group(1), m.group(2)) if m else ("mfma", "lds" if mm.group(1) else mm.group(2))
         groups.setdefault((fl, bt, blocks), []).append(dur)
         seq.append((fl, dur))
     # launches of the look-ahead step: a row-dot launch directly followed by the
@@ -92,7 +92,7 @@ def stats(src: str, trace: str, out: str, command: str):
               "flags: 1 row dots, 2 attention, 4 row sums, 8 histogram, 16 top-k classify, "
               "32 row sums that wait for in-launch attention, 64 zero fill, 128 fp8 rows, "
               "256 KV stores, 512 matrix-core row sums (sums of these for a mixed launch); "
-              "mfma: the matrix-core row dots", "",
+              "mfma: the matrix-core row dots (batch tile lds: y staged in LDS)", "",
               "| phase_kernel<flags, batch tile> | blocks | launches | avg us | median us | min us |",
               "|---|---|---|---|---|---|"]
     for (fl, bt, blocks), v in sorted(groups.items(), key=lambda kv: -len(kv[1])):
