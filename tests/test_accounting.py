@@ -44,6 +44,13 @@ def test_c4_batch1_bytes():
     assert ba.total - b0.total == 2 * c.d * c.d * 2 + 2 * 2 * c.d * 2 + 2 * c.k_a * 2 * c.dh * 2
     pa = A.phase_bytes(**kw, kv_append=True)
     assert sum(pa) - sum(A.phase_bytes(**kw)) == ba.total - b0.total
+    # five look-ahead launches (a batch on the matrix cores): the attention and the
+    # predictor B factors apart, and the score histograms reading the scores once more
+    kw16 = dict(kw, batch=16)
+    p3, p5 = A.phase_bytes(**kw16), A.phase_bytes(**kw16, lookahead_launches=5)
+    assert len(p5) == 5 and p5[0] == p3[0] and p5[4] == p3[2]
+    assert p5[1] + p5[2] == p3[1]
+    assert sum(p5) == sum(p3) + 16 * (c.F + c.h) * 4
 
 
 def test_flops_intensity_batch1():
