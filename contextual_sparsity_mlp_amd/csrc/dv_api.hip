@@ -163,10 +163,10 @@ TopkWs plan_topk_parts(Ws& w, int batch, int N) {
 // most (kRdItems + units) tiles.  Sized from a bound on the rows.
 constexpr int kRdItems = 1024;
 constexpr int kRdUnitRows = kWaves * kMfmaRT * kMfmaRows;   // 128
-constexpr int kRdTile = kWaves * kMfmaRT * 4 * 64;          // partial tile floats
+constexpr int kRdTile = kWaves * kMfmaRT * 4 * 64 * 2;      // partial tile floats (32 tokens)
 struct RdWs { size_t partial = 0, tickets = 0; int ticket_words = 0; };
 bool rd_lds_path(int batch, int d) {
-  return batch >= kMfmaMinBatch && batch <= kMfmaRows && d % kMfmaCols == 0;
+  return batch >= kMfmaMinBatch && batch <= 2 * kMfmaRows && d % kMfmaCols == 0;
 }
 int rd_parts(int units, int d) {
   const int max_parts = std::max(1, d / kMfmaCols / 4);      // at least 4 steps a part
@@ -342,12 +342,14 @@ void finish_rowdot(RowdotTask& T, const float* y, int batch, int d, uint32_t* ze
       // y staged in LDS: 128-row units, row lengths split into parts when units are few
       const int units = cdiv(tiles, kWaves * kMfmaRT);
       assert(units <= rd.ticket_words);
-      T.mfma_nt = 3;
+      T.mfma_nt = batch <= kMfmaRows ? 3 : 4;     // 16 or 32 tokens a block
       T.mfma_parts = rd_parts(units, d);
       T.mfma_partial = reinterpret_cast<float*>(ws + rd.partial);
       T.mfma_tickets = reinterpret_cast<uint32_t*>(ws + rd.tickets);
       T.mfma_ticket_words = units;
-      T.blocks = std::max(1, std::min(units * T.mfma_parts, device_cus() * kMfmaLdsBlocksPerCu));
+      // resident blocks per CU: 4 with 16 tokens (109 registers), 3 with 32 (136)
+      const int per_cu_lds = T.mfma_nt == 3 ? kMfmaLdsBlocksPerCu + 1 : kMfmaLdsBlocksPerCu;
+      T.blocks = std::max(1, std::min(units * T.mfma_parts, device_cus() * per_cu_lds));
     }
   }
 }
@@ -355,7 +357,8 @@ void finish_rowdot(RowdotTask& T, const float* y, int batch, int d, uint32_t* ze
 // small launch outside the per-launch timing slots).
 int launch_rowdot(int flags, int bt, const PhaseArgs& a1, void* stream, const char* fn);
 int rowdot_lds(const RowdotTask& T) {
-  if (T.mfma_nt == 3) return 2 * 4 * 2 * 64 * 16 + 16;   // two steps of y fragments + flag
+  if (T.mfma_nt == 3 || T.mfma_nt == 4)     // two steps of y fragments (16 or 32 tokens) + flag
+    return (T.mfma_nt - 2) * 2 * 4 * 2 * 64 * 16 + 16;
   if (T.mfma_nt > 0) return kWaves * kMfmaRT * T.mfma_nt * 4 * 64 * 4;
   return T.bt_lds * T.d * 4;
 }
@@ -473,7 +476,7 @@ PhaseArgs zero_args() {
 
 int launch_rowdot(int flags, int bt, const PhaseArgs& a1, void* stream, const char* fn) {
   const RowdotTask& T = a1.rowdot;
-  if (T.mfma_nt == 3 && T.mfma_parts > 1) {
+  if ((T.mfma_nt == 3 || T.mfma_nt == 4) && T.mfma_parts > 1) {
     PhaseArgs z = zero_args();
     z.zero.ptr = T.mfma_tickets;
     z.zero.words = T.mfma_ticket_words;

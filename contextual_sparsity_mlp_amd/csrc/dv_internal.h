@@ -45,7 +45,7 @@ constexpr int kMfmaMinBatch = 2;         //   smallest batch that takes them (ro
 constexpr int kAxmTile = 256;           //   row sums: rows whose ids / coefficients sit in LDS (2 groups a wave)
 constexpr int kAxMfmaMinBatch = 3;       //   row sums (measured: batch 4 row sum 187 -> 130 us)
 constexpr int kMfmaBlocksPerCu = 3;      //   resident blocks per CU the grid is sized for (137 VGPRs)
-constexpr int kMfmaLdsBlocksPerCu = 3;   //   the same for the row dots with y in LDS (133 registers)
+constexpr int kMfmaLdsBlocksPerCu = 3;   //   the same for the row dots with y in LDS (32 tokens; 16: one more)
 
 enum : int { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };   // W_FP8: E4M3 codes, one scale per row
 enum : int { A_NONE = 0, A_RELU = 1, A_GELU = 2 };   // row-sum coefficient activations
@@ -83,10 +83,10 @@ struct RowdotTask {
   int batch, d;
   int bt_lds;              // tokens of y staged in LDS at once (<= BT template)
   int mfma_nt;             // the matrix-core row dots (bf16 rows only, no cache stores):
-                           //   1 / 2: mfma_nt token tiles of 16, y from L2; 3: batch <= 16,
-                           //   y staged in LDS; 0: one wave per row
-  int mfma_parts;          // mfma_nt 3: column parts per 128-row unit (1: no partials)
-  float* mfma_partial;     // [unit][part][2048] partial tiles
+                           //   1 / 2: mfma_nt token tiles of 16, y from L2; 3 / 4: batch
+                           //   <= 16 / 32, y staged in LDS; 0: one wave per row
+  int mfma_parts;          // mfma_nt 3, 4: column parts per 128-row unit (1: no partials)
+  float* mfma_partial;     // [unit][part][2048 per 16 tokens] partial tiles
   uint32_t* mfma_tickets;  // [unit] parts finished, zero on entry
   int mfma_ticket_words;
   int blocks;

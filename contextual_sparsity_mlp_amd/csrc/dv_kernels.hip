@@ -642,7 +642,7 @@ __device__ __forceinline__ void rowdot_mfma_task(const RowdotTask& T, float* lds
   }
 }
 
-// Matrix-core row dots with y in LDS (batch <= 16).  Loading each step's 16 tokens of
+// Matrix-core row dots with y in LDS (batch <= 32).  Loading each step's 16 tokens of
 // y from L2 in every wave, as above, costs as much load throughput as the rows
 // themselves (measured: 5.2 TB/s for the row stream alone, 3.2 TB/s with the y
 // loads).  Here a block owns 128 rows (4 waves x 2 tiles of 16) and a part of the
@@ -654,10 +654,14 @@ __device__ __forceinline__ void rowdot_mfma_task(const RowdotTask& T, float* lds
 // several parts per unit, each part stores its partial tile and the last part to
 // finish (ticket) sums them in part order.
 constexpr int kRdwRows = kWaves * kMfmaRT * kMfmaRows;   // 128 rows per unit
-constexpr int kRdwFrag = 4 * 2 * 64;                     // 16-byte B fragments per step
-constexpr int kRdwTile = kWaves * kMfmaRT * 4 * 64;      // partial tile floats per part
+constexpr int kRdwFrag = 4 * 2 * 64;                     // 16-byte B fragments per step and 16 tokens
+constexpr int kRdwTile = kWaves * kMfmaRT * 4 * 64;      // partial tile floats per part and 16 tokens
 
+// NT: groups of 16 tokens (batch <= 16 NT), each with its own B fragments and accumulators
+template <int NT>
 __device__ __forceinline__ void rdw_task(const RowdotTask& T, float* lds) {
+  constexpr int FRAG = NT * kRdwFrag;                    // fragments per LDS buffer
+  constexpr int TILE = NT * kRdwTile;                    // partial tile floats per part
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
@@ -673,9 +677,10 @@ __device__ __forceinline__ void rdw_task(const RowdotTask& T, float* lds) {
   const int nss = d / kMfmaCols;
   const int P = T.mfma_parts;
   const int items = units * P;
-  uint4* ybuf = reinterpret_cast<uint4*>(lds);            // [2][kRdwFrag]
-  int* flag = reinterpret_cast<int*>(ybuf + 2 * kRdwFrag);
-  // the y fragment slot of this thread: j = tid / 64 (< 4), fragment lane tid % 64
+  uint4* ybuf = reinterpret_cast<uint4*>(lds);            // [2][NT][kRdwFrag]
+  int* flag = reinterpret_cast<int*>(ybuf + 2 * FRAG);
+  // the y fragment slot of this thread in each token group: j = tid / 64 (< 4),
+  // fragment lane tid % 64
   const int yj = tid >> 6, yfl = tid & 63;
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
@@ -716,40 +721,54 @@ __device__ __forceinline__ void rdw_task(const RowdotTask& T, float* lds) {
         for (int j = 0; j < 4; ++j)
           w[rt][j] = ld_stream(reinterpret_cast<const uint4*>(rp[rt] + ss * kMfmaCols + 32 * j));
     };
-    // slot (j, fragment lane fl): token min(fl % 16, batch - 1), columns
-    // step * 128 + 32 j + 8 (fl / 16) .. + 8 (the columns of absent tokens are never
-    // stored)
-    auto load_y = [&](int ss, float4 (&yv)[2]) {
-      const int n = min(yfl & 15, T.batch - 1);
-      const float4* q = reinterpret_cast<const float4*>(
-          T.y + (size_t)n * d + ss * kMfmaCols + 32 * yj + (yfl >> 4) * 8);
-      yv[0] = q[0];
-      yv[1] = q[1];
+    // slot (group nt, j, fragment lane fl): token min(16 nt + fl % 16, batch - 1),
+    // columns step * 128 + 32 j + 8 (fl / 16) .. + 8 (the columns of absent tokens
+    // are never stored)
+    auto load_y = [&](int ss, float4 (&yv)[NT][2]) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = min(nt * kMfmaRows + (yfl & 15), T.batch - 1);
+        const float4* q = reinterpret_cast<const float4*>(
+            T.y + (size_t)n * d + ss * kMfmaCols + 32 * yj + (yfl >> 4) * 8);
+        yv[nt][0] = q[0];
+        yv[nt][1] = q[1];
+      }
     };
-    auto stage_y = [&](const float4 (&yv)[2], int buf) {
-      bf16x8 hi, mid;
-      split8(yv[0], yv[1], hi, mid);
-      ybuf[buf * kRdwFrag + (yj * 2 + 0) * 64 + yfl] = __builtin_bit_cast(uint4, hi);
-      ybuf[buf * kRdwFrag + (yj * 2 + 1) * 64 + yfl] = __builtin_bit_cast(uint4, mid);
+    auto stage_y = [&](const float4 (&yv)[NT][2], int buf) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        bf16x8 hi, mid;
+        split8(yv[nt][0], yv[nt][1], hi, mid);
+        uint4* dst = ybuf + buf * FRAG + nt * kRdwFrag;
+        dst[(yj * 2 + 0) * 64 + yfl] = __builtin_bit_cast(uint4, hi);
+        dst[(yj * 2 + 1) * 64 + yfl] = __builtin_bit_cast(uint4, mid);
+      }
     };
-    f32x4 acc[kMfmaRT] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 acc[kMfmaRT][NT];
+#pragma unroll
+    for (int rt = 0; rt < kMfmaRT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](const uint4 (&w)[kMfmaRT][4], int buf) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 hi = __builtin_bit_cast(bf16x8, ybuf[buf * kRdwFrag + (j * 2 + 0) * 64 + lane]);
-        const bf16x8 mid = __builtin_bit_cast(bf16x8, ybuf[buf * kRdwFrag + (j * 2 + 1) * 64 + lane]);
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int rt = 0; rt < kMfmaRT; ++rt) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, w[rt][j]);
-          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc[rt], 0, 0, 0);
-          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, mid, acc[rt], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const uint4* fr = ybuf + buf * FRAG + nt * kRdwFrag;
+          const bf16x8 hi = __builtin_bit_cast(bf16x8, fr[(j * 2 + 0) * 64 + lane]);
+          const bf16x8 mid = __builtin_bit_cast(bf16x8, fr[(j * 2 + 1) * 64 + lane]);
+#pragma unroll
+          for (int rt = 0; rt < kMfmaRT; ++rt) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, w[rt][j]);
+            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc[rt][nt], 0, 0, 0);
+            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, mid, acc[rt][nt], 0, 0, 0);
+          }
         }
-      }
     };
     // one step with the next one's y and rows requested first (issue order y, rows:
     // the load counter is in order, so waiting for y does not wait for the rows)
     auto step = [&](int ss, const uint4 (&cur)[kMfmaRT][4], uint4 (&nxt)[kMfmaRT][4]) {
-      float4 yv[2];
+      float4 yv[NT][2];
       load_y(ss + 1, yv);
       __builtin_amdgcn_sched_barrier(0);
       load_w(ss + 1, nxt);
@@ -762,7 +781,7 @@ __device__ __forceinline__ void rdw_task(const RowdotTask& T, float* lds) {
 
     uint4 wa[kMfmaRT][4], wb[kMfmaRT][4];
     {
-      float4 yv[2];
+      float4 yv[NT][2];
       load_y(s0, yv);
       __builtin_amdgcn_sched_barrier(0);
       load_w(s0, wa);
@@ -783,40 +802,50 @@ __device__ __forceinline__ void rdw_task(const RowdotTask& T, float* lds) {
       compute(wa, (ss - s0) & 1);
     }
 
-    // the wave's outputs: lane ln of tile rt holds rows 4 (ln / 16) + i, token ln % 16
-    float v[kMfmaRT][4];
+    // the wave's outputs: lane ln of tile rt, group nt holds rows 4 (ln / 16) + i,
+    // token 16 nt + ln % 16
+    float v[kMfmaRT][NT][4];
 #pragma unroll
     for (int rt = 0; rt < kMfmaRT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[rt][i] = acc[rt][i];
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[rt][nt][i] = acc[rt][nt][i];
     if (P > 1) {
-      float* base = T.mfma_partial + (size_t)unit * P * kRdwTile;
-      const int off = (wave * kMfmaRT * 4) * 64 + lane;
+      float* base = T.mfma_partial + (size_t)unit * P * TILE;
+      const int off = (wave * kMfmaRT * NT * 4) * 64 + lane;
 #pragma unroll
       for (int rt = 0; rt < kMfmaRT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          st_dev(&base[(size_t)part * kRdwTile + off + (rt * 4 + i) * 64], v[rt][i]);
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            st_dev(&base[(size_t)part * TILE + off + ((rt * NT + nt) * 4 + i) * 64], v[rt][nt][i]);
       if (!arrive_last(&T.mfma_tickets[unit], (uint32_t)P, flag)) continue;   // block-uniform
 #pragma unroll
       for (int rt = 0; rt < kMfmaRT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[rt][i] = 0.f;
-      for (int p = 0; p < P; ++p) {             // part order; 8 loads in flight per part
-        float t[kMfmaRT][4];
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[rt][nt][i] = 0.f;
+      for (int p = 0; p < P; ++p) {             // part order; 8 NT loads in flight per part
+        float t[kMfmaRT][NT][4];
 #pragma unroll
         for (int rt = 0; rt < kMfmaRT; ++rt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) t[rt][i] = ld_dev(&base[(size_t)p * kRdwTile + off + (rt * 4 + i) * 64]);
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              t[rt][nt][i] = ld_dev(&base[(size_t)p * TILE + off + ((rt * NT + nt) * 4 + i) * 64]);
 #pragma unroll
         for (int rt = 0; rt < kMfmaRT; ++rt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[rt][i] += t[rt][i];
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[rt][nt][i] += t[rt][nt][i];
       }
     }
     if (!any) continue;
-    const int n = m;
-    if (n >= T.batch) continue;
 #pragma unroll
     for (int rt = 0; rt < kMfmaRT; ++rt) {
       int s, r0;
@@ -826,12 +855,17 @@ __device__ __forceinline__ void rdw_task(const RowdotTask& T, float* lds) {
       const int ex = S.rows.expand;
       const int nslots = list_slots(S.rows);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + 4 * g + i;
-        const int slot = (ex == 1) ? r : r / ex;
-        if (r < S.cap && slot < nslots) {
-          const int it = S.rows.idx ? S.rows.idx[slot] : slot;
-          S.out[(size_t)n * S.out_ld + r] = ((unsigned)it < (unsigned)S.rows.items) ? v[rt][i] : 0.f;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = nt * kMfmaRows + m;
+        if (n >= T.batch) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + 4 * g + i;
+          const int slot = (ex == 1) ? r : r / ex;
+          if (r < S.cap && slot < nslots) {
+            const int it = S.rows.idx ? S.rows.idx[slot] : slot;
+            S.out[(size_t)n * S.out_ld + r] = ((unsigned)it < (unsigned)S.rows.items) ? v[rt][nt][i] : 0.f;
+          }
         }
       }
     }
@@ -1985,10 +2019,11 @@ __global__ __launch_bounds__(kThreads) void rowdot_mfma_kernel(PhaseArgs a) {
   rowdot_mfma_task<NT>(a.rowdot, lds);
 }
 
-// Matrix-core row dots with y staged in LDS (batch <= 16).
+// Matrix-core row dots with y staged in LDS (batch <= 16 NT).
+template <int NT>
 __global__ __launch_bounds__(kThreads) void rowdot_mfma_lds_kernel(PhaseArgs a) {
   extern __shared__ float lds[];
-  rdw_task(a.rowdot, lds);
+  rdw_task<NT>(a.rowdot, lds);
 }
 
 template <int FLAGS, int BT>
@@ -2020,9 +2055,13 @@ static int launch_bt(int bt, const PhaseArgs& a, int grid, int lds_bytes, void* 
 int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
   switch (flags) {
     case T_ROWDOT:
-      if (a.rowdot.mfma_nt == 3) {
-        hipLaunchKernelGGL(rowdot_mfma_lds_kernel, dim3(grid), dim3(kThreads), lds_bytes,
-                           static_cast<hipStream_t>(stream), a);
+      if (a.rowdot.mfma_nt == 3 || a.rowdot.mfma_nt == 4) {
+        if (a.rowdot.mfma_nt == 3)
+          hipLaunchKernelGGL((rowdot_mfma_lds_kernel<1>), dim3(grid), dim3(kThreads), lds_bytes,
+                             static_cast<hipStream_t>(stream), a);
+        else
+          hipLaunchKernelGGL((rowdot_mfma_lds_kernel<2>), dim3(grid), dim3(kThreads), lds_bytes,
+                             static_cast<hipStream_t>(stream), a);
         return (int)hipGetLastError();
       }
       if (a.rowdot.mfma_nt > 0) {
