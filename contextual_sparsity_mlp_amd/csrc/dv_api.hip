@@ -81,13 +81,15 @@ constexpr size_t kTimingPairs = 8192;
 // Per-call launch counter (the k-th launch of the current entry point).
 thread_local int t_slot = 0;
 
-int axpy_mfma_lds();
+int axpy_mfma_lds(int tokens);
 int launch(int flags, int bt, const PhaseArgs& a, int grid, int lds, void* stream, const char* fn) {
   if (grid <= 0) return DV_OK;
   if (flags & T_AXPY)
-    for (int s = 0; s < a.axpy.nseg; ++s)
+    for (int s = 0; s < a.axpy.nseg; ++s) {
       if (a.axpy.seg[s].mfma_nt) flags |= T_MFMA;
-  if (flags & T_MFMA) lds = std::max(lds, axpy_mfma_lds());
+      if (a.axpy.seg[s].mfma_nt == 2) flags |= T_MFMA2;
+    }
+  if (flags & T_MFMA) lds = std::max(lds, axpy_mfma_lds((flags & T_MFMA2) ? 32 : 16));
   TimingState& T = timing();
   hipEvent_t ea = nullptr, eb = nullptr;
   const int slot = t_slot++;
@@ -120,8 +122,9 @@ int pick_bt(int batch) { return batch <= 1 ? 1 : (batch == 2 ? 2 : 4); }
 
 // Axpy segment geometry that does not depend on the device.  A batch of at least
 // kAxMfmaMinBatch tokens over bf16 rows whose row length is a multiple of 128 runs on
-// the matrix cores (128-column slices, 16 tokens per block tile); otherwise the wave
-// path (pick_bt tokens per block, each row read once per block tile).
+// the matrix cores (128-column slices, 16 tokens per block tile, 32 above 16 tokens);
+// otherwise the wave path (pick_bt tokens per block, each row read once per block
+// tile).
 struct AxGeo { int vec, nslices, nbt, chunks_max, mfma_nt, bt; };
 AxGeo ax_geo(int batch, int ncols, long long row_stride, dv_dtype wdt, int cap_rows) {
   AxGeo g;
@@ -129,7 +132,7 @@ AxGeo ax_geo(int batch, int ncols, long long row_stride, dv_dtype wdt, int cap_r
   g.vec = (ncols % full == 0 && row_stride % full == 0) ? full : 1;
   g.mfma_nt = 0;
   if (batch >= kAxMfmaMinBatch && wdt == DV_BF16 && ncols % kMfmaCols == 0 && row_stride % 8 == 0)
-    g.mfma_nt = 1;
+    g.mfma_nt = batch <= kMfmaRows ? 1 : 2;
   g.nslices = g.mfma_nt ? ncols / kMfmaCols : cdiv(ncols, kAxSliceLanes * g.vec);
   g.bt = g.mfma_nt ? kMfmaRows * g.mfma_nt : pick_bt(batch);
   g.nbt = cdiv(batch, g.bt);
@@ -420,9 +423,11 @@ int axpy_lds(int bt, int vec = 8) {
                   (16 + kHistBins) * 4);
 }
 // LDS of a matrix-core row-sum block: row ids and a padded coefficient tile of
-// kAxmTile rows for 16 tokens, and the wave sums (a launch with T_MFMA takes the larger
-// of this and its other tasks' needs).
-int axpy_mfma_lds() { return (kAxmTile + 16 * (kAxmTile + 4) + 16 * (kMfmaCols + 1)) * 4; }
+// kAxmTile rows for its 16 or 32 tokens, and the wave sums (a launch with T_MFMA takes
+// the larger of this and its other tasks' needs).
+int axpy_mfma_lds(int tokens) {
+  return (kAxmTile + tokens * (kAxmTile + 4) + tokens * (kMfmaCols + 1)) * 4;
+}
 
 // n: cache rows attended; kv_cap: rows per (token, head) in K and V (>= n).
 void setup_attn(AttnTask& A, const float* q, int q_ld, const void* K, const void* V, dv_dtype kvdt,

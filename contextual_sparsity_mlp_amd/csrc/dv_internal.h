@@ -111,8 +111,8 @@ struct AxpySeg {
   int act2;
   int ncols;               // output columns
   int vec;                 // elements per thread per row (8 bf16 / 4 f32 / 1 scalar)
-  int mfma_nt;             // 1: matrix-core blocks with 16 tokens per block tile (bf16 rows,
-                           //   128-column slices); 0: the wave path
+  int mfma_nt;             // 1 / 2: matrix-core blocks with 16 / 32 tokens per block tile
+                           //   (bf16 rows, 128-column slices); 0: the wave path
   int nslices, nchunks, nbt;
   int block0;              // first block of this segment inside the task
   float* partial;          // [nbt][nchunks][BT][ncols]
@@ -208,8 +208,9 @@ struct ZeroTask {
 // without it carry no fp8 code, which keeps their bf16 loops as tight as before.
 // T_MFMA: some row sum of the launch runs on the matrix cores (AxpySeg::mfma_nt); set by
 // the host launcher, so the wave-path launches keep their register budget.
+// T_MFMA2: those row sums hold 32 tokens per block (mfma_nt 2).
 enum : int { T_ROWDOT = 1, T_ATTN = 2, T_AXPY = 4, T_HIST = 8, T_CLASSIFY = 16, T_WAIT = 32,
-             T_ZERO = 64, T_FP8 = 128, T_KV = 256, T_MFMA = 512 };
+             T_ZERO = 64, T_FP8 = 128, T_KV = 256, T_MFMA = 512, T_MFMA2 = 1024 };
 
 struct PhaseArgs {
   RowdotTask rowdot;

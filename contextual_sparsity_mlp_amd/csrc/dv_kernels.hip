@@ -1450,7 +1450,7 @@ __device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int ba
   }
 }
 
-template <int BT, bool WAIT, bool FP8, bool MFMA>
+template <int BT, bool WAIT, bool FP8, bool MFMA, bool MFMA2 = false>
 __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds) {
   int s = 0;
 #pragma unroll
@@ -1459,7 +1459,11 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
   const AxpySeg S = ax_seg(T, s);
   const int lb = blk - S.block0;
   if constexpr (MFMA && BT > 1 && !WAIT && !FP8) {
-    if (S.mfma_nt) { axpy_mfma_block<1>(S, lb, T.batch, lds); return; }
+    if constexpr (MFMA2) {
+      if (S.mfma_nt == 2) { axpy_mfma_block<2>(S, lb, T.batch, lds); return; }
+    } else {
+      if (S.mfma_nt == 1) { axpy_mfma_block<1>(S, lb, T.batch, lds); return; }
+    }
   }
   if (S.wdt == W_BF16) {
     if (S.vec == 8) axpy_block<BT, 8, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
@@ -1967,8 +1971,8 @@ __device__ __forceinline__ void phase_body(const PhaseArgs& a, float* lds) {
   }
   if constexpr ((FLAGS & T_AXPY) != 0) {
     if (blk >= a.b_axpy && blk < a.b_axpy + a.axpy.blocks) {
-      axpy_task<BT, (FLAGS & T_WAIT) != 0, (FLAGS & T_FP8) != 0, (FLAGS & T_MFMA) != 0>(
-          a.axpy, blk - a.b_axpy, lds);
+      axpy_task<BT, (FLAGS & T_WAIT) != 0, (FLAGS & T_FP8) != 0, (FLAGS & T_MFMA) != 0,
+                (FLAGS & T_MFMA2) != 0>(a.axpy, blk - a.b_axpy, lds);
       return;
     }
   }
@@ -2093,6 +2097,16 @@ int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes,
                      : (int)hipErrorInvalidValue;
     case T_AXPY | T_CLASSIFY | T_MFMA:
       return bt == 4 ? launch_t<T_AXPY | T_CLASSIFY | T_MFMA, 4>(a, grid, lds_bytes, stream)
+                     : (int)hipErrorInvalidValue;
+    // 32 tokens per matrix-core row-sum block (batch > 16)
+    case T_AXPY | T_MFMA | T_MFMA2:
+      return bt == 4 ? launch_t<T_AXPY | T_MFMA | T_MFMA2, 4>(a, grid, lds_bytes, stream)
+                     : (int)hipErrorInvalidValue;
+    case T_ATTN | T_AXPY | T_MFMA | T_MFMA2:
+      return bt == 4 ? launch_t<T_ATTN | T_AXPY | T_MFMA | T_MFMA2, 4>(a, grid, lds_bytes, stream)
+                     : (int)hipErrorInvalidValue;
+    case T_AXPY | T_CLASSIFY | T_MFMA | T_MFMA2:
+      return bt == 4 ? launch_t<T_AXPY | T_CLASSIFY | T_MFMA | T_MFMA2, 4>(a, grid, lds_bytes, stream)
                      : (int)hipErrorInvalidValue;
     case T_ATTN: return launch_t<T_ATTN, 1>(a, grid, lds_bytes, stream);
     case T_ZERO: return launch_t<T_ZERO, 1>(a, grid, lds_bytes, stream);
