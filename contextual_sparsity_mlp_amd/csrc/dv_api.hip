@@ -913,9 +913,10 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   if (nx) {
     // B_M's row sum fills the resident round beside the attention (measured 31.0 us for
     // the launch against 31.5 with six blocks per CU and 33.9 with four); on the
-    // matrix-core path, alone in its launch, three blocks per CU (two row chunks per
-    // slice: measured at batch 16 41 us against 48 with 2000 blocks and 48 with 1152)
-    const int bm_blocks = attn_alone ? 3 * device_cus()
+    // matrix-core path, alone in its launch, few long blocks (at OPT-175B one chunk of
+    // all 1000 rows per 128-column slice, no partials): measured at batch 4 / 16 / 32
+    // 30 / 39 / 57 us against 35 / 41 / 67 with two chunks and 40 / 48 / 84 with five
+    const int bm_blocks = attn_alone ? 2 * device_cus()
                                      : std::max(default_axpy_blocks(), resident_blocks() - a2.attn.blocks - 48);
     // The blocks that finish the scores also build their top-digit histograms, except on
     // the matrix-core path: there a block finishes 16 tokens' scores, one LDS histogram
