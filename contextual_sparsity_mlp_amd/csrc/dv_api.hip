@@ -89,7 +89,15 @@ int launch(int flags, int bt, const PhaseArgs& a, int grid, int lds, void* strea
       if (a.axpy.seg[s].mfma_nt) flags |= T_MFMA;
       if (a.axpy.seg[s].mfma_nt == 2) flags |= T_MFMA2;
     }
-  if (flags & T_MFMA) lds = std::max(lds, axpy_mfma_lds((flags & T_MFMA2) ? 32 : 16));
+  if (flags & T_MFMA) {
+    lds = std::max(lds, axpy_mfma_lds((flags & T_MFMA2) ? 32 : 16));
+    // matrix-core launches run the bt-4 kernel instances; at 2 tokens (the look-ahead
+    // output row sum) every row sum of the launch is a matrix-core one, so the wave
+    // path's token tile does not arise
+    bool all = true;
+    for (int s = 0; s < a.axpy.nseg; ++s) all = all && a.axpy.seg[s].mfma_nt > 0;
+    if (all) bt = 4;
+  }
   TimingState& T = timing();
   hipEvent_t ea = nullptr, eb = nullptr;
   const int slot = t_slot++;
@@ -126,12 +134,13 @@ int pick_bt(int batch) { return batch <= 1 ? 1 : (batch == 2 ? 2 : 4); }
 // otherwise the wave path (pick_bt tokens per block, each row read once per block
 // tile).
 struct AxGeo { int vec, nslices, nbt, chunks_max, mfma_nt, bt; };
-AxGeo ax_geo(int batch, int ncols, long long row_stride, dv_dtype wdt, int cap_rows) {
+AxGeo ax_geo(int batch, int ncols, long long row_stride, dv_dtype wdt, int cap_rows,
+             int mfma_min_batch = kAxMfmaMinBatch) {
   AxGeo g;
   const int full = (wdt == DV_FP8) ? 16 : ((wdt == DV_BF16) ? 8 : 4);
   g.vec = (ncols % full == 0 && row_stride % full == 0) ? full : 1;
   g.mfma_nt = 0;
-  if (batch >= kAxMfmaMinBatch && wdt == DV_BF16 && ncols % kMfmaCols == 0 && row_stride % 8 == 0)
+  if (batch >= mfma_min_batch && wdt == DV_BF16 && ncols % kMfmaCols == 0 && row_stride % 8 == 0)
     g.mfma_nt = batch <= kMfmaRows ? 1 : 2;
   g.nslices = g.mfma_nt ? ncols / kMfmaCols : cdiv(ncols, kAxSliceLanes * g.vec);
   g.bt = g.mfma_nt ? kMfmaRows * g.mfma_nt : pick_bt(batch);
@@ -260,10 +269,13 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   const AxGeo g_bm = ax_geo(batch, F, F, pwdt, r);
   const AxGeo g_ba = ax_geo(batch, h, h, pwdt, r);
   const AxGeo g_wo = ax_geo(batch, d, d, wdt, cap_m + cap_a * dh);   // W2 and W^O rows
+  // (the look-ahead step's output row sum takes the matrix cores from 2 tokens: room
+  // for either geometry)
+  const AxGeo g_wo2 = ax_geo(batch, d, d, wdt, cap_m + cap_a * dh, 2);
   p.t_attn = batch * cap_a;
   p.t_bm = (int)ax_tickets(g_bm);
   p.t_ba = (int)ax_tickets(g_ba);
-  p.t_wo = (int)ax_tickets(g_wo);
+  p.t_wo = (int)std::max(ax_tickets(g_wo), ax_tickets(g_wo2));
   p.t_total = p.t_attn + p.t_bm + p.t_ba + p.t_wo;
   // zero region: tickets | hist_m | hist_a | union tickets (2)
   p.zero = w.off;
@@ -287,7 +299,7 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   p.sa = w.take((size_t)batch * h * 4);
   p.p_bm = w.take(ax_partial_floats(batch, F, g_bm) * 4);
   p.p_ba = w.take(ax_partial_floats(batch, h, g_ba) * 4);
-  p.p_wo = w.take(ax_partial_floats(batch, d, g_wo) * 4);
+  p.p_wo = w.take(std::max(ax_partial_floats(batch, d, g_wo), ax_partial_floats(batch, d, g_wo2)) * 4);
   p.tm = plan_topk_parts(w, batch, F);
   p.ta = plan_topk_parts(w, batch, h);
   // row dots: W1 rows of S_M, W^Q rows of S_A and the two predictor factors
@@ -373,13 +385,13 @@ void add_axpy2(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype
                const float* coef2, int coef2_ld, int act2, int ncols, float* partial,
                uint32_t* tickets, float* out, int out_ld, const float* add0, const float* add1,
                int add_ld, int accumulate, int target_blocks, const float* scale = nullptr,
-               const float* scale2 = nullptr) {
+               const float* scale2 = nullptr, int mfma_min_batch = kAxMfmaMinBatch) {
   T.seg_scale[T.nseg][0] = scale;
   T.seg_scale[T.nseg][1] = scale2;
   AxpySeg& S = T.seg[T.nseg];
   int cap_rows = L.host_count * L.expand + (W2 ? L2.host_count * L2.expand : 0);
   cap_rows = std::max(1, cap_rows);
-  const AxGeo g = ax_geo(batch, ncols, stride, wdt, cap_rows);
+  const AxGeo g = ax_geo(batch, ncols, stride, wdt, cap_rows, mfma_min_batch);
   S.W = W; S.row_stride = stride; S.wdt = wcode(wdt);
   S.rows = L; S.coef = coef; S.coef_ld = coef_ld; S.act = act; S.ncols = ncols;
   S.W2 = W2; S.rows2 = L2; S.coef2 = coef2; S.coef2_ld = coef2_ld; S.act2 = act2;
@@ -851,11 +863,15 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   // After the row dots, the rest of the layer: attention over the cache for S_A; one
   // row sum y_out = y_in + sum_{S_M} ReLU(a) W2 rows + sum_{S_A} o W^O rows; and for
   // the next layer its predictor scores (with top-digit histograms) and top-k.
-  auto add_out = [&](AxpyTask& T, int target) {
+  // (mfma_min_batch 2: the look-ahead step's output row sum, which shares its launch with
+  // the top-k only, runs on the matrix cores from 2 tokens: measured at batch 2 82 us
+  // against 96 for the wave path; the sparse step without a next layer keeps the wave
+  // path there, for its single waiting launch)
+  auto add_out = [&](AxpyTask& T, int target, int mfma_min_batch = kAxMfmaMinBatch) {
     add_axpy2(T, batch, L->W2t, d, wdt, LM, fp(P.a), cap_m, act_code(L->act), L->Wo, LQ, fp(P.o),
               cap_a * dh, A_NONE,
               d, fp(P.p_wo), t_wo, y_out, d, y_in, nullptr, d, 0, target,
-              fp8 ? L->W2s : nullptr, fp8 ? L->Wos : nullptr);
+              fp8 ? L->W2s : nullptr, fp8 ? L->Wos : nullptr, mfma_min_batch);
   };
 
   // Without a next layer, one launch when its blocks fit one resident round: every
@@ -937,7 +953,7 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
       return e;
   }
   PhaseArgs a3 = zero_args();
-  add_out(a3.axpy, default_axpy_blocks());
+  add_out(a3.axpy, default_axpy_blocks(), nx ? 2 : kAxMfmaMinBatch);
   a3.axpy.batch = batch;
   int flags3 = T_AXPY | (fp8 ? T_FP8 : 0);
   if (nx) {
