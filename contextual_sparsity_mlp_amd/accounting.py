@@ -83,7 +83,9 @@ def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: i
     or five (lookahead_launches=5: the predictor's row sums on the matrix cores, for a
     batch): the attention alone, the predictor B factors, then the score histograms
     (the scores read) before the row sum and top-k.
-    Without it (the sparse MLP + MHA alone at small batch), two launches:
+    Without it (the sparse MLP + MHA alone), one launch (sparse_launches=1) that
+    streams everything: W1, W^Q, W2 and W^O rows, K/V, y_in read, y_out written; or
+    two launches:
       1 gathered row dots: W1 rows, W^Q rows, y;
       2 attention, and the row sum over W2 then W^O rows: K/V, W2 rows, W^O rows,
         y_in read, y_out written.
@@ -103,6 +105,8 @@ def phase_bytes(*, batch: int, d: int, F: int, h: int, dh: int, n_ctx: int, r: i
         p1 += 2 * h * dh * row + 2 * batch * h * dh * kv_bytes
     out = u_m * row + u_a * dh * row + 2 * batch * d * 4
     if not with_predictor:
+        if sparse_launches == 1:
+            return [p1 - batch * d * 4 + kv + out]
         return [p1, kv, out] if sparse_launches == 3 else [p1, kv + out]
     p1 += 2 * r * d * pb
     p2 = kv + (r * F + r * h) * pb

@@ -75,27 +75,50 @@ def score_bound(y, A, Bm) -> np.ndarray:
 
 
 def check_sets_certified(got, ref_scores, k, union, bound, what=""):
-    """GPU index set vs the oracle's, allowing only swaps certified by rounding.
+    """GPU union index set vs the oracle's, allowing only differences that the
+    certified per-index rounding bounds explain.
 
-    `ref_scores` are the oracle's float64 scores [B][N] and `bound` their certified
-    error [B][N].  Every index in the symmetric difference of the GPU set and the
-    oracle set must lie within bound of the k-th score of some row."""
-    ref_set = O.select_sets(ref_scores.astype(np.float32).astype(np.float64), k, union)
+    ``ref_scores`` are the oracle's float64 scores [B][N] and ``bound`` their
+    certified error [B][N] (``score_bound``).  With eps_j = bound_j plus two units of
+    fp32 rounding of s_j, every GPU score lies in [lo_j, hi_j] = [s_j - eps_j,
+    s_j + eps_j].  Then, row by row:
+      * an index j the GPU took but the oracle did not must be one that some row's
+        GPU top-k could hold: fewer than k indices i of that row have lo_i > hi_j
+        (those certainly rank above j on the GPU);
+      * an index j the oracle took (in row b's top-k) but the GPU left out of every
+        row must be one the GPU could rank below k others in each such row b: at
+        least k indices i != j have hi_i >= lo_j.
+    Both conditions follow from the bounds alone (no tolerance is assumed), and
+    they certify each differing index through its own and its rivals' bounds.
+    Returns the number of differing indices."""
+    assert union, "the decode layer's look-ahead sets are unions"
+    s32 = ref_scores.astype(np.float32).astype(np.float64)
+    per_row = O.select_sets(s32, k, False)
+    ref_set = O.select_sets(s32, k, True)
     got = np.asarray(got, dtype=np.int64)
     assert np.all(np.diff(got) > 0), f"{what}: set not strictly ascending"
-    diff = np.setxor1d(got, ref_set)
-    if diff.size == 0:
+    took = np.setdiff1d(got, ref_set)       # GPU took, oracle did not
+    left = np.setdiff1d(ref_set, got)       # oracle took, GPU did not
+    if took.size == 0 and left.size == 0:
         return 0
-    B, N = ref_scores.shape
-    kth = [np.sort(ref_scores[b])[::-1][min(k, N) - 1] if k > 0 else np.inf for b in range(B)]
-    for j in diff:
-        ok = False
+    s = np.asarray(ref_scores, dtype=np.float64)
+    eps = np.asarray(bound, dtype=np.float64) + 2.0 * U32 * np.abs(s)
+    lo, hi = s - eps, s + eps
+    B = s.shape[0]
+    lo_sorted = [np.sort(lo[b]) for b in range(B)]
+    hi_sorted = [np.sort(hi[b]) for b in range(B)]
+    for j in took:
+        # number of indices certainly above j in row b
+        above = [lo_sorted[b].size - np.searchsorted(lo_sorted[b], hi[b, j], side="right")
+                 for b in range(B)]
+        assert min(above) < k, (f"{what}: index {j} is in the GPU set, but in every row at "
+                                f"least k = {k} indices certainly outrank it")
+    for j in left:
         for b in range(B):
-            # a swap needs two scores that straddle the k-th one and move past each
-            # other: both lie within the sum of two certified bounds of it
-            tol = 2.0 * float(bound[b].max()) + 4.0 * U32 * abs(kth[b])
-            if abs(ref_scores[b, j] - kth[b]) <= tol:
-                ok = True
-                break
-        assert ok, f"{what}: index {j} differs from the oracle set and is not borderline"
-    return int(diff.size)
+            if j not in per_row[b]:
+                continue
+            # indices other than j that may rank above j in row b
+            maybe = hi_sorted[b].size - np.searchsorted(hi_sorted[b], lo[b, j], side="left") - 1
+            assert maybe >= k, (f"{what}: index {j} is in the oracle's row-{b} top-{k}, which "
+                                f"the GPU could not have left: only {maybe} rivals may outrank it")
+    return int(took.size + left.size)

@@ -38,6 +38,10 @@ def test_c4_batch1_bytes():
                         u_a=c.k_a, with_predictor=False, sparse_launches=3)
     # attention in a launch of its own: the same bytes, split three ways
     assert len(sp3) == 3 and sum(sp3) == sum(sp) and sp3[0] == sp[0]
+    sp1 = A.phase_bytes(batch=1, d=c.d, F=c.F, h=c.h, dh=c.dh, n_ctx=c.n_ctx, r=c.r, u_m=c.k_m,
+                        u_a=c.k_a, with_predictor=False, sparse_launches=1)
+    # everything in one launch: exactly the step's bytes, y read once
+    assert sp1 == [b.selected]
     # the KV append: W^K, W^V in full plus the written rows, one more cached row attended
     kw = dict(batch=2, d=c.d, F=c.F, h=c.h, dh=c.dh, n_ctx=c.n_ctx, r=c.r, u_m=c.k_m, u_a=c.k_a)
     ba, b0 = A.step_bytes(**kw, kv_append=True), A.step_bytes(**kw)

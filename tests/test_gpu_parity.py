@@ -102,6 +102,29 @@ def test_predict_parity(name):
         assert torch.equal(s, s2), "predict not deterministic"
 
 
+@pytest.mark.parametrize("batch", [1, 16])
+def test_predict_c4(batch):
+    """The OPT-175B-shaped predictor (d = 12288, r = 1000, 49152 neurons and 96 heads):
+    one token on the wave path, 16 on the matrix cores; every score inside its
+    certified bound and close to the oracle's."""
+    cfg = CONFIGS["c4"]
+    banner(f"predict c4 batch={batch}")
+    P = synth.make_predictor(cfg, DEV)
+    y = synth.make_y(cfg, DEV, batch=batch)
+    yh = host(y)
+    for A, Bm in ((P["A_M"], P["B_M"]), (P["A_A"], P["B_A"])):
+        N = Bm.shape[1]
+        s = torch.empty((batch, N), dtype=torch.float32, device=DEV)
+        ws = dv.workspace(dv.OP_PREDICT, batch=batch, d=cfg.d, r=cfg.r, N=N)
+        dv.predict(y, A, Bm, s, ws)
+        Ah, Bh = host(A), host(Bm)
+        ref = O.predict_scores(yh, Ah, Bh)
+        got = s.cpu().numpy()
+        bound = score_bound(yh, Ah, Bh)
+        assert np.all(np.abs(got - ref) <= bound), f"c4 B={batch} N={N}: score outside the bound"
+        assert_close(got, ref, TIGHT_MLP, f"c4 B={batch} scores N={N}")
+
+
 # --------------------------------------------------------------------------- #
 # A2 top-k / union: bit-exact on identical scores                             #
 # --------------------------------------------------------------------------- #
@@ -469,9 +492,11 @@ def test_decode_layer_lookahead_uses_input():
     assert not np.array_equal(s_in, s_out)
 
 
-@pytest.mark.parametrize("batch", [1, 2, 16])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8, 16])
 def test_decode_layer_c4(batch):
-    """The OPT-175B-shaped layer at full size (batch 1 is the benchmarked launch)."""
+    """The OPT-175B-shaped layer at full size, at every batch of the workload (batch 1
+    is the benchmarked launch; 4 and 8 take the five-launch look-ahead step, the row
+    dots with the row length split into parts and a partly filled 16-token tile)."""
     cfg = CONFIGS["c4"]
     banner(f"decode_layer c4 batch={batch}")
     r = _layer_case(cfg, batch=batch)

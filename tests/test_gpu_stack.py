@@ -7,8 +7,7 @@ What one GPU holds: 24 layers of bf16 weights (W1t, W2t, W^Q, W^O, the predictor
 each layer's bf16 KV cache for 32 sequences of 2048 tokens, about 155 GB of HBM.
 
 Checks at layers 0, 12 and 23:
-  - the layer output on sampled tokens (tokens are independent given the union sets,
-    so the oracle runs the layer on those tokens only);
+  - the layer output of all 32 tokens (both 16-token groups of the matrix-core tiles);
   - the union sets the layer predicted for the next layer, against the oracle's
     scores for all 32 tokens (certified boundary swaps only).
 """
@@ -27,7 +26,6 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 CHECK_LAYERS = (0, 12, 23)
-SAMPLED_TOKENS = [0, 7, 19, 31]
 
 
 @pytest.mark.timeout(900)
@@ -82,8 +80,6 @@ def test_decode_stack_c5_teacher_forced():
     torch.cuda.synchronize()
     assert np.all(np.isfinite(y_cur.cpu().numpy())), "stack output not finite"
 
-    tok = np.array(SAMPLED_TOKENS)
-    tok_d = torch.tensor(SAMPLED_TOKENS, device=DEV)
     for l in CHECK_LAYERS:
         banner(f"decode stack c5: oracle check of layer {l}")
         sv = saved[l]
@@ -91,9 +87,9 @@ def test_decode_stack_c5_teacher_forced():
         # every layer's sets are unions of per-token top-k: sizes within [k, B k]
         assert cfg.k_m <= len(sv["S_M"]) <= cap_m and cfg.k_a <= len(sv["S_A"]) <= cap_a
         ld = dict(W1t=host(L.W1t), W2t=host(L.W2t), Wq=host(L.Wq), Wo=host(L.Wo),
-                  K=host(L.K.index_select(0, tok_d)), V=host(L.V.index_select(0, tok_d)))
-        y_ref, _ = O.decode_layer(sv["y"][tok], ld, sv["S_M"], sv["S_A"], None, cfg.scale)
-        e = assert_close(sv["y_out"][tok], y_ref, TIGHT_ATTN, f"c5 layer {l}")
+                  K=host(L.K), V=host(L.V))
+        y_ref, _ = O.decode_layer(sv["y"], ld, sv["S_M"], sv["S_A"], None, cfg.scale)
+        e = assert_close(sv["y_out"], y_ref, TIGHT_ATTN, f"c5 layer {l}")
         print(f"c5 layer {l}: |S_M|={len(sv['S_M'])} |S_A|={len(sv['S_A'])} rel err {e:.2e}")
         del ld
         if "next" in sv:
