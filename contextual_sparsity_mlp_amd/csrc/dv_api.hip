@@ -753,12 +753,52 @@ int dv_sparse_mha(const float* y, int batch, int d, int h, int dh, const void* W
   return launch(T_AXPY, bt, a3, a3.axpy.blocks, axpy_lds(bt), stream, fn);
 }
 
-int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const float* y_in, float* y_out,
-                    const int32_t* idx_m, const int32_t* count_m, int max_count_m,
-                    const int32_t* idx_a, const int32_t* count_a, int max_count_a,
-                    int32_t* next_idx_m, int32_t* next_count_m, int32_t* next_idx_a,
-                    int32_t* next_count_a, void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "dv_decode_layer";
+}  // extern "C"
+
+namespace {
+
+// ------------------------------------------------------------------------- //
+// allocation-free scratch                                                   //
+// ------------------------------------------------------------------------- //
+
+// The workspace of dv_decode_layer_noalloc: one copy of this array per device, held
+// by the loaded library until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol; its device address comes from hipGetSymbolAddress, per
+// device, and is the only form ever handed to a kernel.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this device's copy of `scratch` (looked up once per device, with
+// that device current); nullptr on failure, with the error text set.
+void* scratch_ptr(const char* fn) {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    fail(DV_EHIP, "%s: no current HIP device", fn);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      fail(DV_EHIP, "%s: scratch lookup failed: %s", fn, hipGetErrorString(e));
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
+// dv_decode_layer's body.  use_scratch: the workspace is the library's scratch array
+// (ws and ws_bytes are ignored; shapes whose workspace exceeds it are rejected).
+int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int batch,
+                      const float* y_in, float* y_out, const int32_t* idx_m,
+                      const int32_t* count_m, int max_count_m, const int32_t* idx_a,
+                      const int32_t* count_a, int max_count_a, int32_t* next_idx_m,
+                      int32_t* next_count_m, int32_t* next_idx_a, int32_t* next_count_a,
+                      void* ws, size_t ws_bytes, bool use_scratch, void* stream) {
   t_slot = 0;
   CHECK_PTR(L); CHECK_PTR(y_in); CHECK_PTR(y_out);
   CHECK_PTR(idx_m); CHECK_PTR(count_m); CHECK_PTR(idx_a); CHECK_PTR(count_a);
@@ -820,6 +860,15 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   const bool fp8 = wdt == DV_FP8;
   const LayerWs P = plan_layer(batch, d, std::max(F, Fn), std::max(h, hn), dh, n, r, max_count_m,
                                max_count_a, wdt, pwdt);
+  if (use_scratch) {
+    if (P.total > kScratchBytes)
+      return fail(DV_EWORKSPACE, "%s: these shapes need %zu bytes of workspace, more than the "
+                  "%zu of the library's scratch (use dv_decode_layer with a workspace)", fn,
+                  P.total, kScratchBytes);
+    ws = scratch_ptr(fn);
+    if (!ws) return DV_EHIP;
+    ws_bytes = kScratchBytes;
+  }
   if (int e = check_ws(fn, ws, ws_bytes, P.total)) return e;
 
   char* w = static_cast<char*>(ws);
@@ -977,6 +1026,32 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const floa
   if (int e = launch(flags3, bt, a3, a3.topk.blocks + a3.axpy.blocks, lds3, stream, fn)) return e;
   return DV_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int dv_decode_layer(const dv_layer* L, const dv_layer* nx, int batch, const float* y_in, float* y_out,
+                    const int32_t* idx_m, const int32_t* count_m, int max_count_m,
+                    const int32_t* idx_a, const int32_t* count_a, int max_count_a,
+                    int32_t* next_idx_m, int32_t* next_count_m, int32_t* next_idx_a,
+                    int32_t* next_count_a, void* ws, size_t ws_bytes, void* stream) {
+  return decode_layer_impl("dv_decode_layer", L, nx, batch, y_in, y_out, idx_m, count_m,
+                           max_count_m, idx_a, count_a, max_count_a, next_idx_m, next_count_m,
+                           next_idx_a, next_count_a, ws, ws_bytes, false, stream);
+}
+
+int dv_decode_layer_noalloc(const dv_layer* L, const dv_layer* nx, int batch, const float* y_in,
+                            float* y_out, const int32_t* idx_m, const int32_t* count_m,
+                            int max_count_m, const int32_t* idx_a, const int32_t* count_a,
+                            int max_count_a, int32_t* next_idx_m, int32_t* next_count_m,
+                            int32_t* next_idx_a, int32_t* next_count_a, void* stream) {
+  return decode_layer_impl("dv_decode_layer_noalloc", L, nx, batch, y_in, y_out, idx_m, count_m,
+                           max_count_m, idx_a, count_a, max_count_a, next_idx_m, next_count_m,
+                           next_idx_a, next_count_a, nullptr, 0, true, stream);
+}
+
+size_t dv_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int dv_timing_enable(int on) {
   TimingState& T = timing();

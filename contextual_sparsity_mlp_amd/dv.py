@@ -24,8 +24,8 @@ OP_PREDICT, OP_SELECT_TOPK, OP_SPARSE_MLP, OP_SPARSE_MHA, OP_DECODE_LAYER = 1, 2
 
 # Every function declared in include/dv.h.
 EXPORTS = ("dv_last_error", "dv_version", "dv_workspace_bytes", "dv_predict", "dv_select_topk",
-           "dv_sparse_mlp", "dv_sparse_mha", "dv_decode_layer", "dv_timing_enable",
-           "dv_timing_read")
+           "dv_sparse_mlp", "dv_sparse_mha", "dv_decode_layer", "dv_decode_layer_noalloc",
+           "dv_noalloc_scratch_bytes", "dv_timing_enable", "dv_timing_read")
 
 
 class DvError(RuntimeError):
@@ -74,11 +74,16 @@ def lib() -> ctypes.CDLL:
                                     vp, sz, vp]
         L.dv_decode_layer.argtypes = [ctypes.POINTER(LayerStruct), ctypes.POINTER(LayerStruct), i,
                                       vp, vp, vp, vp, i, vp, vp, i, vp, vp, vp, vp, vp, sz, vp]
+        L.dv_decode_layer_noalloc.argtypes = [ctypes.POINTER(LayerStruct),
+                                              ctypes.POINTER(LayerStruct), i, vp, vp, vp, vp, i,
+                                              vp, vp, i, vp, vp, vp, vp, vp]
+        L.dv_noalloc_scratch_bytes.restype = sz
+        L.dv_noalloc_scratch_bytes.argtypes = []
         L.dv_timing_enable.argtypes = [i]
         L.dv_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int),
                                      i, ctypes.POINTER(ctypes.c_int)]
         for name in EXPORTS:
-            if name not in ("dv_last_error", "dv_workspace_bytes"):
+            if name not in ("dv_last_error", "dv_workspace_bytes", "dv_noalloc_scratch_bytes"):
                 getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -226,6 +231,24 @@ def decode_layer(layer: Layer, next_layer, y_in, y_out, idx_m, count_m, max_coun
                                  _ptr(count_a), int(max_count_a), _ptr(next_idx_m),
                                  _ptr(next_count_m), _ptr(next_idx_a), _ptr(next_count_a),
                                  _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def decode_layer_noalloc(layer: Layer, next_layer, y_in, y_out, idx_m, count_m, max_count_m,
+                         idx_a, count_a, max_count_a, next_idx_m, next_count_m, next_idx_a,
+                         next_count_a, stream=None, *, batch=None):
+    """dv_decode_layer_noalloc: decode_layer with the library's per-device scratch as
+    its workspace (no workspace argument, nothing allocated)."""
+    batch = y_in.shape[0] if batch is None else batch
+    nxt = ctypes.byref(next_layer.s) if next_layer is not None else None
+    _check(lib().dv_decode_layer_noalloc(ctypes.byref(layer.s), nxt, batch, _ptr(y_in),
+                                         _ptr(y_out), _ptr(idx_m), _ptr(count_m),
+                                         int(max_count_m), _ptr(idx_a), _ptr(count_a),
+                                         int(max_count_a), _ptr(next_idx_m), _ptr(next_count_m),
+                                         _ptr(next_idx_a), _ptr(next_count_a), _stream(stream)))
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().dv_noalloc_scratch_bytes())
 
 
 def timing_enable(on: bool):

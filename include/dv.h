@@ -203,6 +203,27 @@ int dv_decode_layer(const dv_layer* L, const dv_layer* next, int batch,
                     int32_t* next_idx_a, int32_t* next_count_a,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* dv_decode_layer without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, semantics and results as dv_decode_layer; the
+ * workspace is instead a scratch array of dv_noalloc_scratch_bytes() bytes (64 MiB)
+ * that the library holds on each device it runs on until the process ends.  Nothing
+ * is allocated by the call.  Shapes whose workspace (dv_workspace_bytes with
+ * DV_OP_DECODE_LAYER) exceeds the scratch are rejected with DV_EWORKSPACE before
+ * anything is enqueued (a bf16 OPT-175B-shaped layer fits up to batch 2 with the
+ * look-ahead predictor, up to batch 4 without it).  Every call on
+ * one device shares that device's scratch: calls that may overlap on one device
+ * (other streams, other threads) race and must be serialised by the caller. */
+int dv_decode_layer_noalloc(const dv_layer* L, const dv_layer* next, int batch,
+                            const float* y_in, float* y_out,
+                            const int32_t* idx_m, const int32_t* count_m, int max_count_m,
+                            const int32_t* idx_a, const int32_t* count_a, int max_count_a,
+                            int32_t* next_idx_m, int32_t* next_count_m,
+                            int32_t* next_idx_a, int32_t* next_count_a, void* stream);
+
+/* Bytes of the scratch array behind dv_decode_layer_noalloc (per device). */
+size_t dv_noalloc_scratch_bytes(void);
+
 /* Phase timing for measurement.  dv_timing_enable(1) makes every later call record
  * a hipEvent pair around each of its kernel launches on the call's stream (events are
  * created here, once); dv_timing_enable(0) stops recording.  dv_timing_read()

@@ -192,6 +192,30 @@ def test_decode_layer_rejects(lo, no, args, code):
     assert dv.last_error().startswith("dv_decode_layer")
 
 
+def test_decode_layer_noalloc_rejects_oversized():
+    """The allocation-free entry point refuses shapes whose workspace exceeds the
+    library's scratch (OPT-175B at batch 4 with the look-ahead predictor) on the host,
+    and runs every other argument check of dv_decode_layer first."""
+    lib = dv.lib()
+    assert lib.dv_noalloc_scratch_bytes() == 64 << 20
+    big = dict(d=12288, F=49152, h=96, dh=128, n_ctx=2048, r=1000, k_m=4915, k_a=19,
+               pwdt=dv.DV_BF16)
+    B = 4
+    need = dv.workspace_bytes(dv.OP_DECODE_LAYER, batch=B, d=12288, F=49152, h=96, dh=128,
+                              n_ctx=2048, r=1000, max_count_m=B * 4915, max_count_a=B * 19)
+    assert need > lib.dv_noalloc_scratch_bytes()
+    L, N = _layer(**big), _layer(**big)
+
+    def call(L, N, max_m, max_a):
+        return lib.dv_decode_layer_noalloc(ctypes.byref(L), ctypes.byref(N), B, P, P, P, P, max_m,
+                                           P, P, max_a, P, P, P, P, None)
+    assert call(L, N, B * 4915, min(96, B * 19)) == dv.DV_EWORKSPACE
+    assert "scratch" in dv.last_error() and dv.last_error().startswith("dv_decode_layer_noalloc")
+    # the shared argument checks come first
+    assert call(_layer(**dict(big, W1t=None)), N, B * 4915, min(96, B * 19)) == dv.DV_EINVAL
+    assert call(_layer(**dict(big, K=BAD)), N, B * 4915, min(96, B * 19)) == dv.DV_EALIGN
+
+
 def test_timing_read_empty():
     ms, cnt = dv.timing_read(4)
     assert ms == [] and cnt == []

@@ -1,0 +1,91 @@
+"""dv_decode_layer_noalloc (the entry point for callers that cannot allocate) against
+dv_decode_layer with a caller workspace: equal results on consecutive calls that
+share the library's scratch, the second smaller than the first.  (Its host-side
+rejection of shapes whose workspace exceeds the scratch is a CPU test of the ABI.)"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from contextual_sparsity_mlp_amd import dv, synth
+from contextual_sparsity_mlp_amd.synth import CONFIGS
+from gpu_helpers import banner
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _case(cfg, B, with_next):
+    """Inputs of one decode layer: the layer, its sets (random, ascending), the next
+    layer's predictor when asked for."""
+    L = synth.make_layer(cfg, DEV, batch=B)
+    y = synth.make_y(cfg, DEV, batch=B)
+    cap_m, cap_a = min(cfg.F, B * cfg.k_m), min(cfg.h, B * cfg.k_a)
+    S_M = synth.random_index_set(cfg.F, cap_m, seed=cfg.cfg_id + B).numpy()
+    S_A = synth.random_index_set(cfg.h, cap_a, seed=cfg.cfg_id + B + 1).numpy()
+    i32 = lambda a: torch.as_tensor(np.asarray(a, dtype=np.int32), device=DEV)  # noqa: E731
+    layer = dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, L.A_M, L.B_M, L.A_A, L.B_A,
+                     k_m=cfg.k_m, k_a=cfg.k_a, scale=cfg.scale)
+    nxt = None
+    if with_next:
+        P1 = synth.make_predictor(cfg, DEV, layer=1)
+        nxt = dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, P1["A_M"], P1["B_M"], P1["A_A"],
+                       P1["B_A"], k_m=cfg.k_m, k_a=cfg.k_a, scale=cfg.scale)
+    return dict(cfg=cfg, B=B, L=L, y=y, layer=layer, nxt=nxt, idx_m=i32(S_M),
+                cnt_m=i32([len(S_M)]), cap_m=cap_m, idx_a=i32(S_A), cnt_a=i32([len(S_A)]),
+                cap_a=cap_a)
+
+
+def _run(c, noalloc):
+    cfg, B = c["cfg"], c["B"]
+    y_out = torch.full_like(c["y"], np.nan)
+    outs = [torch.full((c["cap_m"],), -9, dtype=torch.int32, device=DEV),
+            torch.full((1,), -9, dtype=torch.int32, device=DEV),
+            torch.full((c["cap_a"],), -9, dtype=torch.int32, device=DEV),
+            torch.full((1,), -9, dtype=torch.int32, device=DEV)]
+    nx = [o if c["nxt"] is not None else None for o in outs]
+    args = (c["layer"], c["nxt"], c["y"], y_out, c["idx_m"], c["cnt_m"], c["cap_m"], c["idx_a"],
+            c["cnt_a"], c["cap_a"], *nx)
+    if noalloc:
+        dv.decode_layer_noalloc(*args)
+    else:
+        ws = dv.workspace(dv.OP_DECODE_LAYER, batch=B, d=cfg.d, F=cfg.F, h=cfg.h, dh=cfg.dh,
+                          n_ctx=cfg.n_ctx, r=cfg.r, max_count_m=c["cap_m"],
+                          max_count_a=c["cap_a"])
+        ws.fill_(0xA5)   # whatever a caller's workspace holds
+        dv.decode_layer(*args, ws)
+    torch.cuda.synchronize()
+    sets = None
+    if c["nxt"] is not None:
+        sets = (outs[0][: int(outs[1][0])].cpu(), outs[2][: int(outs[3][0])].cpu())
+    return y_out, sets
+
+
+def _same(c, what):
+    ref_y, ref_sets = _run(c, False)
+    got_y, got_sets = _run(c, True)
+    # the same kernels on the same inputs: bit-identical results
+    assert torch.equal(got_y, ref_y), f"{what}: y_out differs from dv_decode_layer"
+    assert torch.isfinite(got_y).all(), f"{what}: non-finite output"
+    if ref_sets is not None:
+        for g, r in zip(got_sets, ref_sets):
+            assert torch.equal(g, r), f"{what}: next-layer set differs"
+
+
+def test_noalloc_matches_workspace_entry_point():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    assert dv.noalloc_scratch_bytes() == 64 << 20
+    c4 = CONFIGS["c4"]
+    # first call: the OPT-175B-shaped layer at batch 2 with the look-ahead predictor
+    # (the largest batch whose workspace fits the scratch)
+    banner("noalloc c4 batch 2 with next layer")
+    _same(_case(c4, 2, True), "c4 B=2")
+    # second call, smaller: OPT-6.7B at batch 1, the scratch holding the first call's
+    # contents (counters and tickets it left behind must not leak in)
+    banner("noalloc c2 batch 1 with next layer")
+    _same(_case(CONFIGS["c2"], 1, True), "c2 B=1")
+    # the benchmarked sparse step: OPT-175B at batch 1 without a next layer
+    banner("noalloc c4 batch 1 last layer")
+    _same(_case(c4, 1, False), "c4 B=1 no next")
