@@ -314,6 +314,9 @@ def main():
                     help="the full decode step: every head's k and v of the current token are "
                          "computed (W^K, W^V read in full), stored at row n_ctx of the cache "
                          "and attended with it")
+    ap.add_argument("--step-path", choices=("auto", "two", "one"), default="auto",
+                    help="launch plan of the one-token bf16 step: the library's default, the "
+                         "two-launch plan, or the one-launch queue")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -331,6 +334,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dv.lib()   # raises if the HIP library is missing
+    dv.set_step_path({"auto": dv.PATH_AUTO, "two": dv.PATH_TWO_LAUNCH,
+                      "one": dv.PATH_ONE_LAUNCH}[args.step_path])
 
     if args.copy_calibrate:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the counters

@@ -32,20 +32,44 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
+    """Compile each source to an object in parallel, then link the shared library."""
     os.makedirs(LIBDIR, exist_ok=True)
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function", *DEVICE_FLAGS, "-I", INCLUDE,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and (res.stdout or res.stderr):
-        sys.stderr.write(res.stdout + res.stderr)
-    os.replace(tmp, LIB)
+    tag = f".tmp{os.getpid()}"
+    common = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+              "-Wno-unused-function", *DEVICE_FLAGS, "-I", INCLUDE]
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(LIBDIR, os.path.splitext(src)[0] + tag + ".o")
+        cmd = [*common, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        objs.append(obj)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                      text=True))
+    failed = False
+    for p in procs:
+        out, err = p.communicate()
+        if p.returncode != 0:
+            failed = True
+            sys.stderr.write(out + err)
+        elif verbose and (out or err):
+            sys.stderr.write(out + err)
+    tmp = LIB + tag
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed to compile the sources")
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

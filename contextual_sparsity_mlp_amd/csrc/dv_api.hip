@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cassert>
 #include <cmath>
 #include <cstdarg>
@@ -31,6 +32,16 @@ int fail(int code, const char* fmt, ...) {
   g_err = buf;
   return code;
 }
+
+// Bounded in-launch waits: poll limit and a target offset that tests raise to make
+// every wait give up (dv_debug_wait_limits).
+constexpr uint32_t kDefaultSpins = 1u << 20;
+std::atomic<uint32_t> g_wait_spins{kDefaultSpins};
+std::atomic<uint32_t> g_wait_extra{0};
+
+// Launch plan of the one-token bf16 sparse step (dv_set_step_path).
+std::atomic<int> g_step_path{DV_PATH_AUTO};
+constexpr int kAutoStepPath = DV_PATH_TWO_LAUNCH;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -81,6 +92,27 @@ constexpr size_t kTimingPairs = 8192;
 // Per-call launch counter (the k-th launch of the current entry point).
 thread_local int t_slot = 0;
 
+// Event pair of the next launch slot when timing is on (null otherwise).
+struct SlotEvents { hipEvent_t a = nullptr, b = nullptr; };
+SlotEvents slot_begin(void* stream) {
+  TimingState& T = timing();
+  SlotEvents ev;
+  const int slot = t_slot++;
+  if (T.on) {
+    std::lock_guard<std::mutex> g(T.mu);
+    if (T.used + 2 <= T.pool.size()) {
+      ev.a = T.pool[T.used++];
+      ev.b = T.pool[T.used++];
+      T.recs.push_back({slot, ev.a, ev.b});
+    }
+  }
+  if (ev.a) (void)hipEventRecord(ev.a, static_cast<hipStream_t>(stream));
+  return ev;
+}
+void slot_end(const SlotEvents& ev, void* stream) {
+  if (ev.b) (void)hipEventRecord(ev.b, static_cast<hipStream_t>(stream));
+}
+
 int axpy_mfma_lds(int tokens);
 int launch(int flags, int bt, const PhaseArgs& a, int grid, int lds, void* stream, const char* fn) {
   if (grid <= 0) return DV_OK;
@@ -98,20 +130,9 @@ int launch(int flags, int bt, const PhaseArgs& a, int grid, int lds, void* strea
     for (int s = 0; s < a.axpy.nseg; ++s) all = all && a.axpy.seg[s].mfma_nt > 0;
     if (all) bt = 4;
   }
-  TimingState& T = timing();
-  hipEvent_t ea = nullptr, eb = nullptr;
-  const int slot = t_slot++;
-  if (T.on) {
-    std::lock_guard<std::mutex> g(T.mu);
-    if (T.used + 2 <= T.pool.size()) {
-      ea = T.pool[T.used++];
-      eb = T.pool[T.used++];
-      T.recs.push_back({slot, ea, eb});
-    }
-  }
-  if (ea) (void)hipEventRecord(ea, static_cast<hipStream_t>(stream));
+  const SlotEvents ev = slot_begin(stream);
   const int err = launch_phase(flags, bt, a, grid, lds, stream);
-  if (eb) (void)hipEventRecord(eb, static_cast<hipStream_t>(stream));
+  slot_end(ev, stream);
   if (err != 0)
     return fail(DV_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString((hipError_t)err));
   return DV_OK;
@@ -252,11 +273,40 @@ MhaWs plan_mha(int batch, int d, int dh, int n_ctx, int cap, dv_dtype wdt) {
   return p;
 }
 
+// Geometry of the one-launch sparse step (StreamTask) for one token: cap_m neuron
+// slots, cap_a head slots, n_att keys per head.
+struct StreamGeo {
+  int n_qi, n_mi, ncm, per_m, nslice, nsplit, n_a, n_items;
+  int c_qdone, c_mdone, c_oready, c_stick, nctr, npart;
+};
+int attn_splits(int n, int base, int other_blocks);
+StreamGeo stream_geo(int d, int dh, int n_att, int cap_m, int cap_a) {
+  StreamGeo g;
+  g.n_qi = cdiv(cap_a * dh, kStreamDotRows);
+  g.n_mi = cdiv(cap_m, kStreamDotRows);
+  g.per_m = cdiv(std::max(1, cdiv(std::max(cap_m, 1), kStreamChunks)), kStreamDotRows) *
+            kStreamDotRows;
+  g.ncm = std::max(1, cdiv(cap_m, g.per_m));
+  g.nslice = cdiv(d, kStreamSlice);
+  g.nsplit = attn_splits(std::max(n_att, 1), std::max(cap_a, 1), 1);
+  g.n_a = cap_a * g.nsplit;
+  g.n_items = g.n_qi + g.n_mi + g.n_a + g.ncm * g.nslice + g.nslice * cap_a;
+  g.c_qdone = kStreamQueues;
+  g.c_mdone = g.c_qdone + cap_a;
+  g.c_oready = g.c_mdone + g.ncm;
+  g.c_stick = g.c_oready + cap_a;
+  g.nctr = g.c_stick + g.nslice;
+  g.npart = g.ncm + cap_a;
+  return g;
+}
+
 // Zero region first: all tickets, both score histograms, row and union tickets.
 struct LayerWs {
   size_t zero, tickets, hist_m, hist_a, rtick_m, rtick_a, uticket, done;
   size_t a, q, o, part, zm, za, sm, sa;
   size_t p_bm, p_ba, p_wo, total;
+  size_t s_ctr = 0, s_atick = 0, s_y = 0, s_partial = 0;   // one-launch sparse step (one token)
+  int s_zero_words = 0;                                     // counters + attention tickets
   int t_attn, t_bm, t_ba, t_wo, t_total, zero_words;
   TopkWs tm, ta;
   RdWs rd;
@@ -304,6 +354,14 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   p.ta = plan_topk_parts(w, batch, h);
   // row dots: W1 rows of S_M, W^Q rows of S_A and the two predictor factors
   p.rd = plan_rd(w, batch, d, cap_m + cap_a * dh + 2 * r, wdt == DV_BF16 && pwdt == DV_BF16);
+  if (batch == 1) {
+    const StreamGeo g = stream_geo(d, dh, n_ctx, cap_m, cap_a);
+    p.s_ctr = w.take((size_t)g.nctr * kCtrStride * 4 + (size_t)cap_a * 4);
+    p.s_atick = p.s_ctr + (size_t)g.nctr * kCtrStride * 4;
+    p.s_zero_words = g.nctr * kCtrStride + cap_a;
+    p.s_y = w.take((size_t)d * 4);
+    p.s_partial = w.take((size_t)g.npart * d * 4);
+  }
   p.total = w.off;
   return p;
 }
@@ -441,6 +499,14 @@ int axpy_mfma_lds(int tokens) {
   return (kAxmTile + tokens * (kAxmTile + 4) + tokens * (kMfmaCols + 1)) * 4;
 }
 
+// Key splits per (token, head) for n keys and `base` (token, head) pairs: splits of
+// about 128 keys keep each block's chain of dependent loads short; with few pairs and
+// nothing else in the launch, more splits spread the cache over the chip.
+int attn_splits(int n, int base, int other_blocks) {
+  int ns = std::max(cdiv(n, 128), other_blocks > 0 ? 1 : cdiv(device_cus(), base));
+  return std::max(1, std::min(ns, attn_nsplit_max(n)));
+}
+
 // n: cache rows attended; kv_cap: rows per (token, head) in K and V (>= n).
 void setup_attn(AttnTask& A, const float* q, int q_ld, const void* K, const void* V, dv_dtype kvdt,
                 int batch, int h, int n, int kv_cap, int dh, RowList heads, float scale, float* part,
@@ -448,12 +514,7 @@ void setup_attn(AttnTask& A, const float* q, int q_ld, const void* K, const void
   A.q = q; A.q_ld = q_ld; A.K = K; A.V = V; A.kvdt = (kvdt == DV_BF16) ? W_BF16 : W_F32;
   A.batch = batch; A.h = h; A.n = n; A.cap = kv_cap; A.dh = dh; A.heads = heads; A.scale = scale;
   const int cap = heads.host_count;
-  // Splits of about 128 keys keep each block's chain of dependent loads short;
-  // with few (token, head) pairs and nothing else in the launch, more splits
-  // spread the cache over the chip.
-  const int base = std::max(1, batch * cap);
-  int ns = std::max(cdiv(n, 128), other_blocks > 0 ? 1 : cdiv(device_cus(), base));
-  ns = std::max(1, std::min(ns, attn_nsplit_max(n)));
+  const int ns = attn_splits(n, std::max(1, batch * cap), other_blocks);
   A.nsplit = ns;
   A.per = cdiv(n, ns);
   A.part = part; A.tickets = tickets; A.o = o; A.o_ld = o_ld;
@@ -884,6 +945,68 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
   const RowList LQ = make_list(idx_a, count_a, max_count_a, dh, h);
   const RowList LH = make_list(idx_a, count_a, max_count_a, 1, h);
 
+  // Without a next layer, one token and bf16 rows: the whole step is one launch whose
+  // resident blocks work through one ordered queue (row dots, attention, row sums; see
+  // StreamTask), so no launch boundary, prologue or block-end spread sits between its
+  // parts.
+  const int path = g_step_path.load() == DV_PATH_AUTO ? kAutoStepPath : g_step_path.load();
+  if (path == DV_PATH_ONE_LAUNCH && !nx && batch == 1 && wdt == DV_BF16 && !append) {
+    const StreamGeo G = stream_geo(d, dh, n_att, max_count_m, max_count_a);
+    StreamTask t;
+    memset(&t, 0, sizeof t);
+    t.W1 = L->W1t; t.W2 = L->W2t; t.Wq = L->Wq; t.Wo = L->Wo;
+    t.LM = LM; t.LQ = LQ;
+    t.d = d; t.dh = dh; t.act = act_code(L->act);
+    t.y = y_in; t.y_out = y_out;
+    t.a = fp(P.a); t.q = fp(P.q); t.partial = fp(P.s_partial);
+    t.ctr = up(P.s_ctr);
+    setup_attn(t.at, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, 1, h, n_att, kv_cap, dh, LH,
+               L->scale, fp(P.part), up(P.s_atick), fp(P.o), cap_a * dh, 1);
+    assert(t.at.nsplit == G.nsplit);
+    t.c_qdone = G.c_qdone; t.c_mdone = G.c_mdone; t.c_oready = G.c_oready; t.c_stick = G.c_stick;
+    t.n_qi = G.n_qi; t.n_mi = G.n_mi; t.n_a = G.n_a;
+    t.ncm = G.ncm; t.per_m = G.per_m; t.nslice = G.nslice; t.n_items = G.n_items;
+    t.spins = g_wait_spins.load(); t.extra = g_wait_extra.load();
+    t.fault = fault_word();
+    // LDS: y for the dot items, shared with the row-sum and attention scratch; 64 bytes
+    // of block words after it
+    t.lds_union = (int)align256((size_t)std::max({d * 4, (2 * kAxpyTileRows +
+                                                            kAxGroups * kStreamSlice) * 4,
+                                                   attn_lds()}));
+    const int lds = t.lds_union + 64;
+    const int kvc = L->kvdt == DV_BF16 ? W_BF16 : W_F32;
+    const int per_cu = stream_occupancy(kvc, lds);
+    t.grid = (per_cu * device_cus()) / 64 * 64;
+    // the first round of items (one per block) all dots, plus a quarter round more, so
+    // that the heads' W^Q rows are dotted when the attention items are taken
+    t.n_mfirst = std::max(0, std::min(G.n_mi, t.grid + t.grid / 4 - G.n_qi));
+    if (t.grid >= 64 && t.fault) {
+      // y_out is y: the blocks stage y from a copy, so that no block reads an element of y
+      // another block has already overwritten
+      if (y_in == y_out) {
+        float* yc = fp(P.s_y);
+        const hipError_t e = hipMemcpyAsync(yc, y_in, (size_t)d * 4, hipMemcpyDeviceToDevice,
+                                            static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(DV_EHIP, "%s: copy of y failed: %s", fn, hipGetErrorString(e));
+        t.y = yc;
+      }
+      // the counters start at zero: a small launch clears them
+      PhaseArgs z = zero_args();
+      z.zero.ptr = up(P.s_ctr);
+      z.zero.words = P.s_zero_words;
+      z.zero.blocks = std::max(1, std::min(cdiv(P.s_zero_words, kThreads * 4), 64));
+      int err = launch_phase(T_ZERO, 1, z, z.zero.blocks, 0, stream);
+      if (err == 0) {
+        const SlotEvents ev = slot_begin(stream);
+        err = launch_stream(kvc, t, t.grid, lds, stream);
+        slot_end(ev, stream);
+      }
+      if (err != 0)
+        return fail(DV_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString((hipError_t)err));
+      return DV_OK;
+    }
+  }
+
   // Phase 1: every gathered row dotted with y_in (W1 rows of S_M, W^Q columns of
   // S_A, and the next layer's predictor factors A_M, A_A); clears the counters and
   // histograms the later phases use.
@@ -945,13 +1068,15 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
     add_out(f.axpy, std::max(1, resident_blocks() - f.attn.blocks));
     AxpySeg& S = f.axpy.seg[0];
     S.wait_ctr = up(P.done);
-    S.wait_target = (uint32_t)f.attn.blocks;
+    S.wait_target = (uint32_t)f.attn.blocks + g_wait_extra.load();
+    f.axpy.spins = g_wait_spins.load();
+    f.axpy.fault = fault_word();
     f.axpy.batch = batch;
     const int grid = f.attn.blocks + f.axpy.blocks;
     const int lds = std::max(axpy_lds(bt), attn_lds());
     const int fit = std::min(resident_blocks(),
                              phase_occupancy(T_ATTN | T_AXPY | T_WAIT, bt, lds) * device_cus());
-    if (grid <= fit) return launch(T_ATTN | T_AXPY | T_WAIT, bt, f, grid, lds, stream, fn);
+    if (grid <= fit && f.axpy.fault) return launch(T_ATTN | T_AXPY | T_WAIT, bt, f, grid, lds, stream, fn);
   }
 
   // Otherwise two launches: the attention (its last split of each head combines the
@@ -1052,6 +1177,30 @@ int dv_decode_layer_noalloc(const dv_layer* L, const dv_layer* nx, int batch, co
 }
 
 size_t dv_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int dv_check(void* stream) {
+  const char* fn = "dv_check";
+  uint32_t v = 0;
+  const int e = fault_take(stream, &v);
+  if (e != 0) return fail(DV_EHIP, "%s: %s", fn, hipGetErrorString((hipError_t)e));
+  if (v) return fail(DV_ETIMEOUT, "%s: a wait inside an earlier launch on this device gave up "
+                     "(its blocks were not all resident, or its producers never arrived); "
+                     "the outputs that depended on it were written as NaN", fn);
+  return DV_OK;
+}
+
+int dv_set_step_path(int path) {
+  if (path != DV_PATH_AUTO && path != DV_PATH_TWO_LAUNCH && path != DV_PATH_ONE_LAUNCH)
+    return fail(DV_EINVAL, "dv_set_step_path: unknown path %d", path);
+  g_step_path.store(path);
+  return DV_OK;
+}
+
+int dv_debug_wait_limits(unsigned spins, unsigned extra) {
+  g_wait_spins.store(spins ? spins : kDefaultSpins);
+  g_wait_extra.store(extra);
+  return DV_OK;
+}
 
 int dv_timing_enable(int on) {
   TimingState& T = timing();

@@ -131,6 +131,8 @@ struct AxpySeg {
 };
 
 struct AxpyTask {
+  uint32_t spins;          // bounded waits (AxpySeg::wait_ctr): poll limit
+  uint32_t* fault;         // device word a wait that gave up marks (see dv_check)
   AxpySeg seg[kMaxSeg];
   // W_FP8 segments: per-row scales of the first / second source (row item*expand + e),
   // folded into the coefficients; kept apart from AxpySeg, whose by-value selection
@@ -160,6 +162,63 @@ struct AttnTask {
   int o_ld;
   int blocks;              // batch * cap * nsplit
   uint32_t* done_ctr;      // optional: +1 per finished block, after its stores
+};
+
+// The sparse step in one launch (one token, bf16 rows, no next layer): every block is
+// resident at once and works through one ordered queue of items,
+//   dot items   4 gathered rows each (1 per wave) dotted with y: the W^Q rows of the
+//               selected heads, then the W1 rows of the selected neurons;
+//   attn items  one key split of one selected head;
+//   sum items   one 256-column slice of a row sum: the W2 rows of one chunk of the
+//               neuron list (coefficients sigma(a)), chunk-major, then the W^O rows of
+//               one head (coefficients o), head-major.
+// Queue order: W^Q dots, the first n_mfirst W1 dots (so that the first round of items,
+// one per block, is all dots), the attention items (their heads' W^Q rows are dotted by
+// the time blocks come back for a second item), the remaining W1 dots, the W2 sums,
+// the W^O sums.  y sits in LDS for the dot items; the attention and sum scratch share
+// that region, so a block stages y again before a dot item that follows an attention
+// item (sum items come after every dot item).
+// Item i belongs to queue i % kStreamQueues; the blocks of a queue take its items in
+// order (each block starts with one of the first grid items and claims each later
+// item of its queue from that queue's counter), so a block only waits for items taken
+// before its own.  Readiness is counted per head (W^Q dots, attention) and per
+// W1 chunk; each sum item stores its partial slice and the last one of a slice adds
+// the partials in chunk order to y (fixed order: the result does not depend on which
+// block took which item).
+constexpr int kStreamRowsPerWave = 1;
+constexpr int kStreamDotRows = kWaves * kStreamRowsPerWave;   // rows per dot item
+constexpr int kStreamSlice = 256;                             // columns per sum item
+constexpr int kStreamChunks = 16;                             // W2 chunks (target)
+constexpr int kStreamU = 16;                                  // rows in flight per row group
+constexpr int kStreamQueues = 8;                              // claim counters (item i: queue i % 8)
+// Counters sit one per 256-byte line (same-address atomics and polls serialise); the
+// counter of index c is ctr[c * kCtrStride].
+constexpr int kCtrStride = 64;
+
+struct StreamTask {
+  const void* W1; const void* W2; const void* Wq; const void* Wo;   // bf16 rows of d
+  RowList LM;              // neurons: rows of W1t / W2t
+  RowList LQ;              // heads, expand dh: rows of W^Q / W^O
+  int d, dh, act;
+  const float* y;          // [d] (a copy in the workspace when y_out is y)
+  float* y_out;            // [d] = y + MLP + MHA
+  float* a;                // [cap_m] W1 row dots
+  float* q;                // [cap_a * dh] W^Q row dots (the attention's q)
+  float* partial;          // [ncm + cap_a][d] partial slices of the row sum
+  AttnTask at;             // attention of the selected heads, batch 1, tickets in the workspace
+  uint32_t* ctr;           // counters (zeroed by the launch before), index c at c * kCtrStride:
+                           //   [0, kStreamQueues) claims, then q_done[cap_a] (dot items per
+                           //   head), m_done[ncm] (per W2 chunk), o_ready[cap_a], slice tickets
+  int c_qdone, c_mdone, c_oready, c_stick;   // first counter index of each group
+  int grid;                // a multiple of 64; block b serves queue (b / 8) % kStreamQueues
+  int n_qi, n_mi, n_a;     // dot items over W^Q rows / W1 rows, attention items
+  int n_mfirst;            // W1 dot items queued before the attention items
+  int ncm, per_m;          // W2 chunks, rows per chunk (a multiple of kStreamDotRows)
+  int nslice;              // column slices
+  int n_items;
+  int lds_union;           // bytes of the LDS region shared by y / sum / attention
+  uint32_t spins, extra;   // bounded waits: poll limit; target offset (0 except in tests)
+  uint32_t* fault;
 };
 
 // Exact top-k of score rows, in two steps that each spread over many blocks:
@@ -223,6 +282,14 @@ struct PhaseArgs {
 
 // Host-side launcher implemented in dv_kernels.hip.  Returns a hipError_t as int.
 int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream);
+// The one-launch sparse step (kvdt: W_BF16 or W_F32 cache); blocks per CU it keeps
+// resident with lds_bytes of LDS (0 on error).
+int launch_stream(int kvdt, const StreamTask& t, int grid, int lds_bytes, void* stream);
+int stream_occupancy(int kvdt, int lds_bytes);
+// Device address of this device's fault word (set by in-launch waits that gave up);
+// nullptr on error.  fault_take reads and clears it after synchronising `stream`.
+uint32_t* fault_word();
+int fault_take(void* stream, uint32_t* value);
 // Blocks per CU of the kernel behind (flags, bt) that the runtime keeps resident with
 // lds_bytes of dynamic LDS (0 for mixes it does not cover or on error).
 int phase_occupancy(int flags, int bt, int lds_bytes);

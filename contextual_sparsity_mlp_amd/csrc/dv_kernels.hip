@@ -34,6 +34,7 @@
 // a later launch reads use plain stores (a launch boundary orders them).  There are
 // no floating-point atomics; only integer tickets and histograms.
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <type_traits>
 #include <math.h>
 #include <stdint.h>
@@ -149,21 +150,37 @@ __device__ __forceinline__ bool arrive_last(uint32_t* ticket, uint32_t expected,
   return *flag != 0;
 }
 
+// The device's fault word: a bounded wait that gives up sets bit 0 (dv_check reports
+// it), so that a launch whose blocks were not all resident at once, or whose
+// producers never came, ends normally and says so instead of passing on values it
+// never received.
+__device__ uint32_t dv_fault;
+
 // Waits until *ctr >= target, where other blocks of the same launch raise *ctr.
-// Launches that wait are sized so all their blocks are resident at once and the
-// raising blocks come first in block order; the wait is still bounded (about a
-// quarter of a second), so it ends even if that ever failed to hold.
-constexpr uint32_t kWaitSpins = 1u << 20;
-__device__ __forceinline__ void wait_count(const uint32_t* ctr, uint32_t target) {
+// Launches that wait are sized so all their blocks are resident at once, and a block
+// only waits for work that was handed out before its own; the wait is still bounded
+// (`spins` polls), so it ends even if that ever failed to hold.  Returns true in
+// every thread if it gave up (after marking *fault); the caller then writes NaN
+// wherever it would have used the awaited values.
+// `bcast` is an LDS word of the block (free for this call) through which thread 0
+// hands its outcome to the others.
+__device__ __forceinline__ bool wait_ge(const uint32_t* ctr, uint32_t target, uint32_t spins,
+                                        uint32_t* fault, int* bcast) {
   if (threadIdx.x == 0) {
-    uint32_t spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
-           spins < kWaitSpins) {
+    int gave_up = 0;
+    uint32_t n = 0;
+    while (__hip_atomic_load(const_cast<uint32_t*>(ctr), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (n++ >= spins) { gave_up = 1; break; }
       __builtin_amdgcn_s_sleep(8);
-      ++spins;
     }
+    if (gave_up) __hip_atomic_fetch_or(fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *bcast = gave_up;
   }
   __syncthreads();
+  const bool r = *bcast != 0;
+  __syncthreads();
+  return r;
 }
 
 // Raises *ctr by one once every thread's stores of this block are complete.
@@ -952,7 +969,8 @@ __device__ __forceinline__ void fp8_rows(const int* lrow, const float* lcoef, in
 // One block: a slice of kAxSliceLanes*VEC output columns and a chunk of the row list.
 template <int BT, int VEC, int WT, bool WAIT>
 __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, const float* sc2,
-                                           int lb, int batch, float* lds) {
+                                           int lb, int batch, float* lds,
+                                           const AxpyTask* task = nullptr) {
   constexpr int U = 4;
   constexpr int SW = kAxSliceLanes * VEC;    // columns per slice
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1060,7 +1078,7 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
     // one source's share of rows: coefficients staged in LDS a tile at a time, then the
     // row slices streamed by the row groups
     auto rows_of = [&](const RowList& L, const void* W, const float* cf, int cld, int rl,
-                       const float* sc, bool coherent, int nr) {
+                       const float* sc, bool coherent, int nr, bool poison) {
       const int per = (nr + S.nchunks - 1) / S.nchunks;
       const int r0 = min(chunk * per, nr);
       const int r1 = min(r0 + per, nr);
@@ -1083,6 +1101,7 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
               c = coherent ? ld_dev(cp) : *cp;
               c = activate(c, rl);
               if constexpr (WT == W_FP8) c *= sc[item * ex + e];
+              if (poison) c = __builtin_nanf("");
             }
             lcoef[b * kAxpyTile + i] = c;
           }
@@ -1122,11 +1141,13 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
         }
       }
     };
-    rows_of(S.rows, S.W, S.coef, S.coef_ld, S.act, sc1, false, n1);
+    rows_of(S.rows, S.W, S.coef, S.coef_ld, S.act, sc1, false, n1, false);
     if (n2 > 0) {
       // coefficients of the second source written in this launch: read coherently
-      if (S.wait_ctr) wait_count(S.wait_ctr, S.wait_target);
-      rows_of(S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, sc2, S.wait_ctr != nullptr, n2);
+      const bool gave_up = S.wait_ctr &&
+          wait_ge(S.wait_ctr, S.wait_target, task->spins, task->fault, reinterpret_cast<int*>(lds));
+      rows_of(S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, sc2, S.wait_ctr != nullptr, n2,
+              gave_up);
     }
   }
 
@@ -1466,8 +1487,8 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
     }
   }
   if (S.wdt == W_BF16) {
-    if (S.vec == 8) axpy_block<BT, 8, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
-    else axpy_block<BT, 1, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
+    if (S.vec == 8) axpy_block<BT, 8, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds, &T);
+    else axpy_block<BT, 1, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds, &T);
   } else if (FP8 && S.wdt == W_FP8) {
     // d % 16 == 0 (host check); fp8 layers never take the waiting single launch
     if constexpr (FP8 && !WAIT) {
@@ -1476,8 +1497,8 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
       axpy_block<BT, 16, W_FP8, false>(S, sc[0], sc[1], lb, T.batch, lds);
     }
   } else {
-    if (S.vec == 4) axpy_block<BT, 4, W_F32, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
-    else axpy_block<BT, 1, W_F32, WAIT>(S, nullptr, nullptr, lb, T.batch, lds);
+    if (S.vec == 4) axpy_block<BT, 4, W_F32, WAIT>(S, nullptr, nullptr, lb, T.batch, lds, &T);
+    else axpy_block<BT, 1, W_F32, WAIT>(S, nullptr, nullptr, lb, T.batch, lds, &T);
   }
 }
 
@@ -1488,16 +1509,19 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
 // Each key group (LPK lanes sharing a key row) keeps a running max m, sum l and
 // p.V for its keys; groups merge in LDS (weight exp(m_g - M), 0 for a group that
 // saw no key) and the splits of a (token, head) merge the same way.
-template <int WT>
-__device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds) {
+// One (token b, head slot, key split) of the attention.  COHERENT_Q: q was written by
+// other blocks of the same launch (read with device-coherent loads).  poison: the
+// inputs are not trustworthy (a wait gave up), so the outputs are written as NaN.
+// Returns true in every thread of the block that stored the head's o (the last split
+// to finish, or the only one).
+// U: key rows in flight per key group (16 key groups of a 256-thread block at d_h = 128,
+// bf16: U = 8 keeps a 128-key split in flight at once).
+template <int WT, bool COHERENT_Q, int U = 4>
+__device__ __forceinline__ bool attn_split(const AttnTask& T, int b, int slot, int split,
+                                           float* lds, bool poison) {
   constexpr int VEC = (WT == W_BF16) ? 8 : 4;   // elements per 16-byte load
-  constexpr int U = 4;                           // key rows in flight per key group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = T.heads.host_count;
-  const int split = blk % T.nsplit;
-  const int rest = blk / T.nsplit;
-  const int slot = rest % cap;
-  const int b = rest / cap;
   const int dh = T.dh;
   // the list count, the head index (slot < capacity: readable) and q are independent
   // loads, issued together
@@ -1518,10 +1542,13 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
 
   float qv[VEC];
 #pragma unroll
-  for (int v = 0; v < VEC; ++v)
-    qv[v] = T.scale * T.q[(size_t)b * T.q_ld + (size_t)slot * dh + dg * VEC + v];
-  if (slot >= nslots) return;
-  if ((unsigned)head >= (unsigned)T.h) return;   // contributes nothing; W^O skips it too
+  for (int v = 0; v < VEC; ++v) {
+    const float* qp = &T.q[(size_t)b * T.q_ld + (size_t)slot * dh + dg * VEC + v];
+    qv[v] = T.scale * (COHERENT_Q ? ld_dev(qp) : *qp);
+    if (poison) qv[v] = __builtin_nanf("");
+  }
+  if (slot >= nslots) return false;
+  if ((unsigned)head >= (unsigned)T.h) return false;   // contributes nothing; W^O skips it too
   const size_t row0 = ((size_t)b * T.h + head) * (size_t)T.cap + k0;   // first key row
   constexpr int ESZ = (WT == W_BF16) ? 2 : 4;
   const char* Kb = static_cast<const char*>(T.K);
@@ -1610,13 +1637,13 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
   const int w2 = dh + 2;
   if (T.nsplit == 1) {
     if (tid < dh) st_dev(&T.o[(size_t)b * T.o_ld + (size_t)slot * dh + tid], O / L);
-    return;
+    return true;
   }
   float* P = T.part + (((size_t)b * cap + slot) * T.nsplit + split) * w2;
   if (tid < dh) st_dev(&P[2 + tid], O);
   if (tid == 0) { st_dev(&P[0], M); st_dev(&P[1], L); }
   int* flag = reinterpret_cast<int*>(lds + 128 + 2048);
-  if (!arrive_last(&T.tickets[(size_t)b * cap + slot], (uint32_t)T.nsplit, flag)) return;
+  if (!arrive_last(&T.tickets[(size_t)b * cap + slot], (uint32_t)T.nsplit, flag)) return false;
   // combine the splits: (max, sum) of every split staged in LDS with one parallel load,
   // the p.V pieces fetched in batches of independent loads, summed in split order
   const float* P0 = T.part + ((size_t)b * cap + slot) * T.nsplit * w2;
@@ -1647,6 +1674,15 @@ __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds
     }
     st_dev(&T.o[(size_t)b * T.o_ld + (size_t)slot * dh + tid], OO / LL);
   }
+  return true;
+}
+
+template <int WT>
+__device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds) {
+  const int cap = T.heads.host_count;
+  const int split = blk % T.nsplit;
+  const int rest = blk / T.nsplit;
+  (void)attn_split<WT, false>(T, rest / cap, rest % cap, split, lds, false);
 }
 
 // --------------------------------------------------------------------------- //
@@ -1932,6 +1968,324 @@ __device__ __forceinline__ void topk_task(int stage, const TopkTask& T, int blk,
   const TopkProblem& P = pi == 0 ? T.p[0] : T.p[1];
   if (stage == T_HIST) hist_block(P, lb, lds);
   else classify_block(P, lb, lds);
+}
+
+// --------------------------------------------------------------------------- //
+// the sparse step in one launch (see StreamTask)                               //
+// --------------------------------------------------------------------------- //
+
+// Dot item k: 8 gathered rows (2 per wave) dotted with y (in LDS), stored coherently
+// for the attention (W^Q rows) or the W2 row sums (W1 rows) of this launch.
+__device__ __forceinline__ void stream_dot(const StreamTask& T, int k, const float* ylds,
+                                           bool poison) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool qrows = k < T.n_qi;
+  const int base = (qrows ? k : k - T.n_qi) * kStreamDotRows;
+  const RowList L = qrows ? T.LQ : T.LM;
+  const uint16_t* W = static_cast<const uint16_t*>(qrows ? T.Wq : T.W1);
+  float* out = qrows ? T.q : T.a;
+  const int ex = L.expand;
+  const int cap = L.host_count * ex;
+  const int nslots = list_slots(L);
+#pragma unroll 1
+  for (int j = 0; j < kStreamRowsPerWave; ++j) {
+    const int r = base + wave * kStreamRowsPerWave + j;
+    const int slot = r / ex;
+    if (r >= cap || slot >= nslots) continue;                   // wave-uniform
+    const int item = L.idx ? L.idx[slot] : slot;
+    if ((unsigned)item >= (unsigned)L.items) continue;          // no consumer reads it
+    const long long row = (long long)item * ex + (r - slot * ex);
+    float acc[1] = {0.f};
+    rowdot_bf16<1, 24>(reinterpret_cast<const uint4*>(W + row * T.d), ylds, T.d, 1, lane, acc);
+    float v = wave_sum(acc[0]);
+    if (poison) v = __builtin_nanf("");
+    if (lane == 0) st_dev(&out[r], v);
+  }
+}
+
+// Sum item: one 256-column slice of the row sum over the W2 rows of one chunk of the
+// neuron list (coefficients sigma(a)) or over the W^O rows of one head (coefficients
+// o).  Stores the slice of its partial; the last item of the slice adds the partials
+// in chunk order (W2 chunks, then heads) to y and stores y_out.
+// Latency: the readiness poll goes out with the row-id staging, and the coefficient
+// loads with the first rows' loads (coefficients first: loads complete in order, so
+// waiting for them leaves the rows in flight); two round trips before the first FMA.
+__device__ __forceinline__ void stream_sum(const StreamTask& T, int x, float* lds, int* sm,
+                                           bool& poison) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave * 2 + (lane >> 5), hl = lane & 31;
+  const int d = T.d, dh = T.dh;
+  const int cap_a = T.LQ.host_count;
+  const bool w2 = x < T.ncm * T.nslice;
+  int slice, pidx, r0, r1, head = 0;
+  const uint32_t* ready = nullptr;     // counter that must reach `target` first
+  uint32_t target = 0;
+  const uint16_t* W;
+  if (w2) {
+    const int chunk = x / T.nslice;
+    slice = x - chunk * T.nslice;
+    pidx = chunk;
+    r0 = chunk * T.per_m;
+    r1 = min(r0 + T.per_m, list_slots(T.LM));
+    W = static_cast<const uint16_t*>(T.W2);
+    if (r1 > r0) {
+      // every dot item of the chunk (counted over its capacity) has stored its row dots
+      const int rows_cap = min(T.per_m, T.LM.host_count - r0);
+      ready = &T.ctr[(T.c_mdone + chunk) * kCtrStride];
+      target = (uint32_t)((rows_cap + kStreamDotRows - 1) / kStreamDotRows) + T.extra;
+    }
+  } else {
+    x -= T.ncm * T.nslice;
+    const int slot = x / T.nslice;
+    slice = x - slot * T.nslice;
+    pidx = T.ncm + slot;
+    r0 = slot * dh;
+    r1 = r0;
+    W = static_cast<const uint16_t*>(T.Wo);
+    if (slot < list_slots(T.LQ)) {
+      head = T.LQ.idx ? T.LQ.idx[slot] : slot;
+      if ((unsigned)head < (unsigned)T.LQ.items) {
+        r1 = r0 + dh;
+        ready = &T.ctr[(T.c_oready + slot) * kCtrStride];
+        target = 1u + T.extra;
+      }
+    }
+  }
+  int* lrow = reinterpret_cast<int*>(lds);                 // [kAxpyTile]
+  float* lcoef = lds + kAxpyTile;                          // [kAxpyTile]
+  float* red = lds + 2 * kAxpyTile;                        // [kAxGroups][kStreamSlice]
+  const int col0 = slice * kStreamSlice + hl * 8;
+  const bool active = col0 < d;
+  float acc[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) acc[v] = 0.f;
+  bool first = true;
+  for (int t0 = r0; t0 < r1; t0 += kAxpyTile) {
+    const int tn = min(kAxpyTile, r1 - t0);
+    __syncthreads();
+    // the readiness poll (thread 0, first tile) goes out before the row ids
+    uint32_t seen = 0xffffffffu;
+    if (first && tid == 0 && ready)
+      seen = __hip_atomic_load(const_cast<uint32_t*>(ready), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = tid; i < tn; i += kThreads) {
+      const int r = t0 + i;
+      int row;
+      if (w2) {
+        const int item = T.LM.idx ? T.LM.idx[r] : r;
+        row = (unsigned)item < (unsigned)T.LM.items ? item : -1;
+      } else {
+        row = head * dh + (r - r0);
+      }
+      lrow[i] = row;
+    }
+    if (first && tid == 0) {
+      int gave_up = 0;
+      if (ready && seen < target) {
+        // not yet: poll until it is (bounded)
+        uint32_t n = 0;
+        while (__hip_atomic_load(const_cast<uint32_t*>(ready), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) < target) {
+          if (n++ >= T.spins) { gave_up = 1; break; }
+          __builtin_amdgcn_s_sleep(8);
+        }
+        if (gave_up) __hip_atomic_fetch_or(T.fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      sm[2] = gave_up;
+    }
+    __syncthreads();
+    if (first && sm[2]) poison = true;
+    first = false;
+    // coefficients (this thread's share of the tile), then the first rows of its row
+    // group; the coefficients are stored once they arrive, the rows stay in flight
+    float cf[(kAxpyTile + kThreads - 1) / kThreads];
+#pragma unroll
+    for (int j = 0; j < (kAxpyTile + kThreads - 1) / kThreads; ++j) {
+      const int i = tid + j * kThreads;
+      float c = 0.f;
+      if (i < tn && lrow[i] >= 0)
+        c = w2 ? activate(ld_dev(&T.a[t0 + i]), T.act) : ld_dev(&T.at.o[t0 + i]);
+      cf[j] = poison ? __builtin_nanf("") : c;
+    }
+    uint4 w[kStreamU];
+    int i0 = grp;
+    auto load_rows = [&](int base) {
+#pragma unroll
+      for (int u = 0; u < kStreamU; ++u) {
+        const int i = base + u * kAxGroups;
+        const int row = (active && i < tn) ? lrow[i] : -1;
+        w[u] = (row >= 0) ? ld_stream(reinterpret_cast<const uint4*>(W + (long long)row * d + col0))
+                          : make_uint4(0u, 0u, 0u, 0u);
+      }
+    };
+    load_rows(i0);
+#pragma unroll
+    for (int j = 0; j < (kAxpyTile + kThreads - 1) / kThreads; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < tn) lcoef[i] = cf[j];
+    }
+    __syncthreads();
+    for (;;) {
+#pragma unroll
+      for (int u = 0; u < kStreamU; ++u) {
+        const int i = i0 + u * kAxGroups;
+        const float c = (i < tn) ? lcoef[i] : 0.f;
+        float f[8];
+        unpack8(w[u], f);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[v] = fmaf(c, f[v], acc[v]);
+      }
+      i0 += kAxGroups * kStreamU;
+      if (i0 >= tn) break;
+      load_rows(i0);
+    }
+  }
+  // the row groups in order 0..7, then this item's partial slice
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < 8; ++v) red[grp * kStreamSlice + hl * 8 + v] = acc[v];
+  __syncthreads();
+  const int col = slice * kStreamSlice + tid;
+  if (col < d) {
+    float part = 0.f;
+#pragma unroll
+    for (int g = 0; g < kAxGroups; ++g) part += red[g * kStreamSlice + tid];
+    st_dev(&T.partial[(size_t)pidx * d + col], part);
+  }
+  const int P = T.ncm + cap_a;
+  if (!arrive_last(&T.ctr[(T.c_stick + slice) * kCtrStride], (uint32_t)P, sm + 1)) return;
+  if (col < d) {
+    // all partials of the column requested at once (up to 48), summed in order
+    constexpr int UB = 48;
+    float t = 0.f;
+    for (int p0 = 0; p0 < P; p0 += UB) {
+      float v[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        v[u] = (p0 + u < P) ? ld_dev(&T.partial[(size_t)(p0 + u) * d + col]) : 0.f;
+#pragma unroll
+      for (int u = 0; u < UB; ++u) t += v[u];
+    }
+    float o = T.y[col] + t;
+    if (poison) o = __builtin_nanf("");
+    T.y_out[col] = o;
+  }
+}
+
+template <int KVT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void stream_kernel(StreamTask T) {
+  extern __shared__ __align__(16) float lds[];
+  int* sm = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + T.lds_union);
+  const int tid = threadIdx.x;
+  // y into LDS, for the dot items (staged again after an attention item, whose scratch
+  // shares the region)
+  auto stage_y = [&]() {
+    const float4* src = reinterpret_cast<const float4*>(T.y);
+    float4* dst = reinterpret_cast<float4*>(lds);
+    for (int i = tid; i < (T.d >> 2); i += kThreads) dst[i] = src[i];
+    __syncthreads();
+  };
+  stage_y();
+  bool y_in_lds = true;
+  bool poison = false;
+  const int n_d = T.n_qi + T.n_mi;
+  // Blocks are dealt to the XCDs round-robin (block b on XCD b % 8); queue q is served by
+  // blocks b with (b / 8) % 8 == q, so every queue draws on every XCD and the queues
+  // advance through the order at the same pace.  Block b's first item swaps the two low
+  // octal digits of b: a bijection of each group of 64 blocks onto its 64 items in which
+  // item % 8 is the block's queue.
+  static_assert(kStreamQueues == 8, "queue mapping assumes 8 queues");
+  const int queue = (blockIdx.x >> 3) & 7;
+  uint32_t* claim = &T.ctr[queue * kCtrStride];
+  int item = (blockIdx.x & ~63) | ((blockIdx.x & 7) << 3) | queue;
+  while ((unsigned)item < (unsigned)T.n_items) {
+    // queue position -> dot item index (W^Q dots, then W1 dots) or attention item
+    const int a0 = T.n_qi + T.n_mfirst;        // first attention position
+    const int dot = item < a0 ? item : (item >= a0 + T.n_a && item < n_d + T.n_a) ? item - T.n_a : -1;
+    if (dot >= 0) {
+      if (!y_in_lds) { stage_y(); y_in_lds = true; }
+      stream_dot(T, dot, lds, poison);
+      const int c = dot < T.n_qi ? T.c_qdone + dot * kStreamDotRows / T.dh
+                                 : T.c_mdone + (dot - T.n_qi) * kStreamDotRows / T.per_m;
+      signal_done(&T.ctr[c * kCtrStride]);
+    } else if (item < a0 + T.n_a) {
+      y_in_lds = false;
+      const int x = item - a0;
+      const int slot = x / T.at.nsplit, split = x - slot * T.at.nsplit;
+      // the head's W^Q rows are dotted (dh / kStreamDotRows dot items)
+      if (wait_ge(&T.ctr[(T.c_qdone + slot) * kCtrStride],
+                  (uint32_t)(T.dh / kStreamDotRows) + T.extra, T.spins, T.fault, sm + 2))
+        poison = true;
+      if (attn_split<KVT, true, 8>(T.at, 0, slot, split, lds, poison)) {
+        __builtin_amdgcn_s_waitcnt(0);      // o is stored
+        __syncthreads();
+        if (tid == 0)
+          __hip_atomic_store(&T.ctr[(T.c_oready + slot) * kCtrStride], 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      stream_sum(T, item - n_d - T.n_a, lds, sm, poison);
+    }
+    // The next item of this block's queue is claimed only now: an item claimed earlier
+    // would wait behind this one, however long it runs, while later items of its queue
+    // went ahead (measured: 85 -> 80 us for the OPT-175B layer).  A claim past the end,
+    // however large, ends the loop.
+    if (tid == 0) {
+      const uint32_t nxt = __hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm[0] = T.grid + (int)min(nxt, (uint32_t)T.n_items) * kStreamQueues + queue;
+    }
+    __syncthreads();
+    item = sm[0];
+    __syncthreads();
+  }
+}
+
+int launch_stream(int kvdt, const StreamTask& t, int grid, int lds_bytes, void* stream) {
+  if (kvdt == W_BF16)
+    hipLaunchKernelGGL((stream_kernel<W_BF16>), dim3(grid), dim3(kThreads), lds_bytes,
+                       static_cast<hipStream_t>(stream), t);
+  else
+    hipLaunchKernelGGL((stream_kernel<W_F32>), dim3(grid), dim3(kThreads), lds_bytes,
+                       static_cast<hipStream_t>(stream), t);
+  return (int)hipGetLastError();
+}
+
+int stream_occupancy(int kvdt, int lds_bytes) {
+  int n = 0;
+  const hipError_t e = kvdt == W_BF16
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_kernel<W_BF16>, kThreads, lds_bytes)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_kernel<W_F32>, kThreads, lds_bytes);
+  return e == hipSuccess ? n : 0;
+}
+
+uint32_t* fault_word() {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(dv_fault)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return static_cast<uint32_t*>(ptrs[dev]);
+}
+
+int fault_take(void* stream, uint32_t* value) {
+  *value = 0u;
+  uint32_t* p = fault_word();
+  if (!p) return (int)hipErrorInvalidValue;
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return (int)e;
+  e = hipMemcpy(value, p, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return (int)e;
+  if (*value) {
+    const uint32_t zero = 0u;
+    e = hipMemcpy(p, &zero, sizeof(uint32_t), hipMemcpyHostToDevice);
+  }
+  return (int)e;
 }
 
 // --------------------------------------------------------------------------- //

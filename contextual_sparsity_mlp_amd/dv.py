@@ -19,13 +19,15 @@ LIB_PATH = os.path.join(_HERE, "_lib", "libdv.so")
 
 DV_F32, DV_BF16, DV_FP8 = 0, 1, 2
 DV_ACT_RELU, DV_ACT_GELU = 0, 1
-DV_OK, DV_EINVAL, DV_EALIGN, DV_EUNSUPPORTED, DV_EWORKSPACE, DV_EHIP = 0, -1, -2, -3, -4, -5
+DV_OK, DV_EINVAL, DV_EALIGN, DV_EUNSUPPORTED, DV_EWORKSPACE, DV_EHIP, DV_ETIMEOUT = \
+    0, -1, -2, -3, -4, -5, -6
 OP_PREDICT, OP_SELECT_TOPK, OP_SPARSE_MLP, OP_SPARSE_MHA, OP_DECODE_LAYER = 1, 2, 3, 4, 5
 
 # Every function declared in include/dv.h.
 EXPORTS = ("dv_last_error", "dv_version", "dv_workspace_bytes", "dv_predict", "dv_select_topk",
            "dv_sparse_mlp", "dv_sparse_mha", "dv_decode_layer", "dv_decode_layer_noalloc",
-           "dv_noalloc_scratch_bytes", "dv_timing_enable", "dv_timing_read")
+           "dv_noalloc_scratch_bytes", "dv_check", "dv_debug_wait_limits", "dv_set_step_path", "dv_timing_enable",
+           "dv_timing_read")
 
 
 class DvError(RuntimeError):
@@ -79,6 +81,8 @@ def lib() -> ctypes.CDLL:
                                               vp, vp, i, vp, vp, vp, vp, vp]
         L.dv_noalloc_scratch_bytes.restype = sz
         L.dv_noalloc_scratch_bytes.argtypes = []
+        L.dv_check.argtypes = [vp]
+        L.dv_debug_wait_limits.argtypes = [ctypes.c_uint, ctypes.c_uint]
         L.dv_timing_enable.argtypes = [i]
         L.dv_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int),
                                      i, ctypes.POINTER(ctypes.c_int)]
@@ -249,6 +253,27 @@ def decode_layer_noalloc(layer: Layer, next_layer, y_in, y_out, idx_m, count_m, 
 
 def noalloc_scratch_bytes() -> int:
     return int(lib().dv_noalloc_scratch_bytes())
+
+
+def check(stream=None):
+    """dv_check: synchronise the stream; raise DvError(DV_ETIMEOUT) if an in-launch wait
+    of an earlier call gave up (DV_EHIP on a runtime error)."""
+    _check(lib().dv_check(_stream(stream)))
+
+
+def debug_wait_limits(spins: int = 0, extra: int = 0):
+    """Test hook: poll limit of in-launch waits (0 = default) and an offset added to their
+    targets (extra > 0 makes every such wait give up)."""
+    _check(lib().dv_debug_wait_limits(int(spins), int(extra)))
+
+
+PATH_AUTO, PATH_TWO_LAUNCH, PATH_ONE_LAUNCH = 0, 1, 2
+
+
+def set_step_path(path: int):
+    """dv_set_step_path: launch plan of the one-token bf16 sparse step (PATH_AUTO takes
+    the faster one)."""
+    _check(lib().dv_set_step_path(int(path)))
 
 
 def timing_enable(on: bool):

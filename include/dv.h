@@ -68,7 +68,8 @@ enum {
   DV_EALIGN = -2,        /* tensor pointer not 16-byte aligned, or d not a multiple of 8 */
   DV_EUNSUPPORTED = -3,  /* valid but unsupported shape (e.g. dh not in {32,64,128,256}) */
   DV_EWORKSPACE = -4,    /* ws NULL or ws_bytes smaller than dv_workspace_bytes() */
-  DV_EHIP = -5           /* the HIP runtime reported an error while enqueuing */
+  DV_EHIP = -5,          /* the HIP runtime reported an error while enqueuing */
+  DV_ETIMEOUT = -6       /* dv_check: a wait inside an earlier launch gave up */
 };
 
 /* Text describing the last non-OK return on the calling thread ("" if none). */
@@ -223,6 +224,33 @@ int dv_decode_layer_noalloc(const dv_layer* L, const dv_layer* next, int batch,
 
 /* Bytes of the scratch array behind dv_decode_layer_noalloc (per device). */
 size_t dv_noalloc_scratch_bytes(void);
+
+/* Reports what an asynchronous call cannot return: synchronises `stream`, then
+ * returns DV_ETIMEOUT if a bounded wait inside a launch of an earlier call on this
+ * device gave up (clearing that record), DV_EHIP if the HIP runtime reports an error,
+ * else DV_OK.  Some launches hand values between their own blocks and wait for them
+ * (they are sized so that all their blocks are resident at once); if that ever fails
+ * to hold (another process on the device's compute units, a partitioned device), the
+ * wait ends after a bounded number of polls and every output that depended on the
+ * missing values is written as NaN, never as a silently wrong number. */
+int dv_check(void* stream);
+
+/* Test hook for that failure path: every later launch polls at most `spins` times per
+ * wait (0 restores the default) and adds `extra` to each wait's target, so that with
+ * extra > 0 every such wait gives up and its kernel still ends normally. */
+int dv_debug_wait_limits(unsigned spins, unsigned extra);
+
+/* Launch plan of dv_decode_layer / dv_decode_layer_noalloc for one token, bf16 rows, no
+ * next-layer predictor and no cache append (the sparse MLP + head-sparse MHA step of
+ * the Deja Vu paper, Section 4, Eq. (1) and (2), alone).  DV_PATH_TWO_LAUNCH: one
+ * launch dots every gathered row, a second one runs attention and both row sums.
+ * DV_PATH_ONE_LAUNCH: one launch whose resident blocks take the row dots, attention
+ * items and row-sum slices from an ordered queue, each item waiting (bounded) on the
+ * items it reads.  DV_PATH_AUTO (the default) takes the plan measured faster on
+ * MI355X.  Both give the same results up to the rounding order of the row sums.
+ * Other calls ignore the setting.  Returns DV_EINVAL for an unknown value. */
+enum { DV_PATH_AUTO = 0, DV_PATH_TWO_LAUNCH = 1, DV_PATH_ONE_LAUNCH = 2 };
+int dv_set_step_path(int path);
 
 /* Phase timing for measurement.  dv_timing_enable(1) makes every later call record
  * a hipEvent pair around each of its kernel launches on the call's stream (events are
