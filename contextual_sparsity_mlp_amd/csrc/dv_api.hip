@@ -335,9 +335,11 @@ LayerWs plan_layer(int batch, int d, int F, int h, int dh, int n_ctx, int r, int
   p.rtick_m = p.hist_a + (size_t)batch * kHistBins * 4;
   p.rtick_a = p.rtick_m + (size_t)batch * 4;
   p.uticket = p.rtick_a + (size_t)batch * 4;
-  p.done = p.uticket + 8;                 // attention blocks done (single-launch path)
-  w.off = align256(p.done + 4);
-  p.zero_words = (int)((p.done + 4 - p.zero) / 4);
+  // per head slot, o stored (single-launch path): one counter per 256-byte line
+  p.done = align256(p.uticket + 8);
+  const size_t done_bytes = (size_t)cap_a * kCtrStride * 4;
+  w.off = align256(p.done + done_bytes);
+  p.zero_words = (int)((p.done + done_bytes - p.zero) / 4);
   p.a = w.take((size_t)batch * cap_m * 4);
   p.q = w.take((size_t)batch * cap_a * dh * 4);
   p.o = w.take((size_t)batch * cap_a * dh * 4);
@@ -1047,10 +1049,12 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
   };
 
   // Without a next layer, one launch when its blocks fit one resident round: every
-  // row-sum block streams its W2 rows, then waits for the attention blocks (which come
-  // first in block order; the last key split of each head combines the splits into
-  // o) and stages o as the coefficients of its W^O rows.  The attention, its combine
-  // included, hides under the W2 stream.  (Combining the splits in each row-sum block
+  // row-sum block streams its W2 rows, then takes its W^O rows one head slot at a
+  // time: it waits until that slot's o is stored (attention blocks come first in block
+  // order; the last key split of each head combines the splits into o and raises the
+  // slot's counter) and stages o as the coefficients.  The attention, its combine
+  // included, hides under the W2 stream, and a head that finishes late holds back only
+  // the blocks whose W^O rows belong to it.  (Combining the splits in each row-sum block
   // instead, as it stages its W^O coefficients, measured 48.3 us against 46.1.)
   // (fp8 rows halve the column slices, so each row-sum block would stream as many rows
   // as at bf16 and the launch becomes bound by each block's chain: measured 60 us for
@@ -1068,7 +1072,24 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
     add_out(f.axpy, std::max(1, resident_blocks() - f.attn.blocks));
     AxpySeg& S = f.axpy.seg[0];
     S.wait_ctr = up(P.done);
-    S.wait_target = (uint32_t)f.attn.blocks + g_wait_extra.load();
+    S.wait_target = (uint32_t)batch + g_wait_extra.load();   // each token's o of the slot
+    // When every row-sum block's two shares fit one tile (bf16 rows), the key splits
+    // only store their softmax pieces and each block combines the pieces of its heads
+    // as it stages its W^O coefficients: a head is ready when its last split is, with
+    // no combining round trips after it.
+    {
+      const int per1 = cdiv(std::max(cap_m, 1), S.nchunks);
+      const int per2 = cdiv(cap_a * dh, S.nchunks);
+      const int ns_max = cdiv(per2 + dh - 1, dh) + 1;       // slots one share can touch
+      const int red_floats = kAxGroups * bt * kAxSliceLanes * S.vec;
+      if (f.attn.nsplit > 1 && wdt == DV_BF16 && S.vec == 8 && per1 + per2 <= kAxpyTileRows &&
+          ns_max <= kThreads && 64 + 2 * bt * ns_max * f.attn.nsplit <= red_floats) {
+        f.attn.part_only = 1;
+        f.axpy.part2 = fp(P.part);
+        f.axpy.nsplit2 = f.attn.nsplit;
+        S.wait_target = (uint32_t)(batch * f.attn.nsplit) + g_wait_extra.load();
+      }
+    }
     f.axpy.spins = g_wait_spins.load();
     f.axpy.fault = fault_word();
     f.axpy.batch = batch;

@@ -27,6 +27,11 @@ constexpr int kMaxChunks = 32;           // row chunks per axpy segment (partial
 constexpr int kAxSliceLanes = 32;        // lanes across the columns of one axpy slice
 constexpr int kAxGroups = 8;             // row groups (half-waves) per axpy block
 constexpr int kAxpyTileRows = 512;       // axpy rows whose ids / coefficients sit in LDS
+constexpr int kAxPackedU = 6;            // axpy bf16 rows in flight per row group
+constexpr int kAxPrefetchU = 6;          //   of which loaded before a wait (one-tile path)
+// In-launch counters sit one per 256-byte line (same-address atomics and polls
+// serialise); the counter of index c is ctr[c * kCtrStride].
+constexpr int kCtrStride = 64;
 constexpr int kMaxSplit = 64;            // key splits per (token, head)
 constexpr int kLdsBudget = 64 * 1024;    // dynamic LDS per block
 constexpr int kTopShift = 20;            // first-level digit: the top 12 bits of a score key
@@ -124,8 +129,10 @@ struct AxpySeg {
   const float* add1;
   int add_ld;
   int accumulate;          // add the previous value of out
-  // Hand-off inside one launch (all blocks resident): before its second-source rows a
-  // block waits until *wait_ctr >= wait_target; coef2 is then read coherently.
+  // Hand-off inside one launch (all blocks resident): before the second-source rows
+  // of slot s a block waits until wait_ctr[s * kCtrStride] >= wait_target; coef2 is
+  // then read coherently.  (The block's share of the second source is taken one slot
+  // at a time, so it waits only on the slots its rows belong to.)
   const uint32_t* wait_ctr;
   uint32_t wait_target;
 };
@@ -138,6 +145,12 @@ struct AxpyTask {
   // folded into the coefficients; kept apart from AxpySeg, whose by-value selection
   // costs scalar registers in every launch mix
   const float* seg_scale[kMaxSeg][2];
+  // Waiting segments (wait_ctr) whose second-source coefficients are attention
+  // outputs left as per-split softmax pieces (AttnTask::part_only): the pieces
+  // [batch][rows2.host_count][nsplit2][rows2.expand + 2], combined by the row-sum
+  // block as it stages the coefficients; nullptr: coef2 holds the coefficients.
+  const float* part2;
+  int nsplit2;
   int nseg;
   int batch;
   int blocks;
@@ -161,7 +174,11 @@ struct AttnTask {
   float* o;                // o[b * o_ld + s*dh + c], stored coherently
   int o_ld;
   int blocks;              // batch * cap * nsplit
-  uint32_t* done_ctr;      // optional: +1 per finished block, after its stores
+  int part_only;           // nsplit > 1: the splits only store their pieces (no combine;
+                           //   every split reports its slot, see done_ctr)
+  uint32_t* done_ctr;      // optional: done_ctr[s * kCtrStride] +1 for each token whose o
+                           //   of slot s is stored, or with part_only for each stored
+                           //   piece (after the stores)
 };
 
 // The sparse step in one launch (one token, bf16 rows, no next layer): every block is
@@ -191,9 +208,6 @@ constexpr int kStreamSlice = 256;                             // columns per sum
 constexpr int kStreamChunks = 16;                             // W2 chunks (target)
 constexpr int kStreamU = 16;                                  // rows in flight per row group
 constexpr int kStreamQueues = 8;                              // claim counters (item i: queue i % 8)
-// Counters sit one per 256-byte line (same-address atomics and polls serialise); the
-// counter of index c is ctr[c * kCtrStride].
-constexpr int kCtrStride = 64;
 
 struct StreamTask {
   const void* W1; const void* W2; const void* Wq; const void* Wo;   // bf16 rows of d

@@ -183,6 +183,32 @@ __device__ __forceinline__ bool wait_ge(const uint32_t* ctr, uint32_t target, ui
   return r;
 }
 
+// wait_ge over the ns (<= kThreads) counters ctr[(s0 + t) * kCtrStride], t < ns, polled
+// together (thread t polls counter t).  `bcast`: a free LDS word, as for wait_ge.
+__device__ __forceinline__ bool wait_slots_ge(const uint32_t* ctr, int s0, int ns, uint32_t target,
+                                              uint32_t spins, uint32_t* fault, int* bcast) {
+  if (threadIdx.x == 0) *bcast = 0;
+  __syncthreads();
+  if ((int)threadIdx.x < ns) {
+    const uint32_t* c = ctr + (size_t)(s0 + (int)threadIdx.x) * kCtrStride;
+    uint32_t n = 0;
+    bool gave_up = false;
+    while (__hip_atomic_load(const_cast<uint32_t*>(c), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (n++ >= spins) { gave_up = true; break; }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    if (gave_up) {
+      __hip_atomic_fetch_or(fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      atomicOr(bcast, 1);
+    }
+  }
+  __syncthreads();
+  const bool r = *bcast != 0;
+  __syncthreads();
+  return r;
+}
+
 // Raises *ctr by one once every thread's stores of this block are complete.
 __device__ __forceinline__ void signal_done(uint32_t* ctr) {
   __builtin_amdgcn_s_waitcnt(0);
@@ -406,7 +432,16 @@ __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float*
       const float4* src = reinterpret_cast<const float4*>(T.y + (size_t)b0 * d);
       float4* dst = reinterpret_cast<float4*>(lds);
       const int n4 = (nb * d) >> 2;
-      for (int i = tid; i < n4; i += kThreads) dst[i] = src[i];
+      constexpr int SU = 12;
+      int i0 = tid;
+      for (; i0 + (SU - 1) * kThreads < n4; i0 += kThreads * SU) {
+        float4 t[SU];
+#pragma unroll
+        for (int u = 0; u < SU; ++u) t[u] = src[i0 + u * kThreads];
+#pragma unroll
+        for (int u = 0; u < SU; ++u) dst[i0 + u * kThreads] = t[u];
+      }
+      for (; i0 < n4; i0 += kThreads) dst[i0] = src[i0];
     }
     __syncthreads();
     for (int g = gw; g < total_cap; g += total_waves) {
@@ -966,12 +1001,43 @@ __device__ __forceinline__ void fp8_rows(const int* lrow, const float* lcoef, in
   }
 }
 
+// The same for bf16 rows (8 columns per lane): packed 16-byte loads, unpacked one row
+// at a time, so a row group keeps twice the rows in flight that unpacked loads would
+// allow in the same registers.
+template <int BT, int U, class At>
+__device__ __forceinline__ void bf16_rows(const int* lrow, const float* lcoef, int i0, int tn,
+                                          At at, float (&acc)[BT][8]) {
+  uint4 wr[U];
+  float c[U][BT];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = i0 + u * kAxGroups;
+    const int row = (i < tn) ? lrow[i] : -1;
+    wr[u] = (row >= 0) ? ld_stream(at(row)) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int b = 0; b < BT; ++b) c[u][b] = (i < tn) ? lcoef[b * kAxpyTile + i] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float f[8];
+    unpack8(wr[u], f);
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+#pragma unroll
+      for (int v = 0; v < 8; ++v) acc[b][v] = fmaf(c[u][b], f[v], acc[b][v]);
+  }
+}
+
 // One block: a slice of kAxSliceLanes*VEC output columns and a chunk of the row list.
 template <int BT, int VEC, int WT, bool WAIT>
 __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, const float* sc2,
                                            int lb, int batch, float* lds,
                                            const AxpyTask* task = nullptr) {
-  constexpr int U = 4;
+  // rows in flight per row group: packed bf16 loads hold more in the registers that 4
+  // unpacked ones take (fp8 rows, 16 columns a lane, keep 4: their 16 sums per token
+  // leave no room for more)
+  constexpr bool PACKED = WT == W_BF16 && VEC == 8;
+  constexpr int U = PACKED ? kAxPackedU : 4;
   constexpr int SW = kAxSliceLanes * VEC;    // columns per slice
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave * 2 + (lane >> 5);
@@ -1042,6 +1108,13 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
                   (long long)(row & ((1 << 30) - 1)) * S.row_stride + col0);
             }, acc);
             continue;
+          } else if constexpr (PACKED) {
+            bf16_rows<BT, U>(lrow, lcoef, i0, tn, [&](int row) {
+              const void* W = (row & (1 << 30)) ? S.W2 : S.W;
+              return reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) +
+                  (long long)(row & ((1 << 30) - 1)) * S.row_stride + col0);
+            }, acc);
+            continue;
           }
           float w[U][VEC];
           float c[U][BT];
@@ -1074,14 +1147,161 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
     // produced in the same launch.
     const int n1 = list_slots(S.rows) * S.rows.expand;
     const int n2 = S.W2 ? list_slots(S.rows2) * S.rows2.expand : 0;
+    // the chunk's contiguous share [r0, r1) of nr rows
+    auto share = [&](int nr, int& r0, int& r1) {
+      const int per = (nr + S.nchunks - 1) / S.nchunks;
+      r0 = min(chunk * per, nr);
+      r1 = min(r0 + per, nr);
+    };
+    int r0, r1, q0, q1;
+    share(n1, r0, r1);
+    share(n2, q0, q1);
+    const int m1 = r1 - r0, m2 = q1 - q0;
+
+    if constexpr (PACKED) {
+      const int ex2 = S.W2 ? S.rows2.expand : 1;
+      if (S.wait_ctr && m1 + m2 <= kAxpyTile &&
+          (m2 == 0 || (q1 - 1) / ex2 - q0 / ex2 < kThreads)) {
+        // Both shares fit one tile: the row ids of both and the first source's
+        // coefficients are staged together; the first step of second-source rows is
+        // loaded before its coefficients are ready, then the block waits for the slots
+        // those rows belong to (all at once) and stages their coefficients.
+        const void* const W1 = S.W;
+        const void* const W2 = S.W2;
+        __syncthreads();
+        for (int i = tid; i < m1 + m2; i += kThreads) {
+          const bool second = i >= m1;
+          const RowList& L = second ? S.rows2 : S.rows;
+          const int rr = second ? q0 + i - m1 : r0 + i;
+          const int ex = L.expand;
+          const int slot = (ex == 1) ? rr : rr / ex;
+          const int e = (ex == 1) ? 0 : rr - slot * ex;
+          const int item = L.idx ? L.idx[slot] : slot;
+          const bool ok = (unsigned)item < (unsigned)L.items;
+          lrow[i] = ok ? item * ex + e : -1;
+          if (!second) {
+#pragma unroll
+            for (int b = 0; b < BT; ++b)
+              lcoef[b * kAxpyTile + i] =
+                  (ok && b < nb) ? activate(S.coef[(size_t)(b0 + b) * S.coef_ld + rr], S.act) : 0.f;
+          }
+        }
+        __syncthreads();
+        auto at1 = [&](int row) {
+          return reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W1) +
+                                                (long long)row * S.row_stride + col0);
+        };
+        auto at2 = [&](int row) {
+          return reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W2) +
+                                                (long long)row * S.row_stride + col0);
+        };
+        if (active)
+          for (int i0 = grp; i0 < m1; i0 += kAxGroups * U) bf16_rows<BT, U>(lrow, lcoef, i0, m1, at1, acc);
+        if (m2 > 0) {
+          constexpr int UP = kAxPrefetchU < U ? kAxPrefetchU : U;   // rows loaded early
+          uint4 wpre[UP];
+#pragma unroll
+          for (int u = 0; u < UP; ++u) {
+            const int i = grp + u * kAxGroups;
+            const int row = (active && i < m2) ? lrow[m1 + i] : -1;
+            wpre[u] = (row >= 0) ? ld_stream(at2(row)) : make_uint4(0u, 0u, 0u, 0u);
+          }
+          const int s0 = q0 / ex2, s1 = (q1 - 1) / ex2;
+          const bool gave_up = wait_slots_ge(S.wait_ctr, s0, s1 - s0 + 1, S.wait_target,
+                                             task->spins, task->fault, reinterpret_cast<int*>(red));
+          if (task->part2) {
+            // o from the key splits' softmax pieces (max m, sum l, p.V): the (m, l) of
+            // every (token, slot, split) of the share go to LDS, each row's p.V pieces
+            // are fetched by its thread; o = sum_s w_s pV_s / sum_s w_s l_s with
+            // w_s = exp(m_s - max m), summed in split order
+            const int ns = task->nsplit2, w2 = ex2 + 2, cap2 = S.rows2.host_count;
+            float* pm = red + 64;                            // [BT][slots][ns]
+            float* pl = pm + BT * (s1 - s0 + 1) * ns;
+            const int npc = nb * (s1 - s0 + 1) * ns;
+            for (int t = tid; t < npc; t += kThreads) {
+              const int sp = t % ns, r = t / ns;
+              const int ls = r % (s1 - s0 + 1), b = r / (s1 - s0 + 1);
+              const float* P = task->part2 +
+                  (((size_t)(b0 + b) * cap2 + s0 + ls) * ns + sp) * w2;
+              pm[t] = ld_dev(&P[0]);
+              pl[t] = ld_dev(&P[1]);
+            }
+            __syncthreads();
+            for (int i = tid; i < m2; i += kThreads) {
+              const int rr = q0 + i, slot = rr / ex2, e = rr - slot * ex2;
+#pragma unroll
+              for (int b = 0; b < BT; ++b) {
+                float c = 0.f;
+                if (lrow[m1 + i] >= 0 && b < nb) {
+                  const float* sm_ = pm + (b * (s1 - s0 + 1) + slot - s0) * ns;
+                  const float* sl_ = pl + (b * (s1 - s0 + 1) + slot - s0) * ns;
+                  const float* P0 = task->part2 + (((size_t)(b0 + b) * cap2 + slot) * ns) * w2;
+                  float MM = -INFINITY;
+                  for (int sp = 0; sp < ns; ++sp) MM = fmaxf(MM, sm_[sp]);
+                  float LL = 0.f, OO = 0.f;
+                  constexpr int UB = 8;
+                  for (int sp0 = 0; sp0 < ns; sp0 += UB) {
+                    float ov[UB];
+#pragma unroll
+                    for (int u = 0; u < UB; ++u)
+                      ov[u] = ld_dev(&P0[(size_t)min(sp0 + u, ns - 1) * w2 + 2 + e]);
+#pragma unroll
+                    for (int u = 0; u < UB; ++u) {
+                      if (sp0 + u < ns) {
+                        const float ms = sm_[sp0 + u];
+                        const float wgt = (ms == -INFINITY) ? 0.f : expf(ms - MM);
+                        LL = fmaf(wgt, sl_[sp0 + u], LL);
+                        OO = fmaf(wgt, ov[u], OO);
+                      }
+                    }
+                  }
+                  c = activate(OO / LL, S.act2);
+                  if (gave_up) c = __builtin_nanf("");
+                }
+                lcoef[b * kAxpyTile + m1 + i] = c;
+              }
+            }
+          } else {
+            for (int i = tid; i < m2; i += kThreads) {
+#pragma unroll
+              for (int b = 0; b < BT; ++b) {
+                float c = 0.f;
+                if (lrow[m1 + i] >= 0 && b < nb) {
+                  c = activate(ld_dev(&S.coef2[(size_t)(b0 + b) * S.coef2_ld + q0 + i]), S.act2);
+                  if (gave_up) c = __builtin_nanf("");
+                }
+                lcoef[b * kAxpyTile + m1 + i] = c;
+              }
+            }
+          }
+          __syncthreads();
+          if (active) {
+#pragma unroll
+            for (int u = 0; u < UP; ++u) {
+              const int i = grp + u * kAxGroups;
+              if (i < m2) {
+                float f[8];
+                unpack8(wpre[u], f);
+#pragma unroll
+                for (int b = 0; b < BT; ++b) {
+                  const float c = lcoef[b * kAxpyTile + m1 + i];
+#pragma unroll
+                  for (int v = 0; v < 8; ++v) acc[b][v] = fmaf(c, f[v], acc[b][v]);
+                }
+              }
+            }
+            for (int i0 = grp + kAxGroups * UP; i0 < m2; i0 += kAxGroups * U)
+              bf16_rows<BT, U>(lrow + m1, lcoef + m1, i0, m2, at2, acc);
+          }
+        }
+        goto reduce;
+      }
+    }
 
     // one source's share of rows: coefficients staged in LDS a tile at a time, then the
     // row slices streamed by the row groups
     auto rows_of = [&](const RowList& L, const void* W, const float* cf, int cld, int rl,
-                       const float* sc, bool coherent, int nr, bool poison) {
-      const int per = (nr + S.nchunks - 1) / S.nchunks;
-      const int r0 = min(chunk * per, nr);
-      const int r1 = min(r0 + per, nr);
+                       const float* sc, bool coherent, int r0, int r1, bool poison) {
       const int ex = L.expand;
       for (int t0 = r0; t0 < r1; t0 += kAxpyTile) {
         const int tn = min(kAxpyTile, r1 - t0);
@@ -1115,6 +1335,12 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
                                                       (long long)row * S.row_stride + col0);
               }, acc);
               continue;
+            } else if constexpr (PACKED) {
+              bf16_rows<BT, U>(lrow, lcoef, i0, tn, [&](int row) {
+                return reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) +
+                                                      (long long)row * S.row_stride + col0);
+              }, acc);
+              continue;
             }
             float w[U][VEC];
             float c[U][BT];
@@ -1141,16 +1367,29 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
         }
       }
     };
-    rows_of(S.rows, S.W, S.coef, S.coef_ld, S.act, sc1, false, n1, false);
-    if (n2 > 0) {
-      // coefficients of the second source written in this launch: read coherently
-      const bool gave_up = S.wait_ctr &&
-          wait_ge(S.wait_ctr, S.wait_target, task->spins, task->fault, reinterpret_cast<int*>(lds));
-      rows_of(S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, sc2, S.wait_ctr != nullptr, n2,
-              gave_up);
+    rows_of(S.rows, S.W, S.coef, S.coef_ld, S.act, sc1, false, r0, r1, false);
+    if (!S.wait_ctr) {
+      rows_of(S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, sc2, false, q0, q1, false);
+    } else {
+      // coefficients of the second source written in this launch, one slot at a time:
+      // wait for that slot's counter, then read its coefficients coherently
+      const int ex = S.rows2.expand;
+      for (int a = q0; a < q1;) {
+        const int slot = a / ex;
+        const int e = min(q1, (slot + 1) * ex);
+        const bool gave_up = wait_ge(S.wait_ctr + (size_t)slot * kCtrStride, S.wait_target,
+                                     task->spins, task->fault, reinterpret_cast<int*>(lds));
+        // (coefficients left as attention pieces are combined only on the one-tile
+        // path, which the launch is planned to take: reaching here with them is a
+        // planning error, and the outputs are NaN)
+        rows_of(S.rows2, S.W2, S.coef2, S.coef2_ld, S.act2, sc2, true, a, e,
+                gave_up || task->part2 != nullptr);
+        a = e;
+      }
     }
   }
 
+reduce:
   // sum the row groups in order 0..7
   __syncthreads();
 #pragma unroll
@@ -1512,8 +1751,10 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
 // One (token b, head slot, key split) of the attention.  COHERENT_Q: q was written by
 // other blocks of the same launch (read with device-coherent loads).  poison: the
 // inputs are not trustworthy (a wait gave up), so the outputs are written as NaN.
-// Returns true in every thread of the block that stored the head's o (the last split
-// to finish, or the only one).
+// Returns true in every thread of the block that completed the slot: the one that
+// stored the head's o (the last split to finish, or the only one), or split 0 of a
+// slot whose head index is out of range; with part_only, every split (each stores
+// only its piece).
 // U: key rows in flight per key group (16 key groups of a 256-thread block at d_h = 128,
 // bf16: U = 8 keeps a 128-key split in flight at once).
 template <int WT, bool COHERENT_Q, int U = 4>
@@ -1548,7 +1789,9 @@ __device__ __forceinline__ bool attn_split(const AttnTask& T, int b, int slot, i
     if (poison) qv[v] = __builtin_nanf("");
   }
   if (slot >= nslots) return false;
-  if ((unsigned)head >= (unsigned)T.h) return false;   // contributes nothing; W^O skips it too
+  // a head index outside [0, h) contributes nothing (W^O skips it too); its split 0
+  // (every split with part_only) reports the slot complete
+  if ((unsigned)head >= (unsigned)T.h) return T.part_only || split == 0;
   const size_t row0 = ((size_t)b * T.h + head) * (size_t)T.cap + k0;   // first key row
   constexpr int ESZ = (WT == W_BF16) ? 2 : 4;
   const char* Kb = static_cast<const char*>(T.K);
@@ -1642,6 +1885,7 @@ __device__ __forceinline__ bool attn_split(const AttnTask& T, int b, int slot, i
   float* P = T.part + (((size_t)b * cap + slot) * T.nsplit + split) * w2;
   if (tid < dh) st_dev(&P[2 + tid], O);
   if (tid == 0) { st_dev(&P[0], M); st_dev(&P[1], L); }
+  if (T.part_only) return true;
   int* flag = reinterpret_cast<int*>(lds + 128 + 2048);
   if (!arrive_last(&T.tickets[(size_t)b * cap + slot], (uint32_t)T.nsplit, flag)) return false;
   // combine the splits: (max, sum) of every split staged in LDS with one parallel load,
@@ -1677,12 +1921,16 @@ __device__ __forceinline__ bool attn_split(const AttnTask& T, int b, int slot, i
   return true;
 }
 
+// One attention block; with a done counter, the block that stores a head's o raises
+// that head slot's counter.
 template <int WT>
 __device__ __forceinline__ void attn_task(const AttnTask& T, int blk, float* lds) {
   const int cap = T.heads.host_count;
   const int split = blk % T.nsplit;
   const int rest = blk / T.nsplit;
-  (void)attn_split<WT, false>(T, rest / cap, rest % cap, split, lds, false);
+  const int slot = rest % cap;
+  const bool stored = attn_split<WT, false>(T, rest / cap, slot, split, lds, false);
+  if (T.done_ctr && stored) signal_done(T.done_ctr + (size_t)slot * kCtrStride);
 }
 
 // --------------------------------------------------------------------------- //
@@ -2319,7 +2567,6 @@ __device__ __forceinline__ void phase_body(const PhaseArgs& a, float* lds) {
     if (blk >= a.b_attn && blk < a.b_attn + a.attn.blocks) {
       if (a.attn.kvdt == W_BF16) attn_task<W_BF16>(a.attn, blk - a.b_attn, lds);
       else attn_task<W_F32>(a.attn, blk - a.b_attn, lds);
-      if (a.attn.done_ctr) signal_done(a.attn.done_ctr);
       return;
     }
   }
