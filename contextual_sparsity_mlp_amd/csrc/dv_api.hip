@@ -1077,16 +1077,24 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
     // only store their softmax pieces and each block combines the pieces of its heads
     // as it stages its W^O coefficients: a head is ready when its last split is, with
     // no combining round trips after it.
+    // The W^O rows also get row chunks of their own (about their share of the row
+    // bytes), after the W2 chunks in block order: the W2 blocks are dispatched first and
+    // stream at once, the W^O blocks start as the heads complete.
     {
-      const int per1 = cdiv(std::max(cap_m, 1), S.nchunks);
-      const int per2 = cdiv(cap_a * dh, S.nchunks);
+      const int nch = S.nchunks;
+      const int c2 = nch >= 2 ? std::max(1, std::min(nch - 1, (int)std::lround(nch * kWoChunkShare)))
+                              : 0;
+      const int per1 = cdiv(std::max(cap_m, 1), nch - c2);
+      const int per2 = cdiv(cap_a * dh, c2 > 0 ? c2 : nch);
+      const int tile = c2 > 0 ? std::max(per1, per2) : per1 + per2;
       const int ns_max = cdiv(per2 + dh - 1, dh) + 1;       // slots one share can touch
       const int red_floats = kAxGroups * bt * kAxSliceLanes * S.vec;
-      if (f.attn.nsplit > 1 && wdt == DV_BF16 && S.vec == 8 && per1 + per2 <= kAxpyTileRows &&
+      if (f.attn.nsplit > 1 && wdt == DV_BF16 && S.vec == 8 && tile <= kAxpyTileRows &&
           ns_max <= kThreads && 64 + 2 * bt * ns_max * f.attn.nsplit <= red_floats) {
         f.attn.part_only = 1;
         f.axpy.part2 = fp(P.part);
         f.axpy.nsplit2 = f.attn.nsplit;
+        f.axpy.c2 = c2;
         S.wait_target = (uint32_t)(batch * f.attn.nsplit) + g_wait_extra.load();
       }
     }

@@ -29,6 +29,7 @@ constexpr int kAxGroups = 8;             // row groups (half-waves) per axpy blo
 constexpr int kAxpyTileRows = 512;       // axpy rows whose ids / coefficients sit in LDS
 constexpr int kAxPackedU = 6;            // axpy bf16 rows in flight per row group
 constexpr int kAxPrefetchU = 6;          //   of which loaded before a wait (one-tile path)
+constexpr double kWoChunkShare = 0.40;   // row-sum chunks given to W^O rows (waiting launch)
 // In-launch counters sit one per 256-byte line (same-address atomics and polls
 // serialise); the counter of index c is ctr[c * kCtrStride].
 constexpr int kCtrStride = 64;
@@ -151,6 +152,10 @@ struct AxpyTask {
   // block as it stages the coefficients; nullptr: coef2 holds the coefficients.
   const float* part2;
   int nsplit2;
+  // Waiting segments: c2 > 0 gives the last c2 row chunks of each column slice the
+  // second source's rows alone (its rows split c2 ways) and the others the first
+  // source's rows alone; 0: every chunk takes its share of both, first source first.
+  int c2;
   int nseg;
   int batch;
   int blocks;

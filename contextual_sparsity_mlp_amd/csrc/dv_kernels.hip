@@ -1153,9 +1153,25 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
       r0 = min(chunk * per, nr);
       r1 = min(r0 + per, nr);
     };
-    int r0, r1, q0, q1;
-    share(n1, r0, r1);
-    share(n2, q0, q1);
+    int r0 = 0, r1 = 0, q0 = 0, q1 = 0;
+    if (task->c2 > 0) {
+      // separate chunks for the two sources; the first source's come first in block
+      // order, so their blocks are dispatched first and the second source's blocks wait
+      // for their coefficients without holding back the first source's stream
+      const int c1 = S.nchunks - task->c2;
+      if (chunk < c1) {
+        const int per = (n1 + c1 - 1) / c1;
+        r0 = min(chunk * per, n1);
+        r1 = min(r0 + per, n1);
+      } else {
+        const int per = (n2 + task->c2 - 1) / task->c2;
+        q0 = min((chunk - c1) * per, n2);
+        q1 = min(q0 + per, n2);
+      }
+    } else {
+      share(n1, r0, r1);
+      share(n2, q0, q1);
+    }
     const int m1 = r1 - r0, m2 = q1 - q0;
 
     if constexpr (PACKED) {
