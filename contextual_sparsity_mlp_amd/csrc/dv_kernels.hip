@@ -1569,12 +1569,15 @@ __device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int ba
       const float* cf = second ? S.coef2 : S.coef;
       const int cld = second ? S.coef2_ld : S.coef_ld;
       const int rl = second ? S.act2 : S.act;
-#pragma unroll 4
-      for (int b = 0; b < TB; ++b) {
-        float c = 0.f;
-        if (ok && b < nb) c = activate(cf[(size_t)(b0 + b) * cld + rr], rl);
-        lcoef[b * kAxmCoefLd + i] = c;
-      }
+      // all TB coefficient loads of the row are issued before any is used (one round
+      // trip per tile rather than one per few tokens)
+      float cv[TB];
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+        cv[b] = (ok && b < nb) ? cf[(size_t)(b0 + min(b, nb - 1)) * cld + rr] : 0.f;
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+        lcoef[b * kAxmCoefLd + i] = (ok && b < nb) ? activate(cv[b], rl) : 0.f;
     }
     __syncthreads();
     // 16 bytes of each of the rows q + 8 g + i, i < 8, at columns col0 + 8 m.  Rows
@@ -1602,20 +1605,18 @@ __device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int ba
                                                            q + 8 * g);
         split8(cp[0], cp[1], chi[nt], cmid[nt]);
       }
-      // column vectors: element i of vector j = row 8 g + i, column col0 + 8 m + j
-      uint32_t wu[32];   // w[i] word x at wu[4 i + x], zero for rows outside the list
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool ok = (valid >> i) & 1u;
-        wu[4 * i + 0] = ok ? w[i].x : 0u; wu[4 * i + 1] = ok ? w[i].y : 0u;
-        wu[4 * i + 2] = ok ? w[i].z : 0u; wu[4 * i + 3] = ok ? w[i].w : 0u;
-      }
+      // column vectors: element i of vector j = row 8 g + i, column col0 + 8 m + j;
+      // word x of row i, zero for rows outside the list, is taken where it is used
+      auto word = [&](int i, int x) -> uint32_t {
+        const uint32_t v = x == 0 ? w[i].x : x == 1 ? w[i].y : x == 2 ? w[i].z : w[i].w;
+        return ((valid >> i) & 1u) ? v : 0u;
+      };
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint32_t a[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t lo = wu[4 * (2 * p) + (j >> 1)], hi = wu[4 * (2 * p + 1) + (j >> 1)];
+          const uint32_t lo = word(2 * p, j >> 1), hi = word(2 * p + 1, j >> 1);
           a[p] = (j & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
         }
         const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(a[0], a[1], a[2], a[3]));
