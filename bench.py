@@ -78,11 +78,16 @@ def blas_threads() -> int:
 
 # Kernel symbols behind each launch of the sparse step at batch 1 (bf16 rows), by the
 # number of launches the library issued.
-SPARSE_KERNELS = {
-    1: ["stream_kernel<1>"],
-    2: ["rowdot_kernel<1, 1>", "phase_kernel<38, 1>"],
-    3: ["rowdot_kernel", "phase_kernel<2, 1>", "phase_kernel<4, ...>"],
-}
+def sparse_kernels(n_launches, args):
+    """Kernel symbols behind each launch of the sparse step at batch 1, by the number
+    of launches the library issued (None where they are not pinned down here)."""
+    if args.wdt == "fp8":
+        rd = "rowdot_kv_kernel<385, 1>" if args.kv_append else "rowdot_kernel<129, 1>"
+        return {2: [rd, "phase_kernel_bt<166, 1>"],
+                3: [rd, "phase_kernel<2, 1>", "phase_kernel<132, 1>"]}.get(n_launches)
+    rd = "rowdot_kv_kernel<257, 1>" if args.kv_append else "rowdot_kernel<1, 1>"
+    return {1: ["stream_kernel<1>"], 2: [rd, "phase_kernel<38, 1>"],
+            3: [rd, "phase_kernel<2, 1>", "phase_kernel<4, 1>"]}.get(n_launches)
 
 
 class Workload:
@@ -229,8 +234,8 @@ def measure(W, steps, warmup):
               "bytes": sel, "GBps": gbps(sel, ms * 1e3),
               "frac_of_peak": round(sel / (ms * 1e-3) / 1e9 / PEAK_GBPS, 4),
               "launches": [dict(launch=i, name=names.get(len(ph), [f"launch {i}"] * 8)[i],
-                                kernel=SPARSE_KERNELS.get(len(ph), ["?"] * 8)[i]
-                                if W.B == 1 and W.args.wdt == "bf16" else None,
+                                kernel=(sparse_kernels(len(ph), W.args) or [None] * 8)[i]
+                                if W.B == 1 else None,
                                 avg_us=round(u, 2), bytes=b, GBps=gbps(b, u))
                            for i, (u, b) in enumerate(zip(ph, ph_b))]}
 
@@ -369,7 +374,10 @@ def main():
     roofline = dict(bound="hbm", kernel=f"{dom['kernel']} (launch {dom['launch']}: {dom['name']})",
                     achieved=dom["GBps"], peak=PEAK_GBPS, unit="GB/s",
                     frac=round(dom["GBps"] / PEAK_GBPS, 4),
-                    traffic=(traffic["per_launch"].get(key) if traffic else None),
+                    # (the counters were taken on the bf16 batch-1 step without the
+                    # KV append; GeLU runs the same launches over the same bytes)
+                    traffic=(traffic["per_launch"].get(key) if traffic and W.B == 1 and
+                             args.wdt == "bf16" and not args.kv_append else None),
                     avg_launch_us=dom["avg_us"], algorithmic_bytes=dom["bytes"])
 
     cpu = None

@@ -1056,12 +1056,11 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
   // included, hides under the W2 stream, and a head that finishes late holds back only
   // the blocks whose W^O rows belong to it.  (Combining the splits in each row-sum block
   // instead, as it stages its W^O coefficients, measured 48.3 us against 46.1.)
-  // (fp8 rows halve the column slices, so each row-sum block would stream as many rows
-  // as at bf16 and the launch becomes bound by each block's chain: measured 60 us for
-  // the single launch against 22 + 25 us for the attention and a row-sum launch)
+  // (fp8 rows take it too: with the W^O rows on chunks of their own, no block's chain
+  // holds both sources)
   // (Row sums on the matrix cores do not wait inside a launch: batches of tokens
   // over bf16 rows take the two launches below.)
-  if (!nx && max_count_a > 0 && !fp8 && ax_geo(batch, d, d, wdt, 1).mfma_nt == 0) {
+  if (!nx && max_count_a > 0 && ax_geo(batch, d, d, wdt, 1).mfma_nt == 0) {
     PhaseArgs f = zero_args();
     setup_attn(f.attn, fp(P.q), cap_a * dh, L->K, L->V, L->kvdt, batch, h, n_att, kv_cap, dh, LH,
                L->scale,
@@ -1069,7 +1068,10 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
     f.attn.done_ctr = up(P.done);
     f.b_attn = 0;
     f.b_axpy = f.attn.blocks;
-    add_out(f.axpy, std::max(1, resident_blocks() - f.attn.blocks));
+    const int wflags = T_ATTN | T_AXPY | T_WAIT | (fp8 ? T_FP8 : 0);
+    const int lds = std::max(axpy_lds(bt, fp8 ? 16 : 8), attn_lds());
+    const int fit = std::min(resident_blocks(), phase_occupancy(wflags, bt, lds) * device_cus());
+    add_out(f.axpy, std::max(1, fit - f.attn.blocks));
     AxpySeg& S = f.axpy.seg[0];
     S.wait_ctr = up(P.done);
     S.wait_target = (uint32_t)batch + g_wait_extra.load();   // each token's o of the slot
@@ -1089,12 +1091,12 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
       const int tile = c2 > 0 ? std::max(per1, per2) : per1 + per2;
       const int ns_max = cdiv(per2 + dh - 1, dh) + 1;       // slots one share can touch
       const int red_floats = kAxGroups * bt * kAxSliceLanes * S.vec;
+      f.axpy.c2 = c2;
       if (f.attn.nsplit > 1 && wdt == DV_BF16 && S.vec == 8 && tile <= kAxpyTileRows &&
           ns_max <= kThreads && 64 + 2 * bt * ns_max * f.attn.nsplit <= red_floats) {
         f.attn.part_only = 1;
         f.axpy.part2 = fp(P.part);
         f.axpy.nsplit2 = f.attn.nsplit;
-        f.axpy.c2 = c2;
         S.wait_target = (uint32_t)(batch * f.attn.nsplit) + g_wait_extra.load();
       }
     }
@@ -1102,10 +1104,7 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
     f.axpy.fault = fault_word();
     f.axpy.batch = batch;
     const int grid = f.attn.blocks + f.axpy.blocks;
-    const int lds = std::max(axpy_lds(bt), attn_lds());
-    const int fit = std::min(resident_blocks(),
-                             phase_occupancy(T_ATTN | T_AXPY | T_WAIT, bt, lds) * device_cus());
-    if (grid <= fit && f.axpy.fault) return launch(T_ATTN | T_AXPY | T_WAIT, bt, f, grid, lds, stream, fn);
+    if (grid <= fit && f.axpy.fault) return launch(wflags, bt, f, grid, lds, stream, fn);
   }
 
   // Otherwise two launches: the attention (its last split of each head combines the

@@ -29,6 +29,7 @@ constexpr int kAxGroups = 8;             // row groups (half-waves) per axpy blo
 constexpr int kAxpyTileRows = 512;       // axpy rows whose ids / coefficients sit in LDS
 constexpr int kAxPackedU = 6;            // axpy bf16 rows in flight per row group
 constexpr int kAxPrefetchU = 6;          //   of which loaded before a wait (one-tile path)
+constexpr int kAxFp8WaitU = 8;           //   fp8 rows in the waiting launch
 constexpr double kWoChunkShare = 0.40;   // row-sum chunks given to W^O rows (waiting launch)
 // In-launch counters sit one per 256-byte line (same-address atomics and polls
 // serialise); the counter of index c is ctr[c * kCtrStride].

@@ -1034,10 +1034,10 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
                                            int lb, int batch, float* lds,
                                            const AxpyTask* task = nullptr) {
   // rows in flight per row group: packed bf16 loads hold more in the registers that 4
-  // unpacked ones take (fp8 rows, 16 columns a lane, keep 4: their 16 sums per token
-  // leave no room for more)
+  // unpacked ones take; fp8 rows (16 columns a lane, 16 sums per token) keep 4 at the
+  // 64-register cap and take more in the waiting launch, which runs without it
   constexpr bool PACKED = WT == W_BF16 && VEC == 8;
-  constexpr int U = PACKED ? kAxPackedU : 4;
+  constexpr int U = PACKED ? kAxPackedU : (WT == W_FP8 && WAIT) ? kAxFp8WaitU : 4;
   constexpr int SW = kAxSliceLanes * VEC;    // columns per slice
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave * 2 + (lane >> 5);
@@ -1746,11 +1746,11 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
     if (S.vec == 8) axpy_block<BT, 8, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds, &T);
     else axpy_block<BT, 1, W_BF16, WAIT>(S, nullptr, nullptr, lb, T.batch, lds, &T);
   } else if (FP8 && S.wdt == W_FP8) {
-    // d % 16 == 0 (host check); fp8 layers never take the waiting single launch
-    if constexpr (FP8 && !WAIT) {
+    // d % 16 == 0 (host check)
+    if constexpr (FP8) {
       const float* const* sc = s == 0 ? T.seg_scale[0] : s == 1 ? T.seg_scale[1]
                              : s == 2 ? T.seg_scale[2] : T.seg_scale[3];
-      axpy_block<BT, 16, W_FP8, false>(S, sc[0], sc[1], lb, T.batch, lds);
+      axpy_block<BT, 16, W_FP8, WAIT>(S, sc[0], sc[1], lb, T.batch, lds, &T);
     }
   } else {
     if (S.vec == 4) axpy_block<BT, 4, W_F32, WAIT>(S, nullptr, nullptr, lb, T.batch, lds, &T);
@@ -2596,6 +2596,9 @@ __device__ __forceinline__ void phase_body(const PhaseArgs& a, float* lds) {
   }
 }
 
+// (The waiting launch over fp8 rows, whose 16-column lanes need more registers, takes
+// the kernel without the 8-wave target even for one token: its grid is smaller, 24
+// column slices against 48.)
 // Residency is also bounded by scalar registers: measured on MI355X with 256-thread
 // blocks of <= 64 VGPRs, a kernel of at most 80 SGPRs keeps 8 blocks per CU resident,
 // one of 84 only 7.  The launch descriptor would otherwise take about 85, so every
@@ -2656,7 +2659,7 @@ static int launch_t(const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
   else if constexpr ((FLAGS & ~(T_FP8 | T_KV)) == T_ROWDOT)
     hipLaunchKernelGGL((rowdot_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
                        static_cast<hipStream_t>(stream), a);
-  else if constexpr (BT == 1)
+  else if constexpr (BT == 1 && (FLAGS & (T_WAIT | T_FP8)) != (T_WAIT | T_FP8))
     hipLaunchKernelGGL((phase_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
                        static_cast<hipStream_t>(stream), a);
   else
@@ -2699,6 +2702,8 @@ int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes,
     case T_AXPY: return launch_bt<T_AXPY>(bt, a, grid, lds_bytes, stream);
     case T_ATTN | T_AXPY: return launch_bt<T_ATTN | T_AXPY>(bt, a, grid, lds_bytes, stream);
     case T_ATTN | T_AXPY | T_WAIT: return launch_bt<T_ATTN | T_AXPY | T_WAIT>(bt, a, grid, lds_bytes, stream);
+    case T_ATTN | T_AXPY | T_WAIT | T_FP8:
+      return launch_bt<T_ATTN | T_AXPY | T_WAIT | T_FP8>(bt, a, grid, lds_bytes, stream);
     case T_AXPY | T_CLASSIFY: return launch_bt<T_AXPY | T_CLASSIFY>(bt, a, grid, lds_bytes, stream);
     case T_ROWDOT | T_FP8: return launch_bt<T_ROWDOT | T_FP8>(bt, a, grid, lds_bytes, stream);
     case T_ROWDOT | T_KV: return launch_bt<T_ROWDOT | T_KV>(bt, a, grid, lds_bytes, stream);
@@ -2745,7 +2750,7 @@ static int occupancy_t(int lds_bytes) {
                                                      lds_bytes);
   else if constexpr ((FLAGS & ~(T_FP8 | T_KV)) == T_ROWDOT)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rowdot_kernel<FLAGS, BT>, kThreads, lds_bytes);
-  else if constexpr (BT == 1)
+  else if constexpr (BT == 1 && (FLAGS & (T_WAIT | T_FP8)) != (T_WAIT | T_FP8))
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, phase_kernel<FLAGS, BT>, kThreads, lds_bytes);
   else
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, phase_kernel_bt<FLAGS, BT>, kThreads, lds_bytes);
@@ -2764,6 +2769,8 @@ static int occupancy_bt(int bt, int lds_bytes) {
 int phase_occupancy(int flags, int bt, int lds_bytes) {
   switch (flags) {
     case T_ATTN | T_AXPY | T_WAIT: return occupancy_bt<T_ATTN | T_AXPY | T_WAIT>(bt, lds_bytes);
+    case T_ATTN | T_AXPY | T_WAIT | T_FP8:
+      return occupancy_bt<T_ATTN | T_AXPY | T_WAIT | T_FP8>(bt, lds_bytes);
     default: return 0;
   }
 }

@@ -1,17 +1,19 @@
 """Summaries of rocprofv3 output for the decode-layer benchmark.
 
-    python -m contextual_sparsity_mlp_amd.profsum stats <kernel_stats.csv> <kernel_trace.csv> <out.md> "<command>"
+    python -m contextual_sparsity_mlp_amd.profsum stats <kernel_stats.csv> <kernel_trace.csv> <out.md> "<command>" ["<title>"]
     python -m contextual_sparsity_mlp_amd.profsum traffic <fetch counter_collection.csv>
         <write counter_collection.csv> <out.json> "<command>"
 
 `stats` turns a --kernel-trace --stats kernel summary into a short table, and adds
-the per-launch durations of the decode kernels from the trace (the phase kernel is
-one template per launch mix, so its launches are told apart by grid size).
-`traffic` reads two --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) of the
-benchmark with --copy-calibrate: the plain 1 GiB copy calibrates each counter
-(bytes per counted KiB), and the decode launches (phase kernels) are averaged per
-launch slot of the look-ahead step: 0 row dots, 1 attention + row sums, 2 output
-row sums + top-k.
+the per-launch durations of the decode kernels from the trace, each launch named by
+its kernel (the phase kernel is one template per launch mix; launches of one template
+are told apart by grid size).
+`traffic` reads two --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) of
+`bench.py --sparse-only --copy-calibrate` (batch 1, bf16): the plain 1 GiB copy
+calibrates each counter (bytes per counted KiB), and the two launches of the sparse
+MLP + MHA step are averaged: "2:0" the row dots (rowdot_kernel<1, 1>), "2:1" the
+attention + waiting row sums (phase_kernel<38, 1>), keyed as bench.py's roofline
+looks them up (launches of the step : launch).
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 1 << 30
-# template flags of the phase kernel for each launch slot of the look-ahead step
+# template flags of the decode kernels for each launch slot of the look-ahead step
 SLOT_FLAGS = {0: "1", 1: "6", 2: "20"}
 
 
@@ -39,7 +41,13 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stats(src: str, trace: str, out: str, command: str):
+def kernel_label(name: str) -> str:
+    """Short kernel name with its template arguments (dv::rowdot_kernel<1, 1>)."""
+    m = re.search(r"dv::(\w+)(<[^>]*>)?", name)
+    return (m.group(1) + (m.group(2) or "")) if m else re.sub(r"\(.*", "", name)[:60]
+
+
+def stats(src: str, trace: str, out: str, command: str, title: str = ""):
     rows = list(csv.DictReader(open(src)))
     # fp8 weight rows: the row dots and the output row sum carry the fp8 flag (128),
     # and without a next layer the attention runs alone before the row sum
@@ -47,7 +55,8 @@ def stats(src: str, trace: str, out: str, command: str):
     weights = "fp8 (E4M3) weight rows" if fp8 else "bf16 weights"
     mb = re.search(r"--batch (\d+)", command)
     batch = int(mb.group(1)) if mb else 1
-    lines = [f"# rocprofv3 kernel summary: OPT-175B-shaped decode layer, batch {batch}, {weights}", "",
+    head = title or f"OPT-175B-shaped decode layer, batch {batch}, {weights}"
+    lines = [f"# rocprofv3 kernel summary: {head}", "",
              f"Command: `{command}`", "",
              "## Per kernel (rocprofv3 --stats)", "",
              "| kernel | calls | avg us | min us | max us | % time |",
@@ -61,6 +70,7 @@ def stats(src: str, trace: str, out: str, command: str):
                      f"{float(r['Percentage']):.1f} |")
     groups = {}
     seq = []
+    names_by_flags = {}
     for r in sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"])):
         m = re.search(r"(?:phase|rowdot|rowdot_kv)_kernel(?:_bt)?<(\d+), (\d+)>", r["Kernel_Name"])
         mm = re.search(r"rowdot_mfma(_lds)?_kernel(?:<(\d+)>)?", r["Kernel_Name"])
@@ -71,6 +81,7 @@ def stats(src: str, trace: str, out: str, command: str):
         # matrix-core row dots are listed as flags "mfma", batch tile = token tiles of 16
         fl, bt = (m.group(1), m.group(2)) if m else ("mfma", "lds" if mm.group(1) else mm.group(2))
         groups.setdefault((fl, bt, blocks), []).append(dur)
+        names_by_flags.setdefault(fl, kernel_label(r["Kernel_Name"]))
         seq.append((fl, dur))
     # launches of the look-ahead step: a row-dot launch directly followed by the
     # attention + row-sum launch and the row-sum + top-k launch (with a batch of at
@@ -80,6 +91,8 @@ def stats(src: str, trace: str, out: str, command: str):
     slot_flags = dict(SLOT_FLAGS)
     if fp8:
         slot_flags = {0: "129", 1: "6", 2: "148"}
+    elif batch > 16:
+        slot_flags = {0: "mfma", 1: "2", 2: "1540", 3: "8", 4: "1556"}
     elif batch >= 3:
         slot_flags = {0: "mfma", 1: "2", 2: "516", 3: "8", 4: "532"}
     order = [slot_flags[k] for k in sorted(slot_flags)]
@@ -93,15 +106,15 @@ def stats(src: str, trace: str, out: str, command: str):
               "32 row sums that wait for in-launch attention, 64 zero fill, 128 fp8 rows, "
               "256 KV stores, 512 matrix-core row sums (sums of these for a mixed launch); "
               "mfma: the matrix-core row dots (batch tile lds: y staged in LDS)", "",
-              "| phase_kernel<flags, batch tile> | blocks | launches | avg us | median us | min us |",
-              "|---|---|---|---|---|---|"]
+              "| kernel | flags, batch tile | blocks | launches | avg us | median us | min us |",
+              "|---|---|---|---|---|---|---|"]
     for (fl, bt, blocks), v in sorted(groups.items(), key=lambda kv: -len(kv[1])):
-        lines.append(f"| <{fl}, {bt}> | {blocks} | {len(v)} | {statistics.mean(v):.2f} | "
-                     f"{statistics.median(v):.2f} | {min(v):.2f} |")
+        lines.append(f"| `{names_by_flags.get(fl, '?')}` | <{fl}, {bt}> | {blocks} | {len(v)} | "
+                     f"{statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} |")
     # launches of the sparse MLP + MHA step: row dots, then the single launch of
     # attention and the waiting row sum
-    sp_order = (["129", "2", "132"] if fp8 else ["mfma", "2", "516"] if batch >= 3
-                else ["1", "38"])
+    sp_order = (["129", "2", "132"] if fp8 else ["mfma", "2", "1540"] if batch > 16
+                else ["mfma", "2", "516"] if batch >= 3 else ["1", "38"])
     sp_durs = {k: [] for k in range(len(sp_order))}
     for i in range(len(seq) - len(sp_order) + 1):
         # (not the first launches of a look-ahead step, whose order starts alike)
@@ -118,22 +131,22 @@ def stats(src: str, trace: str, out: str, command: str):
                  {0: "row dots (W1, W^Q, A rows)", 1: "attention + predictor B rows",
                   2: "row sum W2 + W^O rows, combine, top-k"})
         lines += ["", "## Look-ahead decode step, per launch (from the kernel trace)", "",
-                  "| launch | phase_kernel<flags> | launches | avg us | median us | min us |",
+                  "| launch | kernel | launches | avg us | median us | min us |",
                   "|---|---|---|---|---|---|"]
         for k in sorted(slot_durs):
             v = slot_durs[k]
-            lines.append(f"| {k}: {names[k]} | <{slot_flags[k]}> | {len(v)} | "
+            lines.append(f"| {k}: {names[k]} | `{names_by_flags.get(slot_flags[k], '?')}` | {len(v)} | "
                          f"{statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} |")
     if sp_durs[0]:
         names = ({0: "row dots (W1, W^Q rows)", 1: "attention, split pieces combined per head",
                   2: "row sum W2 + W^O rows"} if len(sp_order) == 3 else
                  {0: "row dots (W1, W^Q rows)", 1: "attention + row sum W2 then W^O rows"})
         lines += ["", "## Sparse MLP + MHA step, per launch (from the kernel trace)", "",
-                  "| launch | phase_kernel<flags> | launches | avg us | median us | min us |",
+                  "| launch | kernel | launches | avg us | median us | min us |",
                   "|---|---|---|---|---|---|"]
         for k in sorted(sp_durs):
             v = sp_durs[k]
-            lines.append(f"| {k}: {names[k]} | <{sp_order[k]}> | {len(v)} | "
+            lines.append(f"| {k}: {names[k]} | `{names_by_flags.get(sp_order[k], '?')}` | {len(v)} | "
                          f"{statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} |")
     open(out, "w").write("\n".join(lines) + "\n")
 
@@ -149,32 +162,36 @@ def _counter_rows(path, counter):
     return out
 
 
-def _per_slot(rows):
+# launches of the sparse MLP + MHA step at batch 1 (bf16), keyed as bench.py reads them
+SPARSE_LAUNCHES = {"2:0": r"rowdot_kernel<1, 1>", "2:1": r"phase_kernel<38, 1>"}
+
+
+def _per_launch(rows):
     copy = [v for n, g, v in rows if "copyBuffer" in n]
-    slots = {}
-    for slot, flags in SLOT_FLAGS.items():
-        vals = [(g, v) for n, g, v in rows if re.search(rf"(?:phase|rowdot|rowdot_kv)_kernel<{flags}, 1>", n)]
+    per = {}
+    for key, pat in SPARSE_LAUNCHES.items():
+        vals = [(g, v) for n, g, v in rows if pat in n]
         if not vals:
             continue
         # the decode launches are the most frequent grid size of that kernel
         grids = [g for g, _ in vals]
         common = max(set(grids), key=grids.count)
-        slots[slot] = statistics.median([v for g, v in vals if g == common])
-    return (max(copy) if copy else None), slots
+        per[key] = statistics.median([v for g, v in vals if g == common])
+    return (max(copy) if copy else None), per
 
 
 def traffic(fetch_csv: str, write_csv: str, out: str, command: str):
-    f_copy, f_slots = _per_slot(_counter_rows(fetch_csv, "FETCH_SIZE"))
-    w_copy, w_slots = _per_slot(_counter_rows(write_csv, "WRITE_SIZE"))
+    f_copy, f_per = _per_launch(_counter_rows(fetch_csv, "FETCH_SIZE"))
+    w_copy, w_per = _per_launch(_counter_rows(write_csv, "WRITE_SIZE"))
     f_scale = COPY_BYTES / f_copy if f_copy else None
     w_scale = COPY_BYTES / w_copy if w_copy else None
     per = {}
-    for slot in sorted(set(f_slots) | set(w_slots)):
-        fb = f_slots.get(slot, 0.0) * (f_scale or 0)
-        wb = w_slots.get(slot, 0.0) * (w_scale or 0)
-        per[str(slot)] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
-                          "bytes": round(fb + wb)}
-    res = {"workload": "OPT-175B-shaped decode layer, batch 1, look-ahead predictor",
+    for key in sorted(set(f_per) | set(w_per)):
+        fb = f_per.get(key, 0.0) * (f_scale or 0)
+        wb = w_per.get(key, 0.0) * (w_scale or 0)
+        per[key] = {"kernel": SPARSE_LAUNCHES[key], "fetch_bytes": round(fb),
+                    "write_bytes": round(wb), "bytes": round(fb + wb)}
+    res = {"workload": "OPT-175B-shaped sparse MLP + MHA step, batch 1, bf16 rows",
            "command": command, "source_hash": source_hash(),
            "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": f_copy, "write_kib": w_copy,
                                 "fetch_bytes_per_count": f_scale,
@@ -186,7 +203,7 @@ def traffic(fetch_csv: str, write_csv: str, out: str, command: str):
 
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
-        stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+        stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], *(sys.argv[6:7]))
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
     else:
