@@ -492,6 +492,59 @@ def test_decode_layer_lookahead_uses_input():
     assert not np.array_equal(s_in, s_out)
 
 
+# Shapes that route the single attention + waiting row-sum launch (a layer without a
+# next layer) through its per-slot path: with one 256-column slice, the W2 share of a
+# chunk is more than one tile (12000 rows over 19 chunks), so the blocks take their
+# W^O rows one head slot at a time, each slot waited for by one thread, and the key
+# splits combine o themselves.
+WAIT_SHAPES = {
+    "slot-path": LayerConfig("slot-path", 31, d=256, F=32768, h=4, dh=64, batch=1, n_ctx=300,
+                             k_m=12000, k_a=3, r=16),
+    "slot-path-b2": LayerConfig("slot-path-b2", 32, d=256, F=32768, h=4, dh=64, batch=2,
+                                n_ctx=300, k_m=12000, k_a=3, r=16, union=True),
+}
+
+
+@pytest.mark.parametrize("name", list(WAIT_SHAPES))
+def test_decode_layer_waiting_slot_path(name):
+    cfg = WAIT_SHAPES[name]
+    banner(f"decode_layer waiting launch, per-slot path {name}")
+    r = _layer_case(cfg, with_next=False)
+    assert_close(r["y_out"], r["y_ref"], TIGHT_ATTN, f"per-slot path {name}")
+
+
+@pytest.mark.parametrize("name", ["bf16-ragged", "c4"])
+def test_decode_layer_waiting_bad_heads(name):
+    """The single waiting launch with a head list holding an index outside [0, h) and a
+    count below capacity: the bad head contributes nothing (its W^O rows are skipped,
+    its slot still reported complete, so no wait gives up), slots past the count are
+    never waited for, and the output equals the oracle's over the valid heads."""
+    cfg = cfg_of(name)
+    B = 1
+    banner(f"decode_layer waiting launch, bad head index {name}")
+    L = synth.make_layer(cfg, DEV, batch=B)
+    y = synth.make_y(cfg, DEV, batch=B)
+    S_M = synth.random_index_set(cfg.F, cfg.k_m, seed=cfg.cfg_id + 71).numpy()
+    S_A = synth.random_index_set(cfg.h, min(cfg.k_a, cfg.h - 1), seed=cfg.cfg_id + 72).numpy()
+    listed = np.concatenate([S_A[:1], [cfg.h + 3], S_A[1:]]).astype(np.int32)
+    cap_a = len(listed) + 2                                  # count below capacity
+    idx_m, cnt_m = put_set(S_M, len(S_M))
+    idx_a = torch.full((cap_a,), 7, dtype=torch.int32, device=DEV)
+    idx_a[:len(listed)] = torch.as_tensor(listed, device=DEV)
+    cnt_a = torch.tensor([len(listed)], dtype=torch.int32, device=DEV)
+    ws = dv.workspace(dv.OP_DECODE_LAYER, batch=B, d=cfg.d, F=cfg.F, h=cfg.h, dh=cfg.dh,
+                      n_ctx=cfg.n_ctx, r=cfg.r, max_count_m=len(S_M), max_count_a=cap_a)
+    layer = dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, scale=cfg.scale)
+    y_out = torch.full_like(y, np.nan)
+    dv.decode_layer(layer, None, y, y_out, idx_m, cnt_m, len(S_M), idx_a, cnt_a, cap_a,
+                    None, None, None, None, ws)
+    dv.check()
+    ref, _ = O.decode_layer(host(y), dict(W1t=host(L.W1t), W2t=host(L.W2t), Wq=host(L.Wq),
+                                          Wo=host(L.Wo), K=host(L.K), V=host(L.V)),
+                            S_M, np.sort(S_A), None, cfg.scale)
+    assert_close(y_out.cpu().numpy(), ref, TIGHT_ATTN, f"bad head {name}")
+
+
 @pytest.mark.parametrize("batch", [1, 2, 4, 8, 16])
 def test_decode_layer_c4(batch):
     """The OPT-175B-shaped layer at full size, at every batch of the workload (batch 1
