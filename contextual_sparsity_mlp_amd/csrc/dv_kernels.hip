@@ -2151,7 +2151,8 @@ __device__ __forceinline__ void resolve_row(const TopkProblem& P, int b, uint32_
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (!P.unite) {
+  // (one row: its set is the union, compacted here without publishing the words)
+  if (!P.unite || P.batch == 1) {
     const uint32_t n = words_in_lds
         ? compact_bits<false>(words, 1, nwords, P.idx + (size_t)b * P.k, scratch)
         : compact_bits<true>(words, 1, nwords, P.idx + (size_t)b * P.k, scratch);
