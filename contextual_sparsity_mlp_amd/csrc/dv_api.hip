@@ -611,7 +611,7 @@ extern "C" {
 
 const char* dv_last_error(void) { return g_err.c_str(); }
 
-int dv_version(void) { return 103; }
+int dv_version(void) { return 104; }
 
 static size_t ws_bytes_for(int op, const dv_shape* s, dv_dtype wdt) {
   const int B = s->batch;

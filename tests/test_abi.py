@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(dv.EXPORTS), f"header {names} vs binding {dv.EXPORTS}"
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.dv_version() == 103
+    assert lib.dv_version() == 104
 
 
 def test_library_has_gfx950_code():
@@ -219,3 +219,21 @@ def test_decode_layer_noalloc_rejects_oversized():
 def test_timing_read_empty():
     ms, cnt = dv.timing_read(4)
     assert ms == [] and cnt == []
+
+
+def test_step_path_selector():
+    """dv_set_step_path takes the three plans and rejects anything else (no launch)."""
+    lib = dv.lib()
+    for p in (dv.PATH_ONE_LAUNCH, dv.PATH_TWO_LAUNCH, dv.PATH_AUTO):
+        assert lib.dv_set_step_path(p) == dv.DV_OK
+    for bad in (-1, 3, 99):
+        assert lib.dv_set_step_path(bad) == dv.DV_EINVAL
+        assert "dv_set_step_path" in dv.last_error()
+    assert lib.dv_set_step_path(dv.PATH_AUTO) == dv.DV_OK
+
+
+def test_wait_limits_hook():
+    """dv_debug_wait_limits sets and restores the in-launch wait limits (no launch)."""
+    lib = dv.lib()
+    assert lib.dv_debug_wait_limits(64, 1) == dv.DV_OK
+    assert lib.dv_debug_wait_limits(0, 0) == dv.DV_OK
