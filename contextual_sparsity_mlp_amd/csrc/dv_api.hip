@@ -484,6 +484,11 @@ void add_axpy(AxpyTask& T, int batch, const void* W, long long stride, dv_dtype 
 // for 256-thread blocks of <= 64 VGPRs, <= 80 SGPRs and <= 20 KB of LDS.
 int resident_blocks() { return 8 * device_cus(); }
 
+// Chunk-share skews (AxpyTask::skew) of the row sums without waits: the wave path and
+// the matrix-core path.
+constexpr int kSkewWave = 32;
+constexpr int kSkewMfma = 16;
+
 // Row-sum grid of a launch that runs the segment alone: six blocks per CU.
 int default_axpy_blocks() { return 6 * device_cus(); }
 
@@ -1071,6 +1076,10 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
     const int wflags = T_ATTN | T_AXPY | T_WAIT | (fp8 ? T_FP8 : 0);
     const int lds = std::max(axpy_lds(bt, fp8 ? 16 : 8), attn_lds());
     const int fit = std::min(resident_blocks(), phase_occupancy(wflags, bt, lds) * device_cus());
+    // The grid holds every attention block first; with fewer than two row-sum blocks
+    // per CU left beside them, the separate launches below are faster (OPT-175B batch
+    // 2: 566 against 180 us per layer).
+    const bool room = fit - f.attn.blocks >= 2 * device_cus();
     add_out(f.axpy, std::max(1, fit - f.attn.blocks));
     AxpySeg& S = f.axpy.seg[0];
     S.wait_ctr = up(P.done);
@@ -1104,7 +1113,7 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
     f.axpy.fault = fault_word();
     f.axpy.batch = batch;
     const int grid = f.attn.blocks + f.axpy.blocks;
-    if (grid <= fit && f.axpy.fault) return launch(wflags, bt, f, grid, lds, stream, fn);
+    if (room && grid <= fit && f.axpy.fault) return launch(wflags, bt, f, grid, lds, stream, fn);
   }
 
   // Otherwise two launches: the attention (its last split of each head combines the
@@ -1147,6 +1156,7 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
     a2.axpy.seg[a2.axpy.nseg - 1].hist = attn_alone ? nullptr : up(P.hist_a);
   }
   a2.axpy.batch = batch;
+  a2.axpy.skew = kSkewWave;
   const int flags2 = (a2.attn.blocks ? T_ATTN : 0) | (a2.axpy.nseg ? T_AXPY : 0);
   if (flags2) {
     const int lds2 = std::max((flags2 & T_AXPY) ? axpy_lds(bt) : 0, a2.attn.blocks ? attn_lds() : 0);
@@ -1157,6 +1167,11 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
   PhaseArgs a3 = zero_args();
   add_out(a3.axpy, default_axpy_blocks(), nx ? 2 : kAxMfmaMinBatch);
   a3.axpy.batch = batch;
+  // chunk shares weighted toward the blocks dispatched first (measured at OPT-175B:
+  // look-ahead layer 112.5 -> 109.0 us at batch 1, 969 -> 955 at 16, 1528 -> 1496 at
+  // 32; the matrix-core row sum alone, without the top-k blocks, measured slower, so
+  // it keeps equal shares)
+  a3.axpy.skew = a3.axpy.seg[0].mfma_nt > 0 ? (nx ? kSkewMfma : 0) : kSkewWave;
   int flags3 = T_AXPY | (fp8 ? T_FP8 : 0);
   if (nx) {
     TopkTask& tk = a3.topk;

@@ -157,6 +157,10 @@ struct AxpyTask {
   // second source's rows alone (its rows split c2 ways) and the others the first
   // source's rows alone; 0: every chunk takes its share of both, first source first.
   int c2;
+  // Row sums without waits: chunk c of C takes a share of the rows weighted
+  // skew (C-1-c) + 8 (C-1) (0: equal shares), so the blocks dispatched first, which
+  // stream faster on their CU, take more.
+  int skew;
   int nseg;
   int batch;
   int blocks;

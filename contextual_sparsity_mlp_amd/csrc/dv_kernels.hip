@@ -1028,6 +1028,25 @@ __device__ __forceinline__ void bf16_rows(const int* lrow, const float* lcoef, i
   }
 }
 
+// Rows [r0, r1) of chunk c of C chunks over n rows.  With skew > 0 earlier chunks take
+// more rows (weight skew (C-1-c) + 8 (C-1)): their blocks come first in block order,
+// and on a CU the older waves issue first, so they stream faster than the blocks
+// dispatched after them.
+__device__ __forceinline__ void chunk_range(int c, int C, int n, int skew, int& r0, int& r1) {
+  if (skew == 0 || C <= 1) {
+    const int per = (n + C - 1) / C;
+    r0 = min(c * per, n);
+    r1 = min(r0 + per, n);
+    return;
+  }
+  auto W = [&](long long x) {
+    return (long long)skew * (x * (C - 1) - x * (x - 1) / 2) + 8ll * (C - 1) * x;
+  };
+  const long long tot = W(C);
+  r0 = (int)((long long)n * W(c) / tot);
+  r1 = (int)((long long)n * W(c + 1) / tot);
+}
+
 // One block: a slice of kAxSliceLanes*VEC output columns and a chunk of the row list.
 template <int BT, int VEC, int WT, bool WAIT>
 __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, const float* sc2,
@@ -1066,9 +1085,8 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
     // c takes a contiguous share of it.  lrow marks second-source rows with bit 30.
     const int nrows_a = list_slots(S.rows) * S.rows.expand;
     const int nrows = nrows_a + (S.W2 ? list_slots(S.rows2) * S.rows2.expand : 0);
-    const int per = (nrows + S.nchunks - 1) / S.nchunks;
-    const int r0 = min(chunk * per, nrows);
-    const int r1 = min(r0 + per, nrows);
+    int r0, r1;
+    chunk_range(chunk, S.nchunks, nrows, task ? task->skew : 0, r0, r1);
 
     for (int t0 = r0; t0 < r1; t0 += kAxpyTile) {
       const int tn = min(kAxpyTile, r1 - t0);
@@ -1148,26 +1166,15 @@ __device__ __forceinline__ void axpy_block(const AxpySeg& S, const float* sc1, c
     const int n1 = list_slots(S.rows) * S.rows.expand;
     const int n2 = S.W2 ? list_slots(S.rows2) * S.rows2.expand : 0;
     // the chunk's contiguous share [r0, r1) of nr rows
-    auto share = [&](int nr, int& r0, int& r1) {
-      const int per = (nr + S.nchunks - 1) / S.nchunks;
-      r0 = min(chunk * per, nr);
-      r1 = min(r0 + per, nr);
-    };
+    auto share = [&](int nr, int& r0, int& r1) { chunk_range(chunk, S.nchunks, nr, 0, r0, r1); };
     int r0 = 0, r1 = 0, q0 = 0, q1 = 0;
     if (task->c2 > 0) {
       // separate chunks for the two sources; the first source's come first in block
       // order, so their blocks are dispatched first and the second source's blocks wait
       // for their coefficients without holding back the first source's stream
       const int c1 = S.nchunks - task->c2;
-      if (chunk < c1) {
-        const int per = (n1 + c1 - 1) / c1;
-        r0 = min(chunk * per, n1);
-        r1 = min(r0 + per, n1);
-      } else {
-        const int per = (n2 + task->c2 - 1) / task->c2;
-        q0 = min((chunk - c1) * per, n2);
-        q1 = min(q0 + per, n2);
-      }
+      if (chunk < c1) chunk_range(chunk, c1, n1, 0, r0, r1);
+      else chunk_range(chunk - c1, task->c2, n2, 0, q0, q1);
     } else {
       share(n1, r0, r1);
       share(n2, q0, q1);
@@ -1516,7 +1523,8 @@ __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a 
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
 
 template <int NT>
-__device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int batch, float* lds) {
+__device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int batch, int skew,
+                                                float* lds) {
   constexpr int TB = kMfmaRows * NT;       // tokens per block tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -1543,9 +1551,8 @@ __device__ __forceinline__ void axpy_mfma_block(const AxpySeg& S, int lb, int ba
   // contiguous share; lrow marks second-source rows with bit 30.
   const int nrows_a = list_slots(S.rows) * S.rows.expand;
   const int nrows = nrows_a + (S.W2 ? list_slots(S.rows2) * S.rows2.expand : 0);
-  const int per = (nrows + S.nchunks - 1) / S.nchunks;
-  const int r0 = min(chunk * per, nrows);
-  const int r1 = min(r0 + per, nrows);
+  int r0, r1;
+  chunk_range(chunk, S.nchunks, nrows, skew, r0, r1);
 
   for (int t0 = r0; t0 < r1; t0 += kAxmTile) {
     const int tn = min(kAxmTile, r1 - t0);
@@ -1737,9 +1744,9 @@ __device__ __forceinline__ void axpy_task(const AxpyTask& T, int blk, float* lds
   const int lb = blk - S.block0;
   if constexpr (MFMA && BT > 1 && !WAIT && !FP8) {
     if constexpr (MFMA2) {
-      if (S.mfma_nt == 2) { axpy_mfma_block<2>(S, lb, T.batch, lds); return; }
+      if (S.mfma_nt == 2) { axpy_mfma_block<2>(S, lb, T.batch, T.skew, lds); return; }
     } else {
-      if (S.mfma_nt == 1) { axpy_mfma_block<1>(S, lb, T.batch, lds); return; }
+      if (S.mfma_nt == 1) { axpy_mfma_block<1>(S, lb, T.batch, T.skew, lds); return; }
     }
   }
   if (S.wdt == W_BF16) {
