@@ -414,7 +414,10 @@ __device__ __forceinline__ void rowdot_f32(const float4* __restrict__ rp, const 
 template <int BT, bool FP8, bool KV>
 __device__ __forceinline__ void rowdot_task(const RowdotTask& T, int blk, float* lds) {
   constexpr int NSEG = KV ? kMaxRowdotSeg : kMaxSeg;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index as a scalar: each row's bookkeeping and id load stay in scalar
+  // registers; 159 instead of 165 VGPRs at one token, and the 2- and 4-token and
+  // cache-store instances fit 3 waves per SIMD instead of 2)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Counters and histograms used by later launches of the same call start at zero.
   for (int i = blk * kThreads + tid; i < T.zero_words; i += T.blocks * kThreads) T.zero_ptr[i] = 0u;
 
