@@ -92,9 +92,10 @@ constexpr size_t kTimingPairs = 8192;
 // Per-call launch counter (the k-th launch of the current entry point).
 thread_local int t_slot = 0;
 
-// Event pair of the next launch slot when timing is on (null otherwise).
+// Event pair of the next launch slot when timing is on (null otherwise); the launch
+// hands them to the runtime, which stamps them with the kernel's own start and end.
 struct SlotEvents { hipEvent_t a = nullptr, b = nullptr; };
-SlotEvents slot_begin(void* stream) {
+SlotEvents slot_events() {
   TimingState& T = timing();
   SlotEvents ev;
   const int slot = t_slot++;
@@ -106,11 +107,7 @@ SlotEvents slot_begin(void* stream) {
       T.recs.push_back({slot, ev.a, ev.b});
     }
   }
-  if (ev.a) (void)hipEventRecord(ev.a, static_cast<hipStream_t>(stream));
   return ev;
-}
-void slot_end(const SlotEvents& ev, void* stream) {
-  if (ev.b) (void)hipEventRecord(ev.b, static_cast<hipStream_t>(stream));
 }
 
 int axpy_mfma_lds(int tokens);
@@ -130,9 +127,8 @@ int launch(int flags, int bt, const PhaseArgs& a, int grid, int lds, void* strea
     for (int s = 0; s < a.axpy.nseg; ++s) all = all && a.axpy.seg[s].mfma_nt > 0;
     if (all) bt = 4;
   }
-  const SlotEvents ev = slot_begin(stream);
-  const int err = launch_phase(flags, bt, a, grid, lds, stream);
-  slot_end(ev, stream);
+  const SlotEvents ev = slot_events();
+  const int err = launch_phase(flags, bt, a, grid, lds, stream, ev.a, ev.b);
   if (err != 0)
     return fail(DV_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString((hipError_t)err));
   return DV_OK;
@@ -1004,9 +1000,8 @@ int decode_layer_impl(const char* fn, const dv_layer* L, const dv_layer* nx, int
       z.zero.blocks = std::max(1, std::min(cdiv(P.s_zero_words, kThreads * 4), 64));
       int err = launch_phase(T_ZERO, 1, z, z.zero.blocks, 0, stream);
       if (err == 0) {
-        const SlotEvents ev = slot_begin(stream);
-        err = launch_stream(kvc, t, t.grid, lds, stream);
-        slot_end(ev, stream);
+        const SlotEvents ev = slot_events();
+        err = launch_stream(kvc, t, t.grid, lds, stream, ev.a, ev.b);
       }
       if (err != 0)
         return fail(DV_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString((hipError_t)err));

@@ -305,10 +305,14 @@ struct PhaseArgs {
 };
 
 // Host-side launcher implemented in dv_kernels.hip.  Returns a hipError_t as int.
-int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream);
+// ev0 / ev1 (hipEvent_t, may be null): events the runtime stamps with the kernel's own
+// start and end (the launch's timing slot).
+int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream,
+                 void* ev0 = nullptr, void* ev1 = nullptr);
 // The one-launch sparse step (kvdt: W_BF16 or W_F32 cache); blocks per CU it keeps
 // resident with lds_bytes of LDS (0 on error).
-int launch_stream(int kvdt, const StreamTask& t, int grid, int lds_bytes, void* stream);
+int launch_stream(int kvdt, const StreamTask& t, int grid, int lds_bytes, void* stream,
+                  void* ev0 = nullptr, void* ev1 = nullptr);
 int stream_occupancy(int kvdt, int lds_bytes);
 // Device address of this device's fault word (set by in-launch waits that gave up);
 // nullptr on error.  fault_take reads and clears it after synchronising `stream`.

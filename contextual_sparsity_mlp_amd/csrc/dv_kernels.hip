@@ -34,6 +34,7 @@
 // a later launch reads use plain stores (a launch boundary orders them).  There are
 // no floating-point atomics; only integer tickets and histograms.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <mutex>
 #include <type_traits>
 #include <math.h>
@@ -2517,13 +2518,23 @@ void stream_kernel(StreamTask T) {
   }
 }
 
-int launch_stream(int kvdt, const StreamTask& t, int grid, int lds_bytes, void* stream) {
+// A launch of `kernel` on `stream`; non-null events are stamped by the runtime with the
+// kernel's own start and end (no event packets around it, so a launch's timing slot
+// measures the kernel as a kernel trace does).
+template <typename K, typename A>
+static void launch_k(K kernel, int grid, int lds_bytes, void* stream, void* ev0, void* ev1,
+                     const A& args) {
+  hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), (uint32_t)lds_bytes,
+                        static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev0),
+                        static_cast<hipEvent_t>(ev1), 0u, args);
+}
+
+int launch_stream(int kvdt, const StreamTask& t, int grid, int lds_bytes, void* stream,
+                  void* ev0, void* ev1) {
   if (kvdt == W_BF16)
-    hipLaunchKernelGGL((stream_kernel<W_BF16>), dim3(grid), dim3(kThreads), lds_bytes,
-                       static_cast<hipStream_t>(stream), t);
+    launch_k(stream_kernel<W_BF16>, grid, lds_bytes, stream, ev0, ev1, t);
   else
-    hipLaunchKernelGGL((stream_kernel<W_F32>), dim3(grid), dim3(kThreads), lds_bytes,
-                       static_cast<hipStream_t>(stream), t);
+    launch_k(stream_kernel<W_F32>, grid, lds_bytes, stream, ev0, ev1, t);
   return (int)hipGetLastError();
 }
 
@@ -2663,89 +2674,84 @@ __global__ __launch_bounds__(kThreads) void rowdot_mfma_lds_kernel(PhaseArgs a) 
 }
 
 template <int FLAGS, int BT>
-static int launch_t(const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
+static int launch_t(const PhaseArgs& a, int grid, int lds_bytes, void* stream, void* ev0,
+                    void* ev1) {
   if constexpr ((FLAGS & ~T_FP8) == (T_ROWDOT | T_KV) && BT == 1)
-    hipLaunchKernelGGL((rowdot_kv_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
-                       static_cast<hipStream_t>(stream), a);
+    launch_k(rowdot_kv_kernel<FLAGS, BT>, grid, lds_bytes, stream, ev0, ev1, a);
   else if constexpr ((FLAGS & ~(T_FP8 | T_KV)) == T_ROWDOT)
-    hipLaunchKernelGGL((rowdot_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
-                       static_cast<hipStream_t>(stream), a);
+    launch_k(rowdot_kernel<FLAGS, BT>, grid, lds_bytes, stream, ev0, ev1, a);
   else if constexpr (BT == 1 && (FLAGS & (T_WAIT | T_FP8)) != (T_WAIT | T_FP8))
-    hipLaunchKernelGGL((phase_kernel<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
-                       static_cast<hipStream_t>(stream), a);
+    launch_k(phase_kernel<FLAGS, BT>, grid, lds_bytes, stream, ev0, ev1, a);
   else
-    hipLaunchKernelGGL((phase_kernel_bt<FLAGS, BT>), dim3(grid), dim3(kThreads), lds_bytes,
-                       static_cast<hipStream_t>(stream), a);
+    launch_k(phase_kernel_bt<FLAGS, BT>, grid, lds_bytes, stream, ev0, ev1, a);
   return (int)hipGetLastError();
 }
 
 template <int FLAGS>
-static int launch_bt(int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
+static int launch_bt(int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream,
+                     void* ev0, void* ev1) {
   switch (bt) {
-    case 1: return launch_t<FLAGS, 1>(a, grid, lds_bytes, stream);
-    case 2: return launch_t<FLAGS, 2>(a, grid, lds_bytes, stream);
-    default: return launch_t<FLAGS, 4>(a, grid, lds_bytes, stream);
+    case 1: return launch_t<FLAGS, 1>(a, grid, lds_bytes, stream, ev0, ev1);
+    case 2: return launch_t<FLAGS, 2>(a, grid, lds_bytes, stream, ev0, ev1);
+    default: return launch_t<FLAGS, 4>(a, grid, lds_bytes, stream, ev0, ev1);
   }
 }
 
-int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream) {
+int launch_phase(int flags, int bt, const PhaseArgs& a, int grid, int lds_bytes, void* stream,
+                 void* ev0, void* ev1) {
   switch (flags) {
     case T_ROWDOT:
       if (a.rowdot.mfma_nt == 3 || a.rowdot.mfma_nt == 4) {
         if (a.rowdot.mfma_nt == 3)
-          hipLaunchKernelGGL((rowdot_mfma_lds_kernel<1>), dim3(grid), dim3(kThreads), lds_bytes,
-                             static_cast<hipStream_t>(stream), a);
+          launch_k(rowdot_mfma_lds_kernel<1>, grid, lds_bytes, stream, ev0, ev1, a);
         else
-          hipLaunchKernelGGL((rowdot_mfma_lds_kernel<2>), dim3(grid), dim3(kThreads), lds_bytes,
-                             static_cast<hipStream_t>(stream), a);
+          launch_k(rowdot_mfma_lds_kernel<2>, grid, lds_bytes, stream, ev0, ev1, a);
         return (int)hipGetLastError();
       }
       if (a.rowdot.mfma_nt > 0) {
         if (a.rowdot.mfma_nt == 1)
-          hipLaunchKernelGGL((rowdot_mfma_kernel<1>), dim3(grid), dim3(kThreads), lds_bytes,
-                             static_cast<hipStream_t>(stream), a);
+          launch_k(rowdot_mfma_kernel<1>, grid, lds_bytes, stream, ev0, ev1, a);
         else
-          hipLaunchKernelGGL((rowdot_mfma_kernel<2>), dim3(grid), dim3(kThreads), lds_bytes,
-                             static_cast<hipStream_t>(stream), a);
+          launch_k(rowdot_mfma_kernel<2>, grid, lds_bytes, stream, ev0, ev1, a);
         return (int)hipGetLastError();
       }
-      return launch_bt<T_ROWDOT>(bt, a, grid, lds_bytes, stream);
-    case T_AXPY: return launch_bt<T_AXPY>(bt, a, grid, lds_bytes, stream);
-    case T_ATTN | T_AXPY: return launch_bt<T_ATTN | T_AXPY>(bt, a, grid, lds_bytes, stream);
-    case T_ATTN | T_AXPY | T_WAIT: return launch_bt<T_ATTN | T_AXPY | T_WAIT>(bt, a, grid, lds_bytes, stream);
+      return launch_bt<T_ROWDOT>(bt, a, grid, lds_bytes, stream, ev0, ev1);
+    case T_AXPY: return launch_bt<T_AXPY>(bt, a, grid, lds_bytes, stream, ev0, ev1);
+    case T_ATTN | T_AXPY: return launch_bt<T_ATTN | T_AXPY>(bt, a, grid, lds_bytes, stream, ev0, ev1);
+    case T_ATTN | T_AXPY | T_WAIT: return launch_bt<T_ATTN | T_AXPY | T_WAIT>(bt, a, grid, lds_bytes, stream, ev0, ev1);
     case T_ATTN | T_AXPY | T_WAIT | T_FP8:
-      return launch_bt<T_ATTN | T_AXPY | T_WAIT | T_FP8>(bt, a, grid, lds_bytes, stream);
-    case T_AXPY | T_CLASSIFY: return launch_bt<T_AXPY | T_CLASSIFY>(bt, a, grid, lds_bytes, stream);
-    case T_ROWDOT | T_FP8: return launch_bt<T_ROWDOT | T_FP8>(bt, a, grid, lds_bytes, stream);
-    case T_ROWDOT | T_KV: return launch_bt<T_ROWDOT | T_KV>(bt, a, grid, lds_bytes, stream);
+      return launch_bt<T_ATTN | T_AXPY | T_WAIT | T_FP8>(bt, a, grid, lds_bytes, stream, ev0, ev1);
+    case T_AXPY | T_CLASSIFY: return launch_bt<T_AXPY | T_CLASSIFY>(bt, a, grid, lds_bytes, stream, ev0, ev1);
+    case T_ROWDOT | T_FP8: return launch_bt<T_ROWDOT | T_FP8>(bt, a, grid, lds_bytes, stream, ev0, ev1);
+    case T_ROWDOT | T_KV: return launch_bt<T_ROWDOT | T_KV>(bt, a, grid, lds_bytes, stream, ev0, ev1);
     case T_ROWDOT | T_KV | T_FP8:
-      return launch_bt<T_ROWDOT | T_KV | T_FP8>(bt, a, grid, lds_bytes, stream);
-    case T_AXPY | T_FP8: return launch_bt<T_AXPY | T_FP8>(bt, a, grid, lds_bytes, stream);
+      return launch_bt<T_ROWDOT | T_KV | T_FP8>(bt, a, grid, lds_bytes, stream, ev0, ev1);
+    case T_AXPY | T_FP8: return launch_bt<T_AXPY | T_FP8>(bt, a, grid, lds_bytes, stream, ev0, ev1);
     case T_AXPY | T_CLASSIFY | T_FP8:
-      return launch_bt<T_AXPY | T_CLASSIFY | T_FP8>(bt, a, grid, lds_bytes, stream);
+      return launch_bt<T_AXPY | T_CLASSIFY | T_FP8>(bt, a, grid, lds_bytes, stream, ev0, ev1);
     // matrix-core row sums: batches of at least kAxMfmaMinBatch tokens (bt 4)
     case T_AXPY | T_MFMA:
-      return bt == 4 ? launch_t<T_AXPY | T_MFMA, 4>(a, grid, lds_bytes, stream) : (int)hipErrorInvalidValue;
+      return bt == 4 ? launch_t<T_AXPY | T_MFMA, 4>(a, grid, lds_bytes, stream, ev0, ev1) : (int)hipErrorInvalidValue;
     case T_ATTN | T_AXPY | T_MFMA:
-      return bt == 4 ? launch_t<T_ATTN | T_AXPY | T_MFMA, 4>(a, grid, lds_bytes, stream)
+      return bt == 4 ? launch_t<T_ATTN | T_AXPY | T_MFMA, 4>(a, grid, lds_bytes, stream, ev0, ev1)
                      : (int)hipErrorInvalidValue;
     case T_AXPY | T_CLASSIFY | T_MFMA:
-      return bt == 4 ? launch_t<T_AXPY | T_CLASSIFY | T_MFMA, 4>(a, grid, lds_bytes, stream)
+      return bt == 4 ? launch_t<T_AXPY | T_CLASSIFY | T_MFMA, 4>(a, grid, lds_bytes, stream, ev0, ev1)
                      : (int)hipErrorInvalidValue;
     // 32 tokens per matrix-core row-sum block (batch > 16)
     case T_AXPY | T_MFMA | T_MFMA2:
-      return bt == 4 ? launch_t<T_AXPY | T_MFMA | T_MFMA2, 4>(a, grid, lds_bytes, stream)
+      return bt == 4 ? launch_t<T_AXPY | T_MFMA | T_MFMA2, 4>(a, grid, lds_bytes, stream, ev0, ev1)
                      : (int)hipErrorInvalidValue;
     case T_ATTN | T_AXPY | T_MFMA | T_MFMA2:
-      return bt == 4 ? launch_t<T_ATTN | T_AXPY | T_MFMA | T_MFMA2, 4>(a, grid, lds_bytes, stream)
+      return bt == 4 ? launch_t<T_ATTN | T_AXPY | T_MFMA | T_MFMA2, 4>(a, grid, lds_bytes, stream, ev0, ev1)
                      : (int)hipErrorInvalidValue;
     case T_AXPY | T_CLASSIFY | T_MFMA | T_MFMA2:
-      return bt == 4 ? launch_t<T_AXPY | T_CLASSIFY | T_MFMA | T_MFMA2, 4>(a, grid, lds_bytes, stream)
+      return bt == 4 ? launch_t<T_AXPY | T_CLASSIFY | T_MFMA | T_MFMA2, 4>(a, grid, lds_bytes, stream, ev0, ev1)
                      : (int)hipErrorInvalidValue;
-    case T_ATTN: return launch_t<T_ATTN, 1>(a, grid, lds_bytes, stream);
-    case T_ZERO: return launch_t<T_ZERO, 1>(a, grid, lds_bytes, stream);
-    case T_HIST: return launch_t<T_HIST, 1>(a, grid, lds_bytes, stream);
-    case T_CLASSIFY: return launch_t<T_CLASSIFY, 1>(a, grid, lds_bytes, stream);
+    case T_ATTN: return launch_t<T_ATTN, 1>(a, grid, lds_bytes, stream, ev0, ev1);
+    case T_ZERO: return launch_t<T_ZERO, 1>(a, grid, lds_bytes, stream, ev0, ev1);
+    case T_HIST: return launch_t<T_HIST, 1>(a, grid, lds_bytes, stream, ev0, ev1);
+    case T_CLASSIFY: return launch_t<T_CLASSIFY, 1>(a, grid, lds_bytes, stream, ev0, ev1);
     default: return (int)hipErrorInvalidValue;
   }
 }

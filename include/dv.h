@@ -253,8 +253,9 @@ enum { DV_PATH_AUTO = 0, DV_PATH_TWO_LAUNCH = 1, DV_PATH_ONE_LAUNCH = 2 };
 int dv_set_step_path(int path);
 
 /* Phase timing for measurement.  dv_timing_enable(1) makes every later call record
- * a hipEvent pair around each of its kernel launches on the call's stream (events are
- * created here, once); dv_timing_enable(0) stops recording.  dv_timing_read()
+ * a hipEvent pair for each of its kernel launches, which the runtime stamps with the
+ * kernel's own start and end (hipExtLaunchKernelGGL; events are created here, once);
+ * dv_timing_enable(0) stops recording.  dv_timing_read()
  * synchronises the recorded events and returns, per launch slot (the k-th launch
  * inside an entry point), the summed elapsed milliseconds and the number of launches
  * recorded, then clears the record.  At most `max_slots` slots are returned;
