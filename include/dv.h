@@ -242,7 +242,7 @@ int dv_debug_wait_limits(unsigned spins, unsigned extra);
 
 /* Launch plan of dv_decode_layer / dv_decode_layer_noalloc for one token, bf16 rows, no
  * next-layer predictor and no cache append (the sparse MLP + head-sparse MHA step of
- * the Deja Vu paper, Section 4, Eq. (1) and (2), alone).  DV_PATH_TWO_LAUNCH: one
+ * the Deja Vu page, section 2.3, Eq. (1) and (2), alone).  DV_PATH_TWO_LAUNCH: one
  * launch dots every gathered row, a second one runs attention and both row sums.
  * DV_PATH_ONE_LAUNCH: one launch whose resident blocks take the row dots, attention
  * items and row-sum slices from an ordered queue, each item waiting (bounded) on the
