@@ -2518,15 +2518,19 @@ void stream_kernel(StreamTask T) {
   }
 }
 
-// A launch of `kernel` on `stream`; non-null events are stamped by the runtime with the
-// kernel's own start and end (no event packets around it, so a launch's timing slot
-// measures the kernel as a kernel trace does).
+// A launch of `kernel` on `stream`.  With timing events, the runtime stamps them with
+// the kernel's own start and end (no event packets around it, so a launch's timing slot
+// measures the kernel as a kernel trace does); without, a plain launch.
 template <typename K, typename A>
 static void launch_k(K kernel, int grid, int lds_bytes, void* stream, void* ev0, void* ev1,
                      const A& args) {
-  hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), (uint32_t)lds_bytes,
-                        static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev0),
-                        static_cast<hipEvent_t>(ev1), 0u, args);
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), (uint32_t)lds_bytes,
+                          static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev0),
+                          static_cast<hipEvent_t>(ev1), 0u, args);
+  else
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds_bytes,
+                       static_cast<hipStream_t>(stream), args);
 }
 
 int launch_stream(int kvdt, const StreamTask& t, int grid, int lds_bytes, void* stream,

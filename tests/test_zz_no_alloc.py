@@ -89,3 +89,51 @@ def test_noalloc_matches_workspace_entry_point():
     # the benchmarked sparse step: OPT-175B at batch 1 without a next layer
     banner("noalloc c4 batch 1 last layer")
     _same(_case(c4, 1, False), "c4 B=1 no next")
+
+
+def test_noalloc_graph_replay():
+    """The entry point captured into a HIP graph (torch.cuda.graph) and replayed: every
+    replay, with eager calls of both entry points and host synchronisation between
+    them, gives the eager result bit for bit (y_out and the next layer's sets).  The
+    path records kernels only: its counters and tickets are cleared by its own kernels,
+    not by memset nodes."""
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    # one token with the look-ahead step, the benchmarked sparse step, and four tokens
+    # (matrix-core row dots split into ticketed parts, whose tickets a small launch clears)
+    for cfg, B, with_next in ((CONFIGS["c2"], 1, True), (CONFIGS["c4"], 1, False),
+                              (CONFIGS["c2"], 4, True)):
+        banner(f"noalloc graph replay {cfg.name} batch {B} next={with_next}")
+        c = _case(cfg, B, with_next)
+        ref_y, ref_sets = _run(c, False)
+        y_out = torch.empty_like(c["y"])
+        outs = [torch.empty((c["cap_m"],), dtype=torch.int32, device=DEV),
+                torch.empty((1,), dtype=torch.int32, device=DEV),
+                torch.empty((c["cap_a"],), dtype=torch.int32, device=DEV),
+                torch.empty((1,), dtype=torch.int32, device=DEV)]
+        nx = [o if c["nxt"] is not None else None for o in outs]
+        args = (c["layer"], c["nxt"], c["y"], y_out, c["idx_m"], c["cnt_m"], c["cap_m"],
+                c["idx_a"], c["cnt_a"], c["cap_a"], *nx)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            dv.decode_layer_noalloc(*args)      # set-up outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dv.decode_layer_noalloc(*args)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            y_out.fill_(float("nan"))
+            for o in outs:
+                o.fill_(-9)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y_out, ref_y), f"{cfg.name} replay {rep}: y_out differs"
+            if ref_sets is not None:
+                got = (outs[0][: int(outs[1][0])].cpu(), outs[2][: int(outs[3][0])].cpu())
+                for a, b in zip(got, ref_sets):
+                    assert torch.equal(a, b), f"{cfg.name} replay {rep}: next-layer set differs"
+            # eager work between the replays, on the same scratch and a caller workspace
+            _same(c, f"{cfg.name} eager after replay {rep}")
+        del g
