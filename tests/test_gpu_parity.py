@@ -509,8 +509,45 @@ WAIT_SHAPES = {
 def test_decode_layer_waiting_slot_path(name):
     cfg = WAIT_SHAPES[name]
     banner(f"decode_layer waiting launch, per-slot path {name}")
-    r = _layer_case(cfg, with_next=False)
+    dv.timing_read(16)
+    dv.timing_enable(True)
+    try:
+        r = _layer_case(cfg, with_next=False)
+    finally:
+        dv.timing_enable(False)
+    _, launches = dv.timing_read(16)
+    # the plan under test: the row dots, then the single waiting launch
+    assert len(launches) == 2, f"{name}: {len(launches)} launches, expected the two-launch plan"
     assert_close(r["y_out"], r["y_ref"], TIGHT_ATTN, f"per-slot path {name}")
+
+
+@pytest.mark.parametrize("B,expected", [(1, 2), (2, 3)])
+def test_sparse_step_launch_plan(B, expected):
+    """The OPT-175B-shaped sparse step (no next layer) takes the row dots plus the single
+    waiting launch at one token, and three launches (row dots, attention, row sum) at two
+    tokens, where fewer than two row-sum blocks per CU would fit beside the attention."""
+    cfg = CONFIGS["c4"]
+    banner(f"sparse step launch plan c4 batch {B}")
+    L = synth.make_layer(cfg, DEV, batch=B)
+    y = synth.make_y(cfg, DEV, batch=B)
+    cap_m, cap_a = min(cfg.F, B * cfg.k_m), min(cfg.h, B * cfg.k_a)
+    idx_m, cnt_m = put_set(synth.random_index_set(cfg.F, cap_m, seed=81 + B).numpy(), cap_m)
+    idx_a, cnt_a = put_set(synth.random_index_set(cfg.h, cap_a, seed=91 + B).numpy(), cap_a)
+    layer = dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, k_m=cfg.k_m, k_a=cfg.k_a, scale=cfg.scale)
+    ws = dv.workspace(dv.OP_DECODE_LAYER, batch=B, d=cfg.d, F=cfg.F, h=cfg.h, dh=cfg.dh,
+                      n_ctx=cfg.n_ctx, r=cfg.r, max_count_m=cap_m, max_count_a=cap_a)
+    y_out = torch.full_like(y, np.nan)
+    dv.timing_read(16)
+    dv.timing_enable(True)
+    try:
+        dv.decode_layer(layer, None, y, y_out, idx_m, cnt_m, cap_m, idx_a, cnt_a, cap_a,
+                        None, None, None, None, ws)
+        torch.cuda.synchronize()
+    finally:
+        dv.timing_enable(False)
+    _, launches = dv.timing_read(16)
+    assert len(launches) == expected, f"batch {B}: {len(launches)} launches, expected {expected}"
+    assert torch.isfinite(y_out).all(), f"batch {B}: non-finite output"
 
 
 @pytest.mark.parametrize("name", ["bf16-ragged", "c4"])
