@@ -521,19 +521,27 @@ def test_decode_layer_waiting_slot_path(name):
     assert_close(r["y_out"], r["y_ref"], TIGHT_ATTN, f"per-slot path {name}")
 
 
-@pytest.mark.parametrize("B,expected", [(1, 2), (2, 3)])
-def test_sparse_step_launch_plan(B, expected):
+@pytest.mark.parametrize("B,fp8,expected", [(1, False, 2), (2, False, 3), (1, True, 2)])
+def test_sparse_step_launch_plan(B, fp8, expected):
     """The OPT-175B-shaped sparse step (no next layer) takes the row dots plus the single
-    waiting launch at one token, and three launches (row dots, attention, row sum) at two
-    tokens, where fewer than two row-sum blocks per CU would fit beside the attention."""
+    waiting launch at one token (bf16 or fp8 rows), and three launches (row dots,
+    attention, row sum) at two tokens, where fewer than two row-sum blocks per CU would
+    fit beside the attention."""
     cfg = CONFIGS["c4"]
-    banner(f"sparse step launch plan c4 batch {B}")
+    banner(f"sparse step launch plan c4 batch {B} fp8={fp8}")
     L = synth.make_layer(cfg, DEV, batch=B)
     y = synth.make_y(cfg, DEV, batch=B)
     cap_m, cap_a = min(cfg.F, B * cfg.k_m), min(cfg.h, B * cfg.k_a)
     idx_m, cnt_m = put_set(synth.random_index_set(cfg.F, cap_m, seed=81 + B).numpy(), cap_m)
     idx_a, cnt_a = put_set(synth.random_index_set(cfg.h, cap_a, seed=91 + B).numpy(), cap_a)
-    layer = dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, k_m=cfg.k_m, k_a=cfg.k_a, scale=cfg.scale)
+    row_scales = None
+    if fp8:
+        q = {k: synth.quantize_rows_e4m3(getattr(L, k)) for k in ("W1t", "W2t", "Wq", "Wo")}
+        for k, (codes, _) in q.items():
+            setattr(L, k, codes)
+        row_scales = tuple(q[k][1] for k in ("W1t", "W2t", "Wq", "Wo"))
+    layer = dv.Layer(L.W1t, L.W2t, L.Wq, L.Wo, L.K, L.V, k_m=cfg.k_m, k_a=cfg.k_a, scale=cfg.scale,
+                     row_scales=row_scales)
     ws = dv.workspace(dv.OP_DECODE_LAYER, batch=B, d=cfg.d, F=cfg.F, h=cfg.h, dh=cfg.dh,
                       n_ctx=cfg.n_ctx, r=cfg.r, max_count_m=cap_m, max_count_a=cap_a)
     y_out = torch.full_like(y, np.nan)
