@@ -608,6 +608,46 @@ def check_append_stored_row_attended(O):
     assert_close(y0 - y, ref0, 1e-13, "n = 0: each head returns its own value")
 
 
+def check_append_every_head_two_steps(O):
+    """Why the append stores every head's row (the KV-cache blog page, figure (b), with
+    Eq. (2), whose X holds every previous token for every head): over two steps whose
+    head sets differ, the second step's heads, skipped by the first, still attend over
+    the first step's token.  Reference: causal scaled_dot_product_attention over all
+    n + 2 tokens.  Storing only the first step's selected heads (the alternative reading,
+    which at OPT-175B would read 2 x 19 x 128 rows of 24 KiB, 119.5 MB, instead of
+    2 x 96 x 128, 604 MB) leaves those heads without the token, and the second step's
+    output then departs from the reference."""
+    X, W = _append_data(34, n=7)                         # 8 tokens: n = 6 cached, two steps
+    B, n2, d = X.shape
+    n = n2 - 2
+    h, dh, _ = W["Wq"].shape
+    Xt = torch.from_numpy(X)
+    proj = {k: torch.einsum("bnd,icd->binc", Xt, torch.from_numpy(W[k]))
+            for k in ("Wq", "Wk", "Wv")}                 # [B][h][n+2][dh]
+    cap = n + 3
+    K = np.full((B, h, cap, dh), 7.0)
+    V = np.full((B, h, cap, dh), -7.0)
+    K[:, :, :n] = proj["Wk"][:, :, :n].numpy()
+    V[:, :, :n] = proj["Wv"][:, :, :n].numpy()
+    S1, S2 = [0, 2], [1, 3]                              # the second step's heads skipped the first
+    base = dict(W1t=W["W1t"], W2t=W["W2t"], Wq=W["Wq"], Wo=W["Wo"], Wk=W["Wk"], Wv=W["Wv"])
+    _, _, (k1, v1) = O.decode_layer_append(X[:, n], dict(base, K=K, V=V), [], S1, None, n)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        proj["Wq"], proj["Wk"], proj["Wv"], is_causal=True, scale=1.0)[:, :, n + 1]   # [B][h][dh]
+    ref = sum(o[:, i] @ torch.from_numpy(W["Wo"][i]) for i in S2).numpy()
+    # every head's row stored (the reading built): the second step matches the sequence
+    Ka, Va = K.copy(), V.copy()
+    Ka[:, :, n], Va[:, :, n] = k1, v1
+    y2, _, _ = O.decode_layer_append(X[:, n + 1], dict(base, K=Ka, V=Va), [], S2, None, n + 1)
+    assert_close(y2 - X[:, n + 1], ref, 1e-12, "every head stored: second step = attention over the sequence")
+    # only the first step's heads stored: heads 1 and 3 miss token n
+    Ks, Vs = K.copy(), V.copy()
+    Ks[:, S1, n], Vs[:, S1, n] = k1[:, S1], v1[:, S1]
+    y2s, _, _ = O.decode_layer_append(X[:, n + 1], dict(base, K=Ks, V=Vs), [], S2, None, n + 1)
+    gap = np.max(np.abs((y2s - X[:, n + 1]) - ref)) / np.max(np.abs(ref))
+    assert gap > 1e-3, f"storing the selected heads only should change the output (gap {gap:.2e})"
+
+
 ALL_CHECKS = [
     check_golden_mlp, check_golden_mha, check_golden_predictor, check_golden_layer,
     check_scores_associative, check_scores_identity_factor, check_scores_bf16_widening,
@@ -619,4 +659,5 @@ ALL_CHECKS = [
     check_mha_dense_library, check_mha_empty_and_additive, check_head_closed_forms,
     check_head_mean_shift, check_layer_composition, check_stack_lookahead,
     check_round_bf16, check_append_equals_recompute, check_append_stored_row_attended,
+    check_append_every_head_two_steps,
 ]
