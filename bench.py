@@ -15,7 +15,8 @@ Also reported: the whole look-ahead layer (the same step plus the next layer's
 low-rank predictor and top-k, its sets feeding the next step as in a layer stack),
 per-launch durations from HIP events on the launch stream, the roofline of the
 step's dominant launch, and the CPU oracle timed on the host cores (all of them and
-one) over a bounded sample.  `--sweep` prints one line per workload instead
+one) over a bounded sample, and (`variants`) the same step with fp8 rows, with GeLU
+and with the KV append.  `--sweep` prints one line per workload instead
 (OPT-6.7B, OPT-30B at batch 4, OPT-175B at batch 1-16, the 24-layer stack's layer
 at batch 32).
 """
@@ -319,6 +320,9 @@ def main():
                     help="the full decode step: every head's k and v of the current token are "
                          "computed (W^K, W^V read in full), stored at row n_ctx of the cache "
                          "and attended with it")
+    ap.add_argument("--variants", type=int, default=1,
+                    help="with the headline line: also time the same step with fp8 rows, with "
+                         "GeLU and with the KV append (2 replicas, 100 steps each; 0 = skip)")
     ap.add_argument("--step-path", choices=("auto", "two", "one"), default="auto",
                     help="launch plan of the one-token bf16 step: the library's default, the "
                          "two-launch plan, or the one-launch queue")
@@ -408,8 +412,27 @@ def main():
         "lookahead_layer": look,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "variants": None,
         "source_hash": src,
     }
+    # the same step with fp8 rows, with GeLU, and with the KV append (each measured like
+    # the headline step over 2 replicas; not part of `value`)
+    if args.variants and args.wdt == "bf16" and args.act == "relu" and not args.kv_append:
+        del W
+        torch.cuda.empty_cache()
+        out["variants"] = {}
+        for key, change in (("fp8", dict(wdt="fp8")), ("gelu", dict(act="gelu")),
+                            ("kv_append", dict(kv_append=True))):
+            va = argparse.Namespace(**{**vars(args), **change})
+            V = Workload(cfg, args.batch, 2, va)
+            _, vs, vl = measure(V, 100, 10)
+            out["variants"][key] = {"us_per_layer": vs["us_per_layer"], "bytes": vs["bytes"],
+                                    "GBps": vs["GBps"], "frac_of_peak": vs["frac_of_peak"],
+                                    "launches": vs["launches"],
+                                    "lookahead_us_per_layer": vl["us_per_layer"]}
+            del V
+            torch.cuda.empty_cache()
+
     print(json.dumps(out), flush=True)
 
 
